@@ -1,0 +1,128 @@
+"""Acceptance rules: does a GPU output agree with the oracle's reference?
+
+Test infrastructure (see the package docstring).
+
+The pages give no tolerance (the only exactness they state is that a scalar
+scale folded after the matmul is exact, fp8_gemv page "Scale contract", and
+that two FP4 kernels agree bit-exactly, fp4_matmul page "WHY cooperative-SMEM").
+The rules below are the readings taken:
+
+* float32 outputs: |gpu - ref| <= 2e-3 * B + 1e-6, B = |alpha| sum_k |x w|.
+  Every product of a bfloat16 by a decoded E4M3/NVFP4 weight is exact in
+  binary32, so the only GPU error is the order of the float32 sums; the
+  classical bound gamma_{K-1} <= 2e-3 holds for K <= 33488, so every summation
+  order passes at the shapes used here.
+* bfloat16 outputs: either the GPU value is the oracle's correctly rounded
+  value R or one of R's two bfloat16 neighbours, or (heavy cancellation only)
+  |gpu - ref| <= tau + ulp_bf16(gpu) / 2.
+* integer, code and exact-decode outputs: bit-exact (checked with
+  ``np.array_equal`` on the raw bits by the tests themselves).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_bits_to_f64, f64_to_bf16_bits
+
+__all__ = [
+    "fp_tolerance",
+    "check_f32",
+    "check_bf16",
+    "bf16_ordered",
+    "bf16_ulp",
+    "CheckResult",
+]
+
+REL_TOL = 2e-3
+ABS_TOL = 1e-6
+
+
+def fp_tolerance(bound) -> np.ndarray:
+    """Per-element tolerance tau = 2e-3 * B + 1e-6 for the float paths."""
+    return REL_TOL * np.asarray(bound, dtype=np.float64) + ABS_TOL
+
+
+class CheckResult:
+    """Outcome of a comparison: ``ok`` plus diagnostics for the failure message."""
+
+    def __init__(self, ok, n_bad, worst, n_clause2=0, max_rel=0.0, where=None):
+        self.ok = bool(ok)
+        self.n_bad = int(n_bad)
+        self.worst = worst
+        self.n_clause2 = int(n_clause2)
+        self.max_rel = float(max_rel)
+        self.where = where
+
+    def __bool__(self):
+        return self.ok
+
+    def __repr__(self):
+        return (f"CheckResult(ok={self.ok}, n_bad={self.n_bad}, worst={self.worst}, "
+                f"n_clause2={self.n_clause2}, max_err_over_B={self.max_rel:.3e}, where={self.where})")
+
+
+def check_f32(gpu, ref, bound) -> CheckResult:
+    """float32 GPU output vs float64 reference: |gpu - ref| <= 2e-3 B + 1e-6.
+
+    NaN in the reference must be matched by NaN in the GPU output (weight NaN
+    propagation); NaN anywhere else fails."""
+    g = np.asarray(gpu, dtype=np.float32).astype(np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    b = np.asarray(bound, dtype=np.float64)
+    err = np.abs(g - r)
+    tol = fp_tolerance(b)
+    both_nan = np.isnan(g) & np.isnan(r)
+    bad = ~((err <= tol) | both_nan)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(b > 0, err / b, 0.0)
+    max_rel = float(np.nanmax(rel)) if rel.size else 0.0
+    if np.any(bad):
+        idx = np.unravel_index(np.argmax(np.where(bad, err - tol, -np.inf)), bad.shape)
+        return CheckResult(False, bad.sum(), (float(g[idx]), float(r[idx]), float(tol[idx])),
+                           max_rel=max_rel, where=idx)
+    return CheckResult(True, 0, None, max_rel=max_rel)
+
+
+def bf16_ordered(bits) -> np.ndarray:
+    """Map bfloat16 bit patterns to integers ordered like the values they
+    encode, with +0 and -0 both mapped to 0; neighbouring values differ by 1."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_ulp(bits) -> np.ndarray:
+    """Spacing of the bfloat16 grid at the given values: 2^(max(e, -126) - 7)
+    where e is the value's binary exponent (zero and subnormals: 2^-133)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    e_field = (b >> 7) & 0xFF
+    e = np.maximum(e_field, 1) - 127
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def check_bf16(gpu_bits, ref, tau) -> CheckResult:
+    """bfloat16 GPU output (uint16 bits) vs float64 reference.
+
+    Clause 1: ordered distance between the GPU value and R = bf16_RNE(ref) is
+    at most one.  Clause 2 (cancellation): |gpu - ref| <= tau + ulp(gpu)/2.
+    Reports how many elements needed clause 2 (expected ~0)."""
+    g = np.asarray(gpu_bits, dtype=np.uint16)
+    r = np.asarray(ref, dtype=np.float64)
+    rb = f64_to_bf16_bits(r)
+    d = np.abs(bf16_ordered(g) - bf16_ordered(rb))
+    gnan = (g & 0x7FFF) > 0x7F80
+    rnan = np.isnan(r)
+    clause1 = (d <= 1) & ~gnan & ~rnan
+    gv = bf16_bits_to_f64(g)
+    with np.errstate(invalid="ignore"):
+        clause2 = np.abs(gv - r) <= np.asarray(tau, dtype=np.float64) + 0.5 * bf16_ulp(g)
+    clause2 &= ~gnan & ~rnan
+    ok = clause1 | clause2 | (gnan & rnan)
+    n_c2 = int(np.sum(~clause1 & clause2))
+    if not np.all(ok):
+        bad = ~ok
+        idx = np.unravel_index(np.argmax(np.where(bad, d, -1)), bad.shape)
+        return CheckResult(False, bad.sum(), (int(g[idx]), int(rb[idx]), float(r[idx])),
+                           n_clause2=n_c2, where=idx)
+    return CheckResult(True, 0, None, n_clause2=n_c2)

@@ -1,0 +1,221 @@
+"""Reference results of the weight-quantized linear layer, by definition.
+
+Test infrastructure (see the package docstring): the HIP library never imports
+this module.
+
+Every float result is ``sum_k x[m,k] * w[n,k]`` over exactly decoded operands,
+evaluated as a float64 matrix product (numpy/BLAS is the only library step).
+Alongside each result the functions return the magnitude sum
+``B[m,n] = |alpha| * sum_k |x[m,k] * w[n,k]|`` that the acceptance rule of
+``oracle.compare`` scales its tolerance by.  Integer results are exact.
+
+Inputs are the raw stored codes, exactly as the kernels receive them:
+uint8 E4M3 bytes, uint16 bfloat16 bit patterns, packed uint8 E2M1 nibbles,
+int8 codes, float32 scales.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import (
+    bf16_bits_to_f64,
+    e2m1_to_f64,
+    e4m3_to_f64,
+    unpack_nibbles,
+)
+
+__all__ = [
+    "fp8_materialize",
+    "fp8_linear",
+    "fp8_grouped",
+    "nvfp4_dequant",
+    "nvfp4_linear",
+    "int8_quantize_act",
+    "int8_accumulate",
+    "int8_epilogue",
+]
+
+_ROW_CHUNK = 8192  # weight rows decoded to float64 at a time (bounds memory on the widest layer)
+
+
+def fp8_materialize(w_codes) -> np.ndarray:
+    """FP8 weight -> dense [N, K] values (fp8_gemv page, ``enqueue_fp8_materialize``)."""
+    return e4m3_to_f64(w_codes)
+
+
+def _linear(decode_rows, n_rows: int, x_bits, alpha: float):
+    """out[m, n] = alpha * sum_k x[m,k] * Wdec[n,k] in float64, plus the bound
+    B[m, n] = |alpha| * sum_k |x[m,k] * Wdec[n,k]|.  ``decode_rows(lo, hi)``
+    returns the decoded float64 weight rows lo..hi-1."""
+    x = bf16_bits_to_f64(x_bits)
+    if x.ndim != 2:
+        raise ValueError("activation must be [M, K]")
+    m = x.shape[0]
+    ref = np.empty((m, n_rows), dtype=np.float64)
+    bound = np.empty((m, n_rows), dtype=np.float64)
+    ax = np.abs(x)
+    for lo in range(0, n_rows, _ROW_CHUNK):
+        hi = min(n_rows, lo + _ROW_CHUNK)
+        w = decode_rows(lo, hi)
+        ref[:, lo:hi] = x @ w.T
+        bound[:, lo:hi] = ax @ np.abs(w).T
+    return alpha * ref, abs(alpha) * bound
+
+
+def fp8_linear(w_codes, x_bits, alpha: float = 1.0):
+    """W8A16 linear: out = alpha * x @ dec8(W)^T.
+
+    fp8_gemv page, summary ("out = x @ dequant(W)^T") and "Scale contract"
+    (the kernel returns the raw product; the per-tensor weight_scale is a
+    scalar that multiplies the raw result).  ``alpha = 1`` is the raw result.
+    w_codes: uint8 [N, K]; x_bits: uint16 [M, K].  Returns (ref, bound), both
+    float64 [M, N].
+    """
+    w = np.asarray(w_codes, dtype=np.uint8)
+    if w.ndim != 2:
+        raise ValueError("weight must be [N, K]")
+    x = np.asarray(x_bits, dtype=np.uint16)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("K mismatch")
+    return _linear(lambda lo, hi: e4m3_to_f64(w[lo:hi]), w.shape[0], x, alpha)
+
+
+def fp8_grouped(w_codes, x_bits, a_offsets, expert_ids):
+    """Grouped (MoE) W8A16 linear.
+
+    Matmul2dFp8 page, ``run_grouped``: group z covers the activation rows
+    a_offsets[z] .. a_offsets[z+1]-1 and multiplies them by the transposed
+    weight of expert expert_ids[z]; an inactive group (id -1) writes zeros for
+    its rows; an empty group writes nothing.  The result is raw (no scale).
+
+    Readings where the page is silent: a_offsets has one more entry than
+    expert_ids; rows that no group covers are left untouched (returned as NaN
+    here, with written[r] = False); an id outside 0..E-1 behaves as -1; a
+    group whose end does not exceed its start is empty; row indices are
+    clipped to the T activation rows.
+
+    w_codes: uint8 [E, N, K]; x_bits: uint16 [T, K]; a_offsets: [G+1];
+    expert_ids: [G].  Returns (ref [T, N], bound [T, N], written [T]).
+    """
+    w = np.asarray(w_codes, dtype=np.uint8)
+    x = np.asarray(x_bits, dtype=np.uint16)
+    offs = np.asarray(a_offsets).astype(np.int64)
+    ids = np.asarray(expert_ids).astype(np.int64)
+    e_count, n, _ = w.shape
+    t = x.shape[0]
+    if offs.shape[0] != ids.shape[0] + 1:
+        raise ValueError("a_offsets must have one entry more than expert_ids")
+    ref = np.full((t, n), np.nan)
+    bound = np.full((t, n), np.nan)
+    written = np.zeros(t, dtype=bool)
+    for z in range(ids.shape[0]):
+        start = min(int(offs[z]), t)
+        end = min(int(offs[z + 1]), t)
+        if end <= start:
+            continue
+        e = int(ids[z])
+        if 0 <= e < e_count:
+            r, b = fp8_linear(w[e], x[start:end])
+        else:
+            r = np.zeros((end - start, n))
+            b = np.zeros((end - start, n))
+        ref[start:end] = r
+        bound[start:end] = b
+        written[start:end] = True
+    return ref, bound, written
+
+
+def nvfp4_dequant(w_packed, w_scale_codes) -> np.ndarray:
+    """NVFP4 weight -> dense values D[n, k] = e2m1(code(n, k)) * e4m3(S[n, k // 16]).
+
+    fp4_matmul page, summary: packed ``uint8 [N, K//2]`` lo-nibble-first codes
+    and ``float8_e4m3fn [N, K//16]`` block scales, one scale per 16
+    consecutive k of a row.  Returns float64 [N, K].
+    """
+    p = np.asarray(w_packed, dtype=np.uint8)
+    s = np.asarray(w_scale_codes, dtype=np.uint8)
+    n, half_k = p.shape
+    k = 2 * half_k
+    if k % 16 != 0 or s.shape != (n, k // 16):
+        raise ValueError("block scales must be [N, K//16] with K % 16 == 0")
+    codes = unpack_nibbles(p)
+    block_of_k = np.arange(k) // 16
+    return e2m1_to_f64(codes) * e4m3_to_f64(s)[:, block_of_k]
+
+
+def nvfp4_linear(w_packed, w_scale_codes, x_bits, alpha: float = 1.0):
+    """W4A16 NVFP4 linear: out = alpha * x @ D^T with D from ``nvfp4_dequant``.
+
+    fp4_matmul page, summary (``out = activation @ weight^T``,
+    ``enqueue_apple_fp4_matmul``); alpha is the per-tensor global scale
+    (weight_scale_2, fp8_gemv page "Scale contract").  Returns (ref, bound).
+    """
+    p = np.asarray(w_packed, dtype=np.uint8)
+    s = np.asarray(w_scale_codes, dtype=np.uint8)
+    return _linear(lambda lo, hi: nvfp4_dequant(p[lo:hi], s[lo:hi]), p.shape[0], x_bits, alpha)
+
+
+def int8_quantize_act(x_bits):
+    """Per-row symmetric absmax int8 quantisation of a bfloat16 activation.
+
+    int8_matmul page, "Quantization (W8A8)": scale = absmax / 127 per row;
+    ``AppleInt8ActQuant`` / ``enqueue_apple_int8_quantize_activation``:
+    (M, K) -> int8 q + fp32 a_scale (M,).
+
+    Readings where the page is silent, all in float32 (the precision of the
+    returned scale): absmax = max_k |x[m,k]| (exact); a_scale = absmax / 127
+    with one IEEE float32 division; q = round-half-even(x / a_scale) with one
+    IEEE float32 division, clamped to [-127, 127]; an all-zero row gets
+    a_scale = 0 and q = 0.
+    """
+    x = bf16_bits_to_f64(x_bits).astype(np.float32)   # exact widening
+    if x.ndim != 2:
+        raise ValueError("activation must be [M, K]")
+    absmax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    a_scale = np.divide(absmax, np.float32(127.0), dtype=np.float32)
+    q = np.zeros(x.shape, dtype=np.int8)
+    rows = a_scale > 0
+    if np.any(rows):
+        ratio = np.divide(x[rows], a_scale[rows, None], dtype=np.float32)
+        q[rows] = np.clip(np.rint(ratio), -127, 127).astype(np.int8)
+    return q, a_scale.astype(np.float32)
+
+
+def int8_accumulate(a_codes, b_codes) -> np.ndarray:
+    """int32 accumulators acc[m, n] = sum_k a[m,k] * b[n,k] (int8_matmul page,
+    summary: ``out = dequant(A_int8 @ B_int8^T)``, accumulation in int32).
+
+    Evaluated as a float64 BLAS product of the int8 values: every product and
+    every partial sum is an integer of magnitude <= K * 127^2, exact in
+    float64 for K < 2^53 / 127^2, so the result is exact in any order.
+    Returns int64 [M, N].
+    """
+    a = np.asarray(a_codes, dtype=np.int8).astype(np.float64)
+    b = np.asarray(b_codes, dtype=np.int8).astype(np.float64)
+    if a.shape[1] * 127 * 127 >= 2 ** 53:
+        raise ValueError("K too large for an exact float64 accumulation")
+    return (a @ b.T).astype(np.int64)
+
+
+def int8_epilogue(acc, a_scale, b_scale, bias_bits=None):
+    """Dequantise int32 accumulators: out = acc * a_scale[m] * b_scale[n] + bias[n].
+
+    int8_matmul page, "Quantization (W8A8)": each output is dequantised by
+    a_scale[row] * b_scale[col] and the optional per-column bias is added after
+    the dequantisation.  Reading: bias is bfloat16 [N]; the float64 result is
+    rounded once by the caller.  Returns (ref float64 [M, N], tau float64 [M, N])
+    where tau = 2^-22 * (|acc * a_s * b_s| + |bias|) + 1e-6 is the float32
+    evaluation slack of the epilogue (four float32 roundings at most).
+    """
+    acc = np.asarray(acc, dtype=np.float64)
+    a_s = np.asarray(a_scale, dtype=np.float32).astype(np.float64)
+    b_s = np.asarray(b_scale, dtype=np.float32).astype(np.float64)
+    prod = acc * a_s[:, None] * b_s[None, :]
+    if bias_bits is None:
+        bias = np.zeros(acc.shape[1])
+    else:
+        bias = bf16_bits_to_f64(bias_bits)
+    ref = prod + bias[None, :]
+    tau = 2.0 ** -22 * (np.abs(prod) + np.abs(bias)[None, :]) + 1e-6
+    return ref, tau

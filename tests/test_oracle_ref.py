@@ -1,0 +1,257 @@
+"""Pins of the oracle's reference results (oracle.ref): hand-worked examples
+(tests/golden), exact rational brute force on tiny inputs, exact integer
+brute force, the scale-fold invariant and special cases with known answers."""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import GOLDEN
+from oracle import formats as F
+from oracle import ref as R
+import synth
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _hex_array(rows, dtype):
+    return np.array([[int(v, 16) for v in r] for r in rows], dtype=dtype)
+
+
+# ------------------------------------------------------------------ W8A16
+
+def test_fp8_linear_golden():
+    g = _load("fp8_linear_example.json")
+    w = _hex_array(g["w_codes"], np.uint8)
+    x = _hex_array(g["x_bits"], np.uint16)
+    assert np.array_equal(F.e4m3_to_f64(w), np.array(g["w_values"], float))
+    assert np.array_equal(F.bf16_bits_to_f64(x), np.array(g["x_values"], float))
+    raw, bound = R.fp8_linear(w, x)
+    assert np.array_equal(raw, np.array(g["raw"], float))
+    assert np.array_equal(bound, np.array(g["bound"], float))
+    scaled, _ = R.fp8_linear(w, x, float(g["alpha"]))
+    assert np.array_equal(scaled, np.array(g["scaled"], float))
+    assert np.array_equal(F.f64_to_bf16_bits(raw), _hex_array(g["raw_bf16_bits"], np.uint16))
+
+
+def _fraction_linear(wvals, xvals):
+    m, k = xvals.shape
+    n = wvals.shape[0]
+    out = [[sum((Fraction(float(xvals[i, t])) * Fraction(float(wvals[j, t])) for t in range(k)), Fraction(0))
+            for j in range(n)] for i in range(m)]
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 3, 5), (2, 5, 7), (3, 4, 33), (5, 2, 1)])
+def test_fp8_linear_fraction_brute_force(m, n, k):
+    r = np.random.default_rng(m * 100 + n * 10 + k)
+    w = r.integers(0, 256, size=(n, k), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x38                    # no NaN codes
+    x = synth.bf16_bits_from_f32(r.standard_normal((m, k)).astype(np.float32))
+    got, bound = R.fp8_linear(w, x)
+    exact = _fraction_linear(F.e4m3_to_f64(w), F.bf16_bits_to_f64(x))
+    for i in range(m):
+        for j in range(n):
+            e = exact[i][j]
+            assert abs(Fraction(float(got[i, j])) - e) <= Fraction(2.0 ** -40) * Fraction(float(bound[i, j])) + Fraction(2.0 ** -1000)
+    assert got.shape == (m, n)
+
+
+def test_fp8_linear_one_hot_activation_returns_decoded_column():
+    """x = e_k selects column k of dec(W): out[n] = dec(W[n, k]) exactly (a
+    NaN code anywhere in row n makes out[n] NaN, since NaN * 0 is NaN)."""
+    w = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    w[:, 15] = 0x38                                 # keep NaN codes out of the other columns' rows
+    w[7, 3], w[15, 3] = 0x7F, 0xFF
+    for k in (0, 3, 5, 14):
+        x = np.zeros((1, 16), np.uint16)
+        x[0, k] = 0x3F80                           # bf16 1.0
+        out, _ = R.fp8_linear(w, x)
+        col = F.e4m3_to_f64(w[:, k])
+        nan = np.isnan(F.e4m3_to_f64(w)).any(axis=1)
+        assert np.array_equal(np.isnan(out[0]), nan)
+        assert np.array_equal(out[0][~nan], col[~nan])
+
+
+def test_fp8_scale_fold_invariant():
+    """fp8_gemv page, 'Scale contract': a scalar weight_scale factors out of the
+    sum.  ref(alpha) == alpha * ref(1), bit-equal for powers of two and
+    within float64 rounding otherwise."""
+    c = synth.config1_case(0)
+    w, x = c.w[:64], c.x
+    raw, b1 = R.fp8_linear(w, x)
+    for a in (0.5, 2.0 ** -12, 8.0):
+        got, b = R.fp8_linear(w, x, a)
+        assert np.array_equal(got, a * raw) and np.array_equal(b, a * b1)
+    got, _ = R.fp8_linear(w, x, c.alpha)
+    assert np.allclose(got, c.alpha * raw, rtol=1e-15, atol=0)
+
+
+def test_fp8_linear_chunking_is_transparent(monkeypatch):
+    r = np.random.default_rng(3)
+    w = r.integers(0, 0x7E, size=(50, 40), dtype=np.uint8)
+    x = synth.bf16_bits_from_f32(r.standard_normal((3, 40)).astype(np.float32))
+    full, bf = R.fp8_linear(w, x)
+    monkeypatch.setattr(R, "_ROW_CHUNK", 7)
+    chunked, bc = R.fp8_linear(w, x)
+    assert np.array_equal(full, chunked) and np.array_equal(bf, bc)
+
+
+# ------------------------------------------------------------------ grouped
+
+def _tiny_grouped(seed=11, e=4, n=6, k=9, t=13):
+    r = np.random.default_rng(seed)
+    w = r.integers(0, 0x7E, size=(e, n, k), dtype=np.uint8)
+    x = synth.bf16_bits_from_f32(r.standard_normal((t, k)).astype(np.float32))
+    return w, x
+
+
+def test_grouped_brute_force_and_semantics():
+    w, x = _tiny_grouped()
+    offs = np.array([0, 3, 3, 7, 9, 12], np.uint32)   # group 1 empty, row 12 uncovered
+    ids = np.array([2, 0, -1, 1, 3], np.int32)
+    ref, bound, written = R.fp8_grouped(w, x, offs, ids)
+    assert written.tolist() == [True] * 12 + [False]
+    assert np.all(np.isnan(ref[12]))
+    assert np.array_equal(ref[3:7], np.zeros((4, 6)))            # id -1 -> zeros
+    wd = F.e4m3_to_f64(w)
+    xd = F.bf16_bits_to_f64(x)
+    for rows, ex in (((0, 3), 2), ((7, 9), 1), ((9, 12), 3)):
+        exact = _fraction_linear(wd[ex], xd[rows[0]:rows[1]])
+        for i in range(rows[1] - rows[0]):
+            for j in range(6):
+                assert abs(Fraction(float(ref[rows[0] + i, j])) - exact[i][j]) <= Fraction(2.0 ** -40) * Fraction(float(bound[rows[0] + i, j]) + 1)
+
+
+def test_grouped_single_group_equals_dense():
+    w, x = _tiny_grouped(seed=5)
+    ref, _, written = R.fp8_grouped(w, x, np.array([0, 13], np.uint32), np.array([1], np.int32))
+    dense, _ = R.fp8_linear(w[1], x)
+    assert written.all() and np.array_equal(ref, dense)
+
+
+def test_grouped_guard_readings():
+    """Out-of-range ids behave as -1; a decreasing offset pair is empty; rows
+    past T are clipped."""
+    w, x = _tiny_grouped(seed=6)
+    offs = np.array([0, 2, 1, 5, 40], np.uint32)
+    ids = np.array([7, 0, -5, 1], np.int32)
+    ref, _, written = R.fp8_grouped(w, x, offs, ids)
+    assert np.array_equal(ref[0:2], np.zeros((2, 6)))           # id 7 >= E -> zeros
+    assert np.array_equal(ref[1:5], np.zeros((4, 6)))           # id -5 -> zeros; [2,1) empty
+    dense, _ = R.fp8_linear(w[1], x[5:13])
+    assert np.array_equal(ref[5:13], dense) and written.all()
+
+
+# ------------------------------------------------------------------ NVFP4
+
+def test_nvfp4_dequant_golden():
+    g = _load("nvfp4_dequant_example.json")
+    p = _hex_array(g["packed"], np.uint8)
+    s = _hex_array(g["scales"], np.uint8)
+    d = R.nvfp4_dequant(p, s)
+    want = np.array(g["expected"], float)
+    assert np.array_equal(d, want) and np.array_equal(np.signbit(d), np.signbit(want))
+
+
+def test_nvfp4_identity_activation_gives_transposed_dequant():
+    """X = I_K: out = D^T (each output is one exact product)."""
+    p, s, _ = synth.nvfp4_weight((99, 1), 5, 32)
+    eye = synth.bf16_bits_from_f32(np.eye(32, dtype=np.float32))
+    out, _ = R.nvfp4_linear(p, s, eye)
+    assert np.array_equal(out, R.nvfp4_dequant(p, s).T)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 2, 16), (3, 4, 48)])
+def test_nvfp4_linear_fraction_brute_force(m, n, k):
+    r = np.random.default_rng(k)
+    codes = r.integers(0, 16, size=(n, k)).astype(np.uint8)
+    p = synth.pack_nibbles(codes)
+    s = r.integers(0, 0x7E, size=(n, k // 16), dtype=np.uint8)
+    x = synth.bf16_bits_from_f32(r.standard_normal((m, k)).astype(np.float32))
+    got, bound = R.nvfp4_linear(p, s, x, 0.75)
+    # first principles: value(code) * value(scale), no shared helper beyond the pinned decoders
+    e2 = F.e2m1_to_f64(np.arange(16))
+    e4 = F.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    xd = F.bf16_bits_to_f64(x)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for t in range(k):
+                byte = int(p[j, t // 2])
+                nib = byte & 0xF if t % 2 == 0 else byte >> 4
+                acc += Fraction(float(xd[i, t])) * Fraction(float(e2[nib])) * Fraction(float(e4[s[j, t // 16]]))
+            assert abs(Fraction(float(got[i, j])) - Fraction(3, 4) * acc) <= Fraction(2.0 ** -40) * Fraction(float(bound[i, j]) + 1)
+
+
+def test_nvfp4_rejects_bad_block_layout():
+    with pytest.raises(ValueError):
+        R.nvfp4_dequant(np.zeros((2, 8), np.uint8), np.zeros((2, 2), np.uint8))
+
+
+# ------------------------------------------------------------------ int8
+
+def test_int8_quantize_golden():
+    g = _load("int8_example.json")["quantize"]
+    xv = np.array(g["x_values"], dtype=np.float64)
+    bits = F.f64_to_bf16_bits(xv)
+    assert np.array_equal(F.bf16_bits_to_f64(bits), xv)       # values are bf16-exact
+    q, s = R.int8_quantize_act(bits)
+    assert np.array_equal(q, np.array(g["q"], np.int8))
+    assert s.view(np.uint32).tolist() == [int(h, 16) for h in g["a_scale_bits"]]
+
+
+def test_int8_quantize_properties():
+    c = synth.config5_case(3072, m=64)
+    q, s = R.int8_quantize_act(c.x)
+    x = F.bf16_bits_to_f64(c.x)
+    assert q.dtype == np.int8 and np.all(np.abs(q.astype(int)) <= 127)
+    am = np.abs(x).max(axis=1)
+    assert np.array_equal(s, (am.astype(np.float32) / np.float32(127)).astype(np.float32))
+    # the row absmax maps to +-127
+    idx = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(q[np.arange(64), idx].astype(int)) == 127)
+    # reconstruction error within half a step (plus float32 slack)
+    err = np.abs(x - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 2.0 ** -17))
+
+
+def test_int8_quantize_zero_and_ties():
+    bits = F.f64_to_bf16_bits(np.array([[0.0, -0.0, 0.0], [127.0, 0.5, -1.5]]))
+    q, s = R.int8_quantize_act(bits)
+    assert s[0] == 0 and np.all(q[0] == 0)
+    assert s[1] == 1.0 and q[1].tolist() == [127, 0, -2]
+
+
+def test_int8_accumulate_brute_force():
+    r = np.random.default_rng(21)
+    for (m, n, k) in ((3, 4, 5), (2, 3, 200), (1, 1, 1)):
+        a = r.integers(-127, 128, size=(m, k)).astype(np.int8)
+        b = r.integers(-127, 128, size=(n, k)).astype(np.int8)
+        acc = R.int8_accumulate(a, b)
+        for i in range(m):
+            for j in range(n):
+                assert acc[i, j] == sum(int(a[i, t]) * int(b[j, t]) for t in range(k))
+    a = np.full((1, 3072), 127, np.int8)
+    assert R.int8_accumulate(a, -a)[0, 0] == -3072 * 127 * 127
+
+
+def test_int8_gemm_golden():
+    g = _load("int8_example.json")["gemm"]
+    a = np.array(g["a"], np.int8)
+    b = np.array(g["b"], np.int8)
+    acc = R.int8_accumulate(a, b)
+    assert acc.tolist() == g["acc"]
+    bias = np.array([int(v, 16) for v in g["bias_bits"]], np.uint16)
+    out, tau = R.int8_epilogue(acc, np.array(g["a_scale"], np.float32), np.array(g["b_scale"], np.float32), bias)
+    assert np.array_equal(out, np.array(g["out"], float))
+    assert np.array_equal(F.f64_to_bf16_bits(out), _hex_array(g["out_bf16_bits"], np.uint16))
+    nob, _ = R.int8_epilogue(acc, np.array(g["a_scale"], np.float32), np.array(g["b_scale"], np.float32))
+    assert np.array_equal(nob, out - np.array([1.0, -3.0])[None, :])
+    assert np.all(tau > 0)
