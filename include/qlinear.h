@@ -1,0 +1,200 @@
+/*
+ * libqlinear -- weight-quantized linear layer out = x @ dequant(W)^T on AMD
+ * Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are dense, row-major and contiguous; every pointer is a DEVICE
+ *   pointer on the device that is current in the calling thread, unless the
+ *   comment says otherwise.  Activations x are [M, K], weights W are [N, K]
+ *   (the output feature n owns row n, K contiguous), outputs are [M, N].
+ * - Storage formats: float8_e4m3fn = OCP E4M3 "FN" (bias 7, max 448, NaN only
+ *   at 0x7F/0xFF, no inf); bfloat16 = upper half of an IEEE binary32; NVFP4 =
+ *   two E2M1 codes per byte (even k in the low nibble) plus one E4M3 scale per
+ *   16 consecutive k of a row.
+ * - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *   stream).  Every call only enqueues work on it and returns; nothing
+ *   synchronises.  Outputs are valid once the stream has reached the work.
+ * - Ownership: the caller owns every buffer.  The library keeps no pointer
+ *   past the call, allocates no device memory and has no workspace.  Its only
+ *   state is a per-device cache of the device's properties.
+ * - Errors: the return value (a qlinear_status) is the only error channel.
+ *   Arguments are validated before anything is enqueued; on an error nothing
+ *   is written.  Device-side contents (offsets, ids) are not validated by the
+ *   host; the kernels guard them as documented per call.
+ * - Inputs and outputs must not alias.  Calls are thread-safe.
+ * - Accumulation is float32 (int32 for int8 x int8); float outputs are
+ *   rounded once, to nearest even.
+ *
+ * The operations follow the documentation pages of the Mojo `linalg.matmul.
+ * gpu.apple` kernels: "fp8_gemv", "fp4_matmul", "Matmul2dFp8" and
+ * "int8_matmul".  Those pages describe Apple-M5 kernels; only what they
+ * compute is taken from them, not how.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLINEAR_ABI_VERSION 1
+
+typedef enum qlinear_status {
+  QLINEAR_OK = 0,
+  QLINEAR_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, bad dtype, bad layout */
+  QLINEAR_ERR_UNSUPPORTED = 2,  /* current device is not gfx950 */
+  QLINEAR_ERR_DEVICE = 3,       /* no usable HIP device / device query failed */
+  QLINEAR_ERR_LAUNCH = 4        /* a kernel launch reported an error */
+} qlinear_status;
+
+typedef enum qlinear_dtype {
+  QLINEAR_F32 = 0,
+  QLINEAR_BF16 = 1,
+  QLINEAR_I32 = 2
+} qlinear_dtype;
+
+/* Kernel family for the *_path calls; AUTO is what the plain call does. */
+typedef enum qlinear_path {
+  QLINEAR_PATH_AUTO = 0,
+  QLINEAR_PATH_GEMV = 1,    /* vector-ALU GEMV, 1 <= M <= 4                         */
+  QLINEAR_PATH_SKINNY = 2,  /* matrix-core skinny GEMM, 1 <= M <= 16                */
+  QLINEAR_PATH_TILED = 3    /* LDS-tiled matrix-core GEMM, any M                     */
+} qlinear_path;
+
+/* Version of this ABI (QLINEAR_ABI_VERSION of the build). */
+int qlinear_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* qlinear_status_string(int status);
+
+/*
+ * W8A16 GEMV (batch-1 decode), page "fp8_gemv" (summary, "Structure",
+ * "Scale contract"; enqueue_apple_fp8_gemv):
+ *     out[n] = alpha * sum_k x[k] * dec_e4m3(w[n, k])
+ * w: float8_e4m3fn [N, K]; x: bfloat16 [K]; out: [N] of out_dtype (F32 or
+ * BF16).  alpha = 1 returns the raw product; any other alpha is the
+ * per-tensor weight_scale folded in float32 before the single output
+ * rounding.  Any K >= 1 and any alignment are accepted; rows that are
+ * 16-byte aligned (K % 16 == 0, aligned bases) take the wide-load path.
+ */
+int qlinear_fp8_gemv(const void* w, const void* x, void* out, int out_dtype,
+                     int64_t N, int64_t K, float alpha, void* stream);
+
+/*
+ * W8A16 matmul at any M >= 1, page "fp8_gemv" (enqueue_apple_fp8_matmul) and
+ * page "Matmul2dFp8" (W8A16 GEMM, c_type = fp32/bf16, fp32 accumulation):
+ *     out[m, n] = alpha * sum_k x[m, k] * dec_e4m3(w[n, k])
+ * w: float8_e4m3fn [N, K]; x: bfloat16 [M, K]; out: [M, N] of out_dtype (F32
+ * or BF16).  Chooses the GEMV (M = 1), skinny (M <= 16) or tiled kernel.
+ */
+int qlinear_fp8_gemm(const void* w, const void* x, void* out, int out_dtype,
+                     int64_t M, int64_t N, int64_t K, float alpha, void* stream);
+
+/*
+ * As qlinear_fp8_gemm, with the kernel family forced (tests compare the
+ * families with each other).  A family that cannot take the given M returns
+ * QLINEAR_ERR_INVALID_ARG.
+ */
+int qlinear_fp8_gemm_path(const void* w, const void* x, void* out, int out_dtype,
+                          int64_t M, int64_t N, int64_t K, float alpha, int path,
+                          void* stream);
+
+/*
+ * FP8 weight materialisation, page "fp8_gemv" (enqueue_fp8_materialize):
+ *     out[n, k] = dec_e4m3(w[n, k])     (exact in F32 and in BF16)
+ * w: float8_e4m3fn [N, K]; out: [N, K] of out_dtype (F32 or BF16).  NaN codes
+ * give a quiet NaN.  Uses the same decoder as the matmul kernels.
+ */
+int qlinear_fp8_materialize(const void* w, void* out, int out_dtype,
+                            int64_t N, int64_t K, void* stream);
+
+/*
+ * Grouped (MoE) W8A16 matmul, page "Matmul2dFp8" (run_grouped): for every
+ * group z in 0 .. num_groups-1, with start = a_offsets[z] and
+ * end = a_offsets[z+1],
+ *     out[r, n] = sum_k x[r, k] * dec_e4m3(w[expert_ids[z], n, k])
+ * for rows r in [start, end).  The result is raw (the per-expert scale is
+ * applied by the caller, as on the page).  expert_ids[z] == -1 marks an
+ * inactive group, whose rows are written as zeros; an empty group writes
+ * nothing; rows that no group covers are left untouched.
+ * w: float8_e4m3fn [num_experts, N, K]; x: bfloat16 [T, K]; out: [T, N] of
+ * out_dtype (F32 or BF16); a_offsets: uint32 [num_groups + 1] and
+ * expert_ids: int32 [num_groups], both in DEVICE memory and not read by the
+ * host.  Offsets must be non-decreasing for the result to be defined
+ * (overlapping groups race); the kernel still never reads or writes out of
+ * bounds: offsets are clipped to T, a group whose end does not exceed its
+ * start is empty, and any id outside 0 .. num_experts-1 is treated as -1.
+ * max_tokens_per_group (>= 0) only sizes the launch grid; groups larger
+ * than it are still computed in full.  1 <= num_groups <= 65535.
+ */
+int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_offsets,
+                             const int32_t* expert_ids, void* out, int out_dtype,
+                             int64_t num_groups, int64_t max_tokens_per_group,
+                             int64_t num_experts, int64_t T, int64_t N, int64_t K,
+                             void* stream);
+
+/*
+ * W4A16 NVFP4 matmul, page "fp4_matmul" (enqueue_apple_fp4_matmul):
+ *     out[m, n] = alpha * sum_k x[m, k] * D[n, k],
+ *     D[n, k] = e2m1(code(n, k)) * dec_e4m3(w_scale[n, k / 16])
+ * w_packed: uint8 [N, K/2], code(n, 2j) in the low nibble of byte j and
+ * code(n, 2j+1) in the high nibble; w_scale: float8_e4m3fn [N, K/16];
+ * x: bfloat16 [M, K]; out: [M, N] of out_dtype (F32 or BF16).  K % 16 == 0.
+ * alpha is the per-tensor global scale (weight_scale_2; 1 = raw), applied in
+ * float32 before the single output rounding.  M <= 4 runs on the vector ALU,
+ * larger M dequantises weight tiles to bfloat16 in LDS for the matrix cores.
+ */
+int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x, void* out,
+                       int out_dtype, int64_t M, int64_t N, int64_t K, float alpha,
+                       void* stream);
+
+/* As qlinear_nvfp4_gemm with the kernel family forced: QLINEAR_PATH_GEMV
+ * (M <= 4) or QLINEAR_PATH_TILED (any M); others are QLINEAR_ERR_INVALID_ARG. */
+int qlinear_nvfp4_gemm_path(const void* w_packed, const void* w_scale, const void* x,
+                            void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                            float alpha, int path, void* stream);
+
+/*
+ * NVFP4 dequantisation, page "fp4_matmul" (summary: the packed weight is
+ * dequantised to bf16): out[n, k] = D[n, k] as above, exact in BF16 and F32.
+ * Uses the same decoders as the matmul kernels (BF16: the matrix-core tile
+ * decoder, F32: the vector-ALU decoder).  K % 16 == 0.
+ */
+int qlinear_nvfp4_dequant(const void* w_packed, const void* w_scale, void* out, int out_dtype,
+                          int64_t N, int64_t K, void* stream);
+
+/*
+ * Per-row symmetric int8 quantisation of a bfloat16 activation, page
+ * "int8_matmul" ("Quantization (W8A8)"; enqueue_apple_int8_quantize_activation):
+ *     a_scale[m] = absmax_k |x[m, k]| / 127      (IEEE float32 division)
+ *     q[m, k]    = clamp(round_half_even(x[m, k] / a_scale[m]), -127, 127)
+ * with IEEE float32 division per element; an all-zero row gives a_scale 0
+ * and zero codes; -128 is never produced.  x: bfloat16 [M, K]; q: int8
+ * [M, K]; a_scale: float32 [M].  Reads x once per row when K <= 4096.
+ */
+int qlinear_int8_quantize_act(const void* x, void* q, float* a_scale, int64_t M, int64_t K,
+                              void* stream);
+
+/*
+ * W8A8 int8 matmul with the dequantising epilogue, page "int8_matmul"
+ * (enqueue_apple_int8_matmul, Int8DequantWriter):
+ *     acc[m, n] = sum_k a[m, k] * b[n, k]                       (exact int32)
+ *     out[m, n] = acc[m, n] * a_scale[m] * b_scale[n] + bias[n]   (float32, one rounding to out)
+ * a: int8 [M, K]; b: int8 [N, K] (row n = output channel n); a_scale: float32
+ * [M]; b_scale: float32 [N]; bias: bfloat16 [N] or NULL (no bias).
+ * out_dtype BF16 or F32 gives the dequantised result; I32 stores the raw
+ * accumulators (a_scale, b_scale and bias are then ignored and may be NULL).
+ * K <= 133144 so that no int32 accumulator can overflow.
+ */
+int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const float* b_scale,
+                      const void* bias, void* out, int out_dtype, int64_t M, int64_t N,
+                      int64_t K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

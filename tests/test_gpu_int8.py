@@ -1,0 +1,121 @@
+"""GPU parity of the W8A8 int8 calls: activation quantiser (bit-exact codes
+and scales) and int8 GEMM (bit-exact int32 accumulators; dequantised bf16)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import compare as C
+from oracle import formats as F
+from oracle import ref as R
+from gpu_util import DEV, bf16_bits, show, to_dev_bf16, to_dev_i8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import weight_quantized_linear_amd as q
+    return q
+
+
+@pytest.fixture(scope="module")
+def case3072():
+    return synth.config5_case(3072)
+
+
+def test_quantizer_workload_bit_exact(q, case3072):
+    c = case3072
+    show("int8 quantize", c.name)
+    qd, sd = q.int8_quantize_act(to_dev_bf16(c.x))
+    want_q, want_s = R.int8_quantize_act(c.x)
+    assert np.array_equal(sd.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(qd.cpu().numpy(), want_q)
+
+
+@pytest.mark.parametrize("m,k", [(5, 8), (7, 5000), (9, 4096), (3, 3), (6, 1001), (2, 8192 + 8)])
+def test_quantizer_shapes_bit_exact(q, m, k):
+    x = synth.bf16_activation((60, m, k), m, k, outlier_p=0.05)
+    x[0, :] = 0                                             # zero row
+    if m > 1:                                               # a row with exact ties: absmax 127 -> scale 1
+        vals = np.resize(np.array([127.0, 2.5, -2.5, 3.5, -0.5, 0.5, -126.5, 1.5]), k)
+        x[1] = F.f64_to_bf16_bits(vals)
+    show("int8 quantize", m, k)
+    qd, sd = q.int8_quantize_act(to_dev_bf16(x))
+    want_q, want_s = R.int8_quantize_act(x)
+    assert np.array_equal(sd.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(qd.cpu().numpy(), want_q)
+
+
+def test_quantizer_unaligned_view(q):
+    x = synth.bf16_activation((61,), 1, 4 * 1000 + 1)
+    xd = to_dev_bf16(x)[0, 1:].reshape(4, 1000)            # base not 16-byte aligned
+    show("int8 quantize unaligned")
+    qd, sd = q.int8_quantize_act(xd)
+    want_q, want_s = R.int8_quantize_act(x[0, 1:].reshape(4, 1000))
+    assert np.array_equal(qd.cpu().numpy(), want_q) and np.array_equal(sd.cpu().numpy(), want_s)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (130, 70, 100), (257, 129, 4099), (128, 256, 3072), (333, 1000, 64)])
+def test_int32_accumulators_bit_exact(q, m, n, k):
+    r = np.random.default_rng(m * 7 + n)
+    a = r.integers(-127, 128, size=(m, k)).astype(np.int8)
+    b = r.integers(-127, 128, size=(n, k)).astype(np.int8)
+    show("int8 acc", m, n, k)
+    out = q.int8_gemm(to_dev_i8(a), to_dev_i8(b), None, None, out_dtype=torch.int32)
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), R.int8_accumulate(a, b))
+
+
+def test_int32_accumulators_extreme_values(q):
+    k = 133144 // 8 * 8
+    a = np.full((3, k), -127, np.int8)
+    b = np.full((5, k), 127, np.int8)
+    b[1] = -127
+    show("int8 acc extreme")
+    out = q.int8_gemm(to_dev_i8(a), to_dev_i8(b), None, None, out_dtype=torch.int32)
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), R.int8_accumulate(a, b))
+
+
+@pytest.mark.parametrize("n", [3072, 12288])
+def test_w8a8_workload(q, n):
+    c = synth.config5_case(n)
+    qx, sx = R.int8_quantize_act(c.x)
+    show("w8a8 workload", c.name)
+    a_d, sa_d = q.int8_quantize_act(to_dev_bf16(c.x))
+    b_d = to_dev_i8(c.b)
+    sb_d = torch.from_numpy(c.b_scale).to(DEV)
+    bias_d = to_dev_bf16(c.bias)
+    out = q.int8_gemm(a_d, b_d, sa_d, sb_d, bias_d, out_dtype=torch.bfloat16)
+    acc = q.int8_gemm(a_d, b_d, None, None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(n).choice(c.x.shape[0], 256, replace=False),
+                                     np.arange(c.x.shape[0] - 5, c.x.shape[0])]))
+    want_acc = R.int8_accumulate(qx[rows], c.b)
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), want_acc)
+    ref, tau = R.int8_epilogue(want_acc, sx[rows], c.b_scale, c.bias)
+    res = C.check_bf16(bf16_bits(out)[rows], ref, tau)
+    assert res and res.n_clause2 <= 2, res
+
+
+def test_epilogue_without_bias_and_f32(q):
+    r = np.random.default_rng(62)
+    m, n, k = 200, 300, 512
+    a = r.integers(-127, 128, size=(m, k)).astype(np.int8)
+    b = r.integers(-127, 128, size=(n, k)).astype(np.int8)
+    sa = (r.random(m).astype(np.float32) * 0.01).astype(np.float32)
+    sb = (r.random(n).astype(np.float32) * 0.01).astype(np.float32)
+    show("int8 epilogue f32")
+    out = q.int8_gemm(to_dev_i8(a), to_dev_i8(b), torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
+                      None, out_dtype=torch.float32)
+    ref, tau = R.int8_epilogue(R.int8_accumulate(a, b), sa, sb)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= tau)
+
+
+def test_int8_rejects_bad_arguments(q):
+    a = torch.zeros((2, 16), dtype=torch.int8, device=DEV)
+    assert q.lib.qlinear_int8_gemm(a.data_ptr(), a.data_ptr(), None, None, None, a.data_ptr(), 1, 2, 2, 16,
+                                   None) == q.ERR_INVALID_ARG  # bf16 output needs the scales
+    assert q.lib.qlinear_int8_gemm(a.data_ptr(), a.data_ptr(), None, None, None, a.data_ptr(), 2, 2, 2, 133145,
+                                   None) == q.ERR_INVALID_ARG  # K past the int32 range

@@ -1,0 +1,134 @@
+// Device-side building blocks shared by the libqlinear kernels (gfx950 only):
+// storage-format decoders, the float32 -> bfloat16 output rounding, the
+// wave64 reduction and the vector types the matrix-core builtins take.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlinear {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- loads
+
+// 16-byte global load.  The pointer must be 16-byte aligned.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 16-byte streaming load: the weight is read exactly once per launch, so it
+// is marked non-temporal to keep it from displacing the reused activation.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ---------------------------------------------------------------- decoders
+
+// Four float8_e4m3fn bytes (byte i = element i) -> four floats, exact.  The
+// gfx950 conversion decodes the OCP E4M3 "FN" encoding; the exhaustive
+// 256-code materialisation test checks it against the CPU decoder.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&o)[4]) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+}
+
+// One float8_e4m3fn byte (in bits 0..7) -> float, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(b, false)[0];
+}
+
+// Two float8_e4m3fn bytes (word `hi` of w) -> two packed bfloat16, exact:
+// every E4M3 value has at most 4 significant bits and lies inside the
+// bfloat16 exponent range, so the conversion (scale 1) never rounds.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight float8_e4m3fn bytes -> eight bfloat16 in the matrix-core operand type.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r.x = e4m3x2_to_bf16x2<false>(w0);
+  r.y = e4m3x2_to_bf16x2<true>(w0);
+  r.z = e4m3x2_to_bf16x2<false>(w1);
+  r.w = e4m3x2_to_bf16x2<true>(w1);
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// Two E2M1 codes (byte BYTE of w; the low nibble is the even element)
+// multiplied by the float block scale s -> two packed bfloat16.  Exact for
+// E4M3 block scales: every E2M1 x E4M3 product has at most 5 significant
+// bits and lies inside the bfloat16 range.  The exhaustive NVFP4
+// dequantisation test checks the hardware conversion against the CPU decoder.
+template <int BYTE>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w, float s) {
+  v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, BYTE);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Same decode to two floats (exact).
+template <int BYTE>
+__device__ __forceinline__ void e2m1x2_to_f32(uint32_t w, float s, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, BYTE);
+  lo = r[0];
+  hi = r[1];
+}
+
+// Packed bfloat16 pair -> floats (exact: bfloat16 is the top half of binary32).
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// ---------------------------------------------------------------- epilogue store
+
+// out[i] = round(alpha * acc) in the output type (0 = float32, 1 = bfloat16).
+__device__ __forceinline__ void store_out(void* out, int64_t i, float acc, float alpha, int out_bf16) {
+  const float v = acc * alpha;
+  if (out_bf16) reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
+  else reinterpret_cast<float*>(out)[i] = v;
+}
+
+// ---------------------------------------------------------------- wave reduction
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+  return v + __int_as_float(moved);
+}
+
+// Sum over the 64 lanes of a wave; the total is returned in every lane.
+// Steps: pairs and quads inside each row of 16 (quad_perm), the two halves
+// of the row (row_half_mirror), the row (row_mirror), then the four rows
+// through row_bcast:15 / row_bcast:31, which leaves the total in lane 63.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);          // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);          // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);         // row_half_mirror
+  v = dpp_add<0x140>(v);         // row_mirror
+  v = dpp_add<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+}  // namespace qlinear

@@ -1,0 +1,295 @@
+// W8A8 int8: the per-row activation quantiser and the int8 x int8 -> int32
+// matrix-core GEMM with the dequantising epilogue.
+//
+// What is computed ("int8_matmul" page, "Quantization (W8A8)" and summary):
+// both operands are symmetric absmax int8 with scale = absmax / 127, the
+// activation per row (quantised online by a separate one-pass kernel), the
+// weight per output channel (pre-quantised); raw products accumulate in
+// int32; the epilogue multiplies each output by a_scale[row] * b_scale[col],
+// adds the optional per-column bias after the dequantisation and casts to
+// bfloat16.
+//
+// Quantiser (gfx950): one wave per row.  The row is read once into registers
+// (16-byte loads, up to 64 x 8 x CHUNKS elements), the absmax is a wave-wide
+// max reduction, and the codes are produced from the registers: q =
+// round-half-even(x / scale) with IEEE float32 division, clamped to +-127
+// (an all-zero row gives scale 0 and zero codes).  Rows longer than the
+// register budget are read a second time for the quantisation pass.
+//
+// GEMM: a 256-thread block computes a 128 x 128 int32 tile in 128-byte K
+// strips staged in LDS; four waves (2 x 2, 64 x 64) each run 4 x 4
+// v_mfma_i32_16x16x64_i8 per 64-byte K step.  The next strip's loads are
+// issued before the current strip's matrix-core work.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qlinear {
+
+namespace {
+
+// ---------------------------------------------------------------- quantiser
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int8_t quantize_one(float x, float scale) {
+  float q = rintf(x / scale);  // IEEE division, round half to even
+  q = fminf(fmaxf(q, -127.f), 127.f);
+  return int8_t(int(q));
+}
+
+// Fast path: K % 8 == 0, x 16-byte aligned, q 8-byte aligned.
+template <int CHUNKS>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x,
+                                                            int8_t* __restrict__ q,
+                                                            float* __restrict__ a_scale, int64_t M,
+                                                            int64_t K) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= M) return;
+  const uint16_t* xr = x + row * K;
+  int8_t* qr = q + row * K;
+  const int64_t nchunks = K >> 3;  // 8 elements per 16-byte chunk
+  const bool fits = nchunks <= int64_t(kWave) * CHUNKS;
+
+  u32x4 v[CHUNKS];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    const int64_t c = int64_t(i) * kWave + lane;
+    v[i] = c < nchunks ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (int64_t c0 = 0; c0 < nchunks; c0 += int64_t(kWave) * CHUNKS) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) {
+        const int64_t c = c0 + int64_t(i) * kWave + lane;
+        v[i] = c < nchunks ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(v[i][d])), fabsf(bf16hi(v[i][d]))));
+    if (fits) break;
+  }
+  amax = wave_max(amax);
+  const float scale = amax / 127.f;
+  if (lane == 0) a_scale[row] = scale;
+  for (int64_t c0 = 0; c0 < nchunks; c0 += int64_t(kWave) * CHUNKS) {
+    if (!fits) {
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) {
+        const int64_t c = c0 + int64_t(i) * kWave + lane;
+        v[i] = c < nchunks ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int64_t c = c0 + int64_t(i) * kWave + lane;
+      if (c >= nchunks) continue;
+      uint32_t packed[2] = {0u, 0u};
+      if (amax > 0.f) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t lo = uint8_t(quantize_one(bf16lo(v[i][d]), scale));
+          const uint32_t hi = uint8_t(quantize_one(bf16hi(v[i][d]), scale));
+          packed[d >> 1] |= (lo | (hi << 8)) << (16 * (d & 1));
+        }
+      }
+      *reinterpret_cast<u32x2*>(qr + c * 8) = u32x2{packed[0], packed[1]};
+    }
+    if (fits) break;
+  }
+}
+
+// Any K, any alignment: element-wise, two passes over the row.
+__global__ __launch_bounds__(256) void quantize_rows_any_kernel(const uint16_t* __restrict__ x,
+                                                                int8_t* __restrict__ q,
+                                                                float* __restrict__ a_scale, int64_t M,
+                                                                int64_t K) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= M) return;
+  const uint16_t* xr = x + row * K;
+  float amax = 0.f;
+  for (int64_t k = lane; k < K; k += kWave) amax = fmaxf(amax, fabsf(bf16_to_f32(xr[k])));
+  amax = wave_max(amax);
+  const float scale = amax / 127.f;
+  if (lane == 0) a_scale[row] = scale;
+  for (int64_t k = lane; k < K; k += kWave)
+    q[row * K + k] = amax > 0.f ? quantize_one(bf16_to_f32(xr[k]), scale) : int8_t(0);
+}
+
+// ---------------------------------------------------------------- GEMM
+
+constexpr int BM = 128, BN = 128, BK = 128;  // BK in bytes = int8 elements
+constexpr int kThreads = 256;
+constexpr int kLdsRow = BK + 16;
+constexpr int kLdsTile = 128 * kLdsRow;
+
+struct I8Operand {
+  const int8_t* p;  // [rows, K]
+  int64_t rows, K;
+  bool vec;         // K % 16 == 0 and 16-byte aligned base
+};
+
+struct I8Stage { u32x4 v[4]; };
+
+// Thread t loads chunks id = t + 256 i (i < 4): row id / 8, bytes 16 (id % 8) .. +15.
+__device__ __forceinline__ void i8_load(const I8Operand& A, int64_t r0, int64_t k0, I8Stage& st, bool stream) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = threadIdx.x + kThreads * i;
+    const int64_t r = r0 + (id >> 3);
+    const int64_t k = k0 + 16 * (id & 7);
+    if (r < A.rows && A.vec && k + 16 <= A.K) {
+      st.v[i] = stream ? ld16_stream(A.p + r * A.K + k) : ld16(A.p + r * A.K + k);
+    } else {
+      uint32_t e[4] = {0u, 0u, 0u, 0u};
+      if (r < A.rows) {
+        for (int j = 0; j < 16; ++j)
+          if (k + j < A.K) e[j >> 2] |= uint32_t(uint8_t(A.p[r * A.K + k + j])) << (8 * (j & 3));
+      }
+      st.v[i] = u32x4{e[0], e[1], e[2], e[3]};
+    }
+  }
+}
+
+__device__ __forceinline__ void i8_store(char* lds, const I8Stage& st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = threadIdx.x + kThreads * i;
+    *reinterpret_cast<u32x4*>(lds + (id >> 3) * kLdsRow + 16 * (id & 7)) = st.v[i];
+  }
+}
+
+__device__ __forceinline__ void i8_tile_of_block(int64_t b, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                                 int64_t& tn) {
+  constexpr int kXcd = 8, kGroupM = 8;
+  const int64_t total = tiles_m * tiles_n;
+  const int64_t q = total / kXcd, r = total % kXcd;
+  const int64_t xcd = b % kXcd, local = b / kXcd;
+  const int64_t t = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int64_t group = kGroupM * tiles_n;
+  const int64_t g = t / group;
+  const int64_t first_m = g * kGroupM;
+  const int64_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int64_t in_group = t % group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
+// out_mode: 0 = float32, 1 = bfloat16 (both dequantised), 2 = raw int32 accumulators.
+__global__ __launch_bounds__(kThreads) void int8_gemm_kernel(I8Operand A, I8Operand B,
+                                                             const float* __restrict__ a_scale,
+                                                             const float* __restrict__ b_scale,
+                                                             const uint16_t* __restrict__ bias,
+                                                             void* __restrict__ out, int out_mode) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsTile];
+  char* lds_a = lds;
+  char* lds_b = lds + kLdsTile;
+  const int64_t M = A.rows, N = B.rows;
+  int64_t tm, tn;
+  i8_tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int wy = wid >> 1, wx = wid & 1;
+  const int r16 = lane & 15, kq = lane >> 4;
+
+  v4i acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  I8Stage sa, sb;
+  const int64_t nk = (A.K + BK - 1) / BK;
+  i8_load(A, m0, 0, sa, false);
+  i8_load(B, n0, 0, sb, true);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+    i8_store(lds_a, sa);
+    i8_store(lds_b, sb);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      i8_load(A, m0, (kt + 1) * BK, sa, false);
+      i8_load(B, n0, (kt + 1) * BK, sb, true);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i a[4], b[4];
+      const int koff = ks * 64 + kq * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const v4i*>(lds_a + (wy * 64 + 16 * i + r16) * kLdsRow + koff);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const v4i*>(lds_b + (wx * 64 + 16 * j + r16) * kLdsRow + koff);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // acc[i][j][v] = C[m0 + 64 wy + 16 i + 4 kq + v][n0 + 64 wx + 16 j + r16]
+  float bs[4], bb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wx * 64 + 16 * j + r16;
+    bs[j] = (out_mode != 2 && n < N) ? b_scale[n] : 0.f;
+    bb[j] = (out_mode != 2 && bias && n < N) ? bf16_to_f32(bias[n]) : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = m0 + wy * 64 + 16 * i + 4 * kq + v;
+      if (m >= M) continue;
+      const float as = out_mode != 2 ? a_scale[m] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wx * 64 + 16 * j + r16;
+        if (n >= N) continue;
+        const int32_t a32 = acc[i][j][v];
+        if (out_mode == 2) {
+          reinterpret_cast<int32_t*>(out)[m * N + n] = a32;
+        } else {
+          const float val = float(a32) * as * bs[j] + bb[j];
+          if (out_mode == 1) reinterpret_cast<uint16_t*>(out)[m * N + n] = f32_to_bf16(val);
+          else reinterpret_cast<float*>(out)[m * N + n] = val;
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_int8_quantize(const uint16_t* x, int8_t* q, float* a_scale, int64_t M, int64_t K,
+                                hipStream_t s) {
+  const bool vec = (K % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(q) % 8 == 0);
+  const int64_t blocks = (M + 3) / 4;
+  if (!vec) return launch(quantize_rows_any_kernel, dim3(blocks), dim3(256), 0, s, x, q, a_scale, M, K);
+  return launch(quantize_rows_kernel<8>, dim3(blocks), dim3(256), 0, s, x, q, a_scale, M, K);
+}
+
+hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, const float* a_scale, const float* b_scale,
+                            const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
+                            hipStream_t s) {
+  const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(b) % 16 == 0);
+  const I8Operand A{a, M, K, vec}, B{b, N, K, vec};
+  const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  return launch(int8_gemm_kernel, dim3(blocks), dim3(kThreads), 0, s, A, B, a_scale, b_scale, bias, out,
+                out_mode);
+}
+
+}  // namespace qlinear

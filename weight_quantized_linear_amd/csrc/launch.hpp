@@ -1,0 +1,60 @@
+// Host-side launch helper and the internal entry points that the C ABI
+// (qlinear.cpp) dispatches to.  Each launcher only enqueues; it returns the
+// HIP error of the launch itself.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlinear {
+
+template <typename T> struct same_type { using type = T; };
+
+// Launch through hipLaunchKernel so the launch status comes back directly
+// (no reliance on the thread's sticky last-error state).  Arguments are
+// converted to the kernel's own parameter types first.
+template <typename... Params>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                  typename same_type<Params>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, s);
+}
+
+// fp8_gemv.hip
+hipError_t launch_fp8_gemv(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
+                           int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s);
+
+// fp8_skinny.hip
+hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
+                             int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
+                             hipStream_t s);
+
+// gemm_bf16.hip
+hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
+                            int64_t N, int64_t K, float alpha, hipStream_t s);
+hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
+                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, hipStream_t s);
+hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
+                              const int32_t* expert_ids, void* out, int out_bf16, int64_t G,
+                              int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
+                              int num_cus, hipStream_t s);
+
+// nvfp4.hip
+hipError_t launch_nvfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
+                             int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
+                             hipStream_t s);
+hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, void* out, int out_bf16,
+                                int64_t N, int64_t K, hipStream_t s);
+
+// int8.hip
+hipError_t launch_int8_quantize(const uint16_t* x, int8_t* q, float* a_scale, int64_t M, int64_t K,
+                                hipStream_t s);
+hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, const float* a_scale, const float* b_scale,
+                            const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
+                            hipStream_t s);
+
+// materialize.hip
+hipError_t launch_fp8_materialize(const uint8_t* w, void* out, int out_bf16, int64_t count,
+                                  hipStream_t s);
+
+}  // namespace qlinear

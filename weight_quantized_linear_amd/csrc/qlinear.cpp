@@ -1,0 +1,250 @@
+// The C ABI of libqlinear: argument validation, the gfx950 device check and
+// the choice of kernel.  Declarations and the contract of every call are in
+// include/qlinear.h.
+#include "qlinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <limits>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+using namespace qlinear;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  std::atomic<int> state{0};  // 0 unknown, 1 gfx950, 2 other arch, 3 query failed
+  int num_cus = 0;
+};
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_device_mutex;
+
+// Status of the current device, cached per device index; fills num_cus.
+int current_device(int* num_cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLINEAR_ERR_DEVICE;
+  DeviceInfo& d = g_devices[dev];
+  int st = d.state.load(std::memory_order_acquire);
+  if (st == 0) {
+    std::lock_guard<std::mutex> lock(g_device_mutex);
+    st = d.state.load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        st = 3;
+      } else {
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        d.num_cus = prop.multiProcessorCount;
+      }
+      d.state.store(st, std::memory_order_release);
+    }
+  }
+  if (st == 3) return QLINEAR_ERR_DEVICE;
+  if (st == 2) return QLINEAR_ERR_UNSUPPORTED;
+  *num_cus = d.num_cus > 0 ? d.num_cus : 256;
+  return QLINEAR_OK;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// n1 * n2 (* n3) must stay addressable; all factors are already > 0.
+bool fits(int64_t a, int64_t b, int64_t c = 1) {
+  const int64_t lim = std::numeric_limits<int64_t>::max() / 8;
+  if (a > lim / b) return false;
+  const int64_t ab = a * b;
+  return ab <= lim / c;
+}
+
+int float_out_ok(int out_dtype) { return out_dtype == QLINEAR_F32 || out_dtype == QLINEAR_BF16; }
+
+size_t out_size(int out_dtype) { return out_dtype == QLINEAR_BF16 ? 2 : 4; }
+
+int finish(hipError_t e) { return e == hipSuccess ? QLINEAR_OK : QLINEAR_ERR_LAUNCH; }
+
+int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
+                  int64_t K, float alpha, int path, void* stream) {
+  if (!w || !x || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!float_out_ok(out_dtype)) return QLINEAR_ERR_INVALID_ARG;
+  if (!aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
+  const bool wide = K % 16 == 0 && aligned(w, 16) && aligned(x, 16);
+  if (path == QLINEAR_PATH_AUTO) {
+    if (M == 1) path = QLINEAR_PATH_GEMV;
+    else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
+    else if (M <= 4) path = QLINEAR_PATH_GEMV;
+    else path = QLINEAR_PATH_TILED;
+  }
+  switch (path) {
+    case QLINEAR_PATH_GEMV:
+      if (M > 4) return QLINEAR_ERR_INVALID_ARG;
+      break;
+    case QLINEAR_PATH_SKINNY:
+      if (M > 16 || !wide) return QLINEAR_ERR_INVALID_ARG;
+      break;
+    case QLINEAR_PATH_TILED:
+      break;
+    default:
+      return QLINEAR_ERR_INVALID_ARG;
+  }
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  auto s = static_cast<hipStream_t>(stream);
+  auto* wp = static_cast<const uint8_t*>(w);
+  auto* xp = static_cast<const uint16_t*>(x);
+  const int bf16 = out_dtype == QLINEAR_BF16;
+  if (path == QLINEAR_PATH_GEMV)
+    return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  if (path == QLINEAR_PATH_SKINNY)
+    return finish(launch_fp8_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, s));
+}
+
+int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, int out_dtype, int64_t M,
+                    int64_t N, int64_t K, float alpha, int path, void* stream) {
+  if (!wp || !ws || !x || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!float_out_ok(out_dtype) || !aligned(x, 2) || !aligned(out, out_size(out_dtype)))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (path == QLINEAR_PATH_AUTO) path = M <= 4 ? QLINEAR_PATH_GEMV : QLINEAR_PATH_TILED;
+  if (path == QLINEAR_PATH_GEMV) {
+    if (M > 4) return QLINEAR_ERR_INVALID_ARG;
+  } else if (path != QLINEAR_PATH_TILED) {
+    return QLINEAR_ERR_INVALID_ARG;
+  }
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  auto s = static_cast<hipStream_t>(stream);
+  auto* p = static_cast<const uint8_t*>(wp);
+  auto* sc = static_cast<const uint8_t*>(ws);
+  auto* xp = static_cast<const uint16_t*>(x);
+  const int bf16 = out_dtype == QLINEAR_BF16;
+  if (path == QLINEAR_PATH_GEMV)
+    return finish(launch_nvfp4_gemv(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  return finish(launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlinear_abi_version(void) { return QLINEAR_ABI_VERSION; }
+
+const char* qlinear_status_string(int status) {
+  switch (status) {
+    case QLINEAR_OK: return "ok";
+    case QLINEAR_ERR_INVALID_ARG: return "invalid argument";
+    case QLINEAR_ERR_UNSUPPORTED: return "unsupported device or configuration";
+    case QLINEAR_ERR_DEVICE: return "no usable HIP device";
+    case QLINEAR_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int qlinear_fp8_gemv(const void* w, const void* x, void* out, int out_dtype, int64_t N, int64_t K,
+                     float alpha, void* stream) {
+  return fp8_gemm_impl(w, x, out, out_dtype, 1, N, K, alpha, QLINEAR_PATH_GEMV, stream);
+}
+
+int qlinear_fp8_gemm(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
+                     int64_t K, float alpha, void* stream) {
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
+}
+
+int qlinear_fp8_gemm_path(const void* w, const void* x, void* out, int out_dtype, int64_t M,
+                          int64_t N, int64_t K, float alpha, int path, void* stream) {
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream);
+}
+
+int qlinear_fp8_materialize(const void* w, void* out, int out_dtype, int64_t N, int64_t K,
+                            void* stream) {
+  if (!w || !out || N <= 0 || K <= 0 || !fits(N, K) || !float_out_ok(out_dtype))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_fp8_materialize(static_cast<const uint8_t*>(w), out,
+                                       out_dtype == QLINEAR_BF16, N * K,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_offsets,
+                             const int32_t* expert_ids, void* out, int out_dtype, int64_t num_groups,
+                             int64_t max_tokens_per_group, int64_t num_experts, int64_t T, int64_t N,
+                             int64_t K, void* stream) {
+  if (!w || !x || !a_offsets || !expert_ids || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (num_groups <= 0 || num_groups > 65535 || max_tokens_per_group < 0 || num_experts <= 0 || T <= 0 ||
+      N <= 0 || K <= 0)
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!fits(num_experts, N, K) || !fits(T, K) || !fits(T, N)) return QLINEAR_ERR_INVALID_ARG;
+  if (!float_out_ok(out_dtype) || !aligned(x, 2) || !aligned(out, out_size(out_dtype)) ||
+      !aligned(a_offsets, 4) || !aligned(expert_ids, 4))
+    return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_fp8_grouped(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x),
+                                   a_offsets, expert_ids, out, out_dtype == QLINEAR_BF16, num_groups,
+                                   max_tokens_per_group, num_experts, T, N, K, num_cus,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
+                       int64_t M, int64_t N, int64_t K, float alpha, void* stream) {
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
+}
+
+int qlinear_nvfp4_gemm_path(const void* w_packed, const void* w_scale, const void* x, void* out,
+                            int out_dtype, int64_t M, int64_t N, int64_t K, float alpha, int path,
+                            void* stream) {
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, path, stream);
+}
+
+int qlinear_nvfp4_dequant(const void* w_packed, const void* w_scale, void* out, int out_dtype, int64_t N,
+                          int64_t K, void* stream) {
+  if (!w_packed || !w_scale || !out || N <= 0 || K <= 0 || K % 16 != 0 || !fits(N, K) ||
+      !float_out_ok(out_dtype) || !aligned(out, out_size(out_dtype)))
+    return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_nvfp4_dequant(static_cast<const uint8_t*>(w_packed), static_cast<const uint8_t*>(w_scale),
+                                     out, out_dtype == QLINEAR_BF16, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_int8_quantize_act(const void* x, void* q, float* a_scale, int64_t M, int64_t K, void* stream) {
+  if (!x || !q || !a_scale || M <= 0 || K <= 0 || !fits(M, K) || !aligned(x, 2) || !aligned(a_scale, 4))
+    return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_int8_quantize(static_cast<const uint16_t*>(x), static_cast<int8_t*>(q), a_scale, M, K,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const float* b_scale,
+                      const void* bias, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                      void* stream) {
+  if (!a || !b || !out || M <= 0 || N <= 0 || K <= 0 || K > 133144) return QLINEAR_ERR_INVALID_ARG;
+  if (!fits(M, K) || !fits(N, K) || !fits(M, N)) return QLINEAR_ERR_INVALID_ARG;
+  int mode;
+  if (out_dtype == QLINEAR_F32) mode = 0;
+  else if (out_dtype == QLINEAR_BF16) mode = 1;
+  else if (out_dtype == QLINEAR_I32) mode = 2;
+  else return QLINEAR_ERR_INVALID_ARG;
+  if (mode != 2 && (!a_scale || !b_scale || !aligned(a_scale, 4) || !aligned(b_scale, 4)))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (mode != 2 && bias && !aligned(bias, 2)) return QLINEAR_ERR_INVALID_ARG;
+  if (!aligned(out, mode == 1 ? 2 : 4)) return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_int8_gemm(static_cast<const int8_t*>(a), static_cast<const int8_t*>(b), a_scale, b_scale,
+                                 mode == 2 ? nullptr : static_cast<const uint16_t*>(bias), out, mode, M, N, K,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
