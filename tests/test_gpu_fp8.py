@@ -146,7 +146,7 @@ def test_decode_workload_bf16(q, config2_weights, shape_idx, m):
     ref, bound = R.fp8_linear(codes[rows], c.x, c.alpha)
     res = C.check_bf16(got[:, rows], ref, C.fp_tolerance(bound))
     assert res, res
-    assert res.n_clause2 <= 2, res
+    assert res.n_clause2 <= C.clause2_budget(ref), res
 
 
 # ------------------------------------------------------------------ hygiene

@@ -95,7 +95,7 @@ def test_w8a8_workload(q, n):
     assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), want_acc)
     ref, tau = R.int8_epilogue(want_acc, sx[rows], c.b_scale, c.bias)
     res = C.check_bf16(bf16_bits(out)[rows], ref, tau)
-    assert res and res.n_clause2 <= 2, res
+    assert res and res.n_clause2 <= C.clause2_budget(ref), res
 
 
 def test_epilogue_without_bias_and_f32(q):

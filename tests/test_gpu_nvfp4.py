@@ -90,7 +90,7 @@ def test_nvfp4_workload_bf16(q, nvfp4_weight, m):
     show("nvfp4 workload", c.name)
     out = q.nvfp4_gemm(to_dev_u8(c.w_packed), to_dev_u8(c.w_scale), to_dev_bf16(c.x), alpha=c.alpha)
     res = C.check_bf16(bf16_bits(out), ref, C.fp_tolerance(bound))
-    assert res and res.n_clause2 <= 2, res
+    assert res and res.n_clause2 <= C.clause2_budget(ref), res
 
 
 def test_nvfp4_workload_f32_m128(q, nvfp4_weight):

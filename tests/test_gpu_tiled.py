@@ -50,7 +50,7 @@ def test_tiled_realistic(q, m, n, k, out_dtype):
         assert res and res.max_rel < 1e-5, res
     else:
         res = C.check_bf16(bf16_bits(out), ref, C.fp_tolerance(bound))
-        assert res and res.n_clause2 <= 2, res
+        assert res and res.n_clause2 <= C.clause2_budget(ref), res
 
 
 def test_tiled_and_skinny_agree_on_exact_inputs(q):
@@ -83,7 +83,7 @@ def test_grouped_moe_workload(q):
     got = bf16_bits(out)
     assert written.all()
     res = C.check_bf16(got, ref, C.fp_tolerance(bound))
-    assert res and res.n_clause2 <= 2, res
+    assert res and res.n_clause2 <= C.clause2_budget(ref), res
     inactive = np.zeros(t, bool)
     for z in np.flatnonzero(c.expert_ids == -1):
         inactive[c.a_offsets[z]:c.a_offsets[z + 1]] = True

@@ -68,23 +68,40 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(v8bf, r);
 }
 
-// Two E2M1 codes (byte BYTE of w; the low nibble is the even element)
-// multiplied by the float block scale s -> two packed bfloat16.  Exact for
-// E4M3 block scales: every E2M1 x E4M3 product has at most 5 significant
-// bits and lies inside the bfloat16 range.  The exhaustive NVFP4
-// dequantisation test checks the hardware conversion against the CPU decoder.
+// Two E2M1 codes (byte BYTE of w; the low nibble is the even element) ->
+// two floats, exact.  The gfx950 conversion takes a float scale but applies
+// only its power-of-two part (the MX scale convention), so it is called with
+// scale 1 and an E4M3 block scale is multiplied in afterwards.
 template <int BYTE>
-__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w, float s) {
-  v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, BYTE);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// Same decode to two floats (exact).
-template <int BYTE>
-__device__ __forceinline__ void e2m1x2_to_f32(uint32_t w, float s, float& lo, float& hi) {
-  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, BYTE);
+__device__ __forceinline__ void e2m1x2_to_f32(uint32_t w, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BYTE);
   lo = r[0];
   hi = r[1];
+}
+
+// Two E2M1 codes times the E4M3 block scale s -> two floats, exact: every
+// E2M1 x E4M3 product has at most 5 significant bits, far inside float32.
+template <int BYTE>
+__device__ __forceinline__ void e2m1x2_scaled_f32(uint32_t w, float s, float& lo, float& hi) {
+  e2m1x2_to_f32<BYTE>(w, lo, hi);
+  lo *= s;
+  hi *= s;
+}
+
+// Two floats that are exactly representable in bfloat16 -> packed bfloat16
+// (the upper halves; no rounding is needed).
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Two E2M1 codes times the E4M3 block scale s -> two packed bfloat16, exact
+// (the products also lie inside the bfloat16 exponent range).  The
+// exhaustive NVFP4 dequantisation test checks this decoder against the CPU.
+template <int BYTE>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w, float s) {
+  float lo, hi;
+  e2m1x2_scaled_f32<BYTE>(w, s, lo, hi);
+  return pack_exact_bf16x2(lo, hi);
 }
 
 // Packed bfloat16 pair -> floats (exact: bfloat16 is the top half of binary32).

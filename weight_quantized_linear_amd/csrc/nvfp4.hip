@@ -9,8 +9,8 @@
 //
 // The GEMV mirrors the FP8 one: each 64-lane wave owns ROWS weight rows;
 // lane l takes the 16-byte packed chunks c = l, l + 64, ... (32 weights and
-// two block scales each), decodes pairs of nibbles straight to float32 with
-// the block scale folded in by the conversion, and accumulates in float32.
+// two block scales each), decodes pairs of nibbles to float32, multiplies by
+// the block scale (exact) and accumulates in float32.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -78,10 +78,10 @@ __global__ __launch_bounds__(256) void nvfp4_gemv_wide_kernel(
           const float s = e4m3_to_f32((sv[u][r] >> (8 * (q >> 1))) & 0xFFu);
           const uint32_t d = wv[u][r][q];
           float wf[8];
-          e2m1x2_to_f32<0>(d, s, wf[0], wf[1]);
-          e2m1x2_to_f32<1>(d, s, wf[2], wf[3]);
-          e2m1x2_to_f32<2>(d, s, wf[4], wf[5]);
-          e2m1x2_to_f32<3>(d, s, wf[6], wf[7]);
+          e2m1x2_scaled_f32<0>(d, s, wf[0], wf[1]);
+          e2m1x2_scaled_f32<1>(d, s, wf[2], wf[3]);
+          e2m1x2_scaled_f32<2>(d, s, wf[4], wf[5]);
+          e2m1x2_scaled_f32<3>(d, s, wf[6], wf[7]);
 #pragma unroll
           for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -105,7 +105,7 @@ __device__ __forceinline__ float nvfp4_at(const uint8_t* packed, const uint8_t* 
   const uint32_t byte = packed[n * (K >> 1) + (k >> 1)];
   const float s = e4m3_to_f32(scales[n * (K >> 4) + (k >> 4)]);
   float lo, hi;
-  e2m1x2_to_f32<0>(byte, s, lo, hi);
+  e2m1x2_scaled_f32<0>(byte, s, lo, hi);
   return (k & 1) ? hi : lo;
 }
 
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __res
       o[1] = uint16_t(v >> 16);
     } else {
       float lo, hi;
-      e2m1x2_to_f32<0>(byte, s, lo, hi);
+      e2m1x2_scaled_f32<0>(byte, s, lo, hi);
       float* o = reinterpret_cast<float*>(out) + n * K + k;
       o[0] = lo;
       o[1] = hi;
