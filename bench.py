@@ -1,21 +1,34 @@
-"""Throughput of the W8A16 decode path on one MI355X.
+"""Throughput of the weight-quantized linear layer on one MI355X.
 
-One step = one pass over the decode workload: the FP8 W8A16 GEMV / skinny
-GEMM at M in {1, 4, 16} for each of (N, K) in {(4096, 4096), (14336, 4096),
-(4096, 14336), (128256, 4096)}, bf16 output, alpha = the weight's per-tensor
-scale.  Weights (E4M3 of N(0, 0.02^2), per-tensor absmax/448 scale) and bf16
-N(0, 1) activations are seeded synthetic data, resident in HBM before timing.
-The step visits the M values in the outer loop, so about 640 MB of other
-weights stream between two reads of the same weight and no read is served
-from the 256 MB last-level cache.
+Default workload ("decode", the headline): one step = the FP8 W8A16 GEMV /
+skinny GEMM at M in {1, 4, 16} for each of (N, K) in {(4096, 4096),
+(14336, 4096), (4096, 14336), (128256, 4096)}, bf16 output, alpha = the
+weight's per-tensor scale.  Weights (E4M3 of N(0, 0.02^2), per-tensor
+absmax/448 scale) and bf16 N(0, 1) activations are seeded synthetic data,
+resident in HBM before timing.  The step visits the M values in the outer
+loop, so about 640 MB of other weights stream between two reads of the same
+weight and no read is served from the 256 MB last-level cache.
 
-Prints ONE JSON line: value = algorithmic bytes of the step (weights +
-activations + outputs, each once) / step time, in GB/s; ``roofline`` for the
-dominant launch (the M = 1 GEMV over the 128256 x 4096 weight), timed with
-HIP events on its stream inside the timed steps; ``cpu_baseline`` = the CPU
-oracle on a bounded sample of the same workload.
+Other workloads (--workload): "gemv2048" (M = 1, N = 2048, K = 2048 / 2050,
+fp32 out), "nvfp4" (W4A16 at M in {1, 128, 2048}, N = K = 4096), "grouped"
+(MoE W8A16, 64 experts [64, 1536, 2048], 4096 Zipf-routed tokens), "int8"
+(W8A8: activation quantiser + int8 GEMM at N in {3072, 12288}, M = 4096,
+K = 3072).  Where a workload's weights would fit the last-level cache, the
+timed graph cycles through enough copies of them (>= 1 GiB) that every read
+comes from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The step is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
+graph is replayed: host-side launch overhead of the Python binding would
+otherwise exceed the 5-20 us kernels.  Prints ONE JSON line: value =
+algorithmic traffic (decode, gemv2048, grouped: weights + activations +
+outputs once, GB/s) or work (nvfp4: TFLOP/s, int8: TOPS) per step / step
+time; ``roofline`` for the workload's dominant kernel, whose average launch
+duration is measured with HIP events around a graph of back-to-back launches
+of that kernel on its stream; ``cpu_baseline`` = the CPU oracle on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+                       [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -31,14 +44,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-SHAPES = ((4096, 4096), (14336, 4096), (4096, 14336), (128256, 4096))
-MS = (1, 4, 16)
-DOMINANT = (1, 3)  # (M, shape index): the M = 1 GEMV over the 128256 x 4096 weight
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fp8_gemv_m1_n128256_k4096.json")
-
-
-def alg_bytes(m, n, k):
-    return n * k + m * k * 2 + m * n * 2  # weight bytes + bf16 x + bf16 out
+BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+POOL_BYTES = 1 << 30
 
 
 def kernel_source_hash():
@@ -50,11 +58,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per dominant launch from the committed rocprofv3 counter
     summary, if it was taken from the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -63,37 +72,273 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(heads, scales, rows: int):
-    """The CPU oracle (oracle.ref.fp8_linear, as it stands) on the first
-    `rows` weight rows of each of the 12 cases (``heads[si]`` holds them)."""
-    import synth
-    from oracle import ref
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    total_bytes = 0
-    elapsed = 0.0
-    for si, (n, k) in enumerate(SHAPES):
-        w, s = heads[si], scales[si]
-        for m in MS:
-            x = synth.bf16_activation((2, si, 1, m), m, k)
-            t0 = time.perf_counter()
-            ref.fp8_linear(w, x, float(s))
-            elapsed += time.perf_counter() - t0
-            total_bytes += alg_bytes(m, w.shape[0], k)
-    return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"first {rows} weight rows of each of the 12 (M, N, K) cases, full K "
-                      f"({total_bytes / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
+        return os.cpu_count() or 1
+
+
+class Case:
+    """One launch of the step: ``run(copy)`` enqueues it on the current stream
+    using weight copy ``copy`` of its pool."""
+
+    def __init__(self, name, run, nbytes, work, copies=1):
+        self.name, self.run, self.bytes, self.work, self.copies = name, run, nbytes, work, copies
+
+
+def copies_for(nbytes):
+    """Weight copies to cycle so that >= 1 GiB streams between two reads of
+    one copy (only for weights small enough to stay in the 256 MB cache)."""
+    if nbytes >= (256 << 20):
+        return 1
+    return max(2, min(64, -(-POOL_BYTES // max(nbytes, 1))))
+
+
+def bf16_dev(bits, dev, np, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- workloads
+
+def build_decode(dev, q, synth, np, torch):
+    shapes = ((4096, 4096), (14336, 4096), (4096, 14336), (128256, 4096))
+    ms = (1, 4, 16)
+    weights, scales, heads = {}, {}, {}
+    for si, (n, k) in enumerate(shapes):
+        codes, s = synth.fp8_weight((2, si, 0), n, k)
+        weights[si] = torch.from_numpy(codes).to(dev)
+        scales[si] = float(s)
+        heads[si] = codes[:8192].copy()
+        del codes
+    cases = []
+    for m in ms:
+        for si, (n, k) in enumerate(shapes):
+            x = bf16_dev(synth.bf16_activation((2, si, 1, m), m, k), dev, np, torch)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            nbytes = n * k + m * k * 2 + m * n * 2
+
+            def run(copy, w=weights[si], x=x, out=out, a=scales[si]):
+                q.fp8_gemm(w, x, out=out, out_dtype=torch.bfloat16, alpha=a)
+            cases.append(Case(f"fp8 m={m} n={n} k={k}", run, nbytes, 2 * m * n * k))
+    dominant = cases[3]  # M = 1 over the 128256 x 4096 weight
+
+    def baseline():
+        from oracle import ref
+        total, elapsed = 0, 0.0
+        for m in ms:
+            for si, (n, k) in enumerate(shapes):
+                x = synth.bf16_activation((2, si, 1, m), m, k)
+                t0 = time.perf_counter()
+                ref.fp8_linear(heads[si], x, scales[si])
+                elapsed += time.perf_counter() - t0
+                rows = heads[si].shape[0]
+                total += rows * k + m * k * 2 + m * rows * 2
+        return {"value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"first 8192 weight rows (all 4096 where N = 4096) of each of the 12 (M, N, K) cases, "
+                          f"full K ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
+
+    return dict(
+        metric="FP8 W8A16 GEMV M=1 achieved HBM GB/s; dequant-GEMM TFLOP/s; % of roofline",
+        unit="GB/s", per="bytes", cases=cases, dominant=dominant, bound="hbm", peak=HBM_PEAK_GBS,
+        kernel="fp8_gemv_wide_kernel<1,2,4> (M=1, N=128256, K=4096)", dtype="f32",
+        config={"workload": "fp8_w8a16_decode: M in {1,4,16} x (N,K) in {(4096,4096),(14336,4096),"
+                            "(4096,14336),(128256,4096)}, E4M3 weight, bf16 activation, bf16 out"},
+        baseline=baseline)
+
+
+def build_gemv2048(dev, q, synth, np, torch):
+    cases, raw = [], []
+    for case in (0, 1):
+        c = synth.config1_case(case)
+        raw.append(c)
+        n, k = c.w.shape
+        copies = copies_for(n * k)
+        pool = [torch.from_numpy(c.w).to(dev) for _ in range(copies)]
+        x = bf16_dev(c.x[0], dev, np, torch)
+        out = torch.empty((n,), dtype=torch.float32, device=dev)
+
+        def run(copy, pool=pool, x=x, out=out):
+            q.fp8_gemv(pool[copy % len(pool)], x, out=out, out_dtype=torch.float32)
+        cases.append(Case(c.name, run, n * k + k * 2 + n * 4, 2 * n * k, copies))
+
+    def baseline():
+        from oracle import ref
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10:
+            for c in raw:
+                ref.fp8_linear(c.w, c.x)
+            reps += 1
+        el = time.perf_counter() - t0
+        b = reps * sum(cc.bytes for cc in cases)
+        return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"{reps} passes over both cases ({el:.1f} s)"}
+
+    return dict(metric="FP8 W8A16 GEMV M=1 N=2048 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
+                dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS, kernel="fp8_gemv_wide_kernel (M=1, N=K=2048)",
+                dtype="f32", config={"workload": "fp8_gemv_n2048: M=1, N=2048, K in {2048, 2050}, fp32 out"},
+                baseline=baseline)
+
+
+def build_nvfp4(dev, q, synth, np, torch):
+    n = k = 4096
+    packed, sc, g = synth.nvfp4_weight((3, 0, 0), n, k)
+    wbytes = packed.nbytes + sc.nbytes
+    copies = copies_for(wbytes)
+    pp = [torch.from_numpy(packed).to(dev) for _ in range(copies)]
+    ps = [torch.from_numpy(sc).to(dev) for _ in range(copies)]
+    cases = []
+    for m in (1, 128, 2048):
+        x = bf16_dev(synth.bf16_activation((3, 0, 1, m), m, k), dev, np, torch)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+        def run(copy, x=x, out=out):
+            q.nvfp4_gemm(pp[copy % copies], ps[copy % copies], x, out=out, alpha=float(g))
+        cases.append(Case(f"nvfp4 m={m} n={n} k={k}", run, wbytes + m * k * 2 + m * n * 2, 2 * m * n * k, copies))
+
+    def baseline():
+        from oracle import ref
+        rows = 512
+        t0 = time.perf_counter()
+        for m in (1, 128, 2048):
+            x = synth.bf16_activation((3, 0, 1, m), m, k)
+            ref.nvfp4_linear(packed[:rows], sc[:rows], x, float(g))
+        el = time.perf_counter() - t0
+        fl = sum(2 * m * rows * k for m in (1, 128, 2048))
+        return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"first {rows} weight rows for M in (1, 128, 2048), full K ({el:.1f} s)"}
+
+    return dict(metric="W4A16 NVFP4 dequant-GEMM TFLOP/s", unit="TFLOP/s", per="work", cases=cases,
+                dominant=cases[2], bound="mfma", peak=BF16_PEAK_TFLOPS,
+                kernel="gemm_dense_kernel<Nvfp4Tile> (M=2048, N=K=4096)", dtype="bf16",
+                config={"workload": "nvfp4_w4a16: M in {1,128,2048}, N=K=4096, E2M1 + E4M3 per-16 scales, bf16 out"},
+                baseline=baseline)
+
+
+def build_grouped(dev, q, synth, np, torch):
+    c = synth.config4_case()
+    e, n, k = c.w.shape
+    t = c.x.shape[0]
+    copies = 2  # 201 MB stack: two copies alternate so no read is served from the last-level cache
+    pw = [torch.from_numpy(c.w).to(dev) for _ in range(copies)]
+    x = bf16_dev(c.x, dev, np, torch)
+    offs = torch.from_numpy(c.a_offsets.astype(np.int32)).to(dev)
+    ids = torch.from_numpy(c.expert_ids.astype(np.int32)).to(dev)
+    out = torch.empty((t, n), dtype=torch.bfloat16, device=dev)
+    active = [z for z in range(e) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
+    rows_active = int(sum(int(c.a_offsets[z + 1]) - int(c.a_offsets[z]) for z in active))
+    nbytes = len(active) * n * k + t * k * 2 + t * n * 2
+    flops = 2 * rows_active * n * k
+
+    def run(copy):
+        q.fp8_grouped_gemm(pw[copy % copies], x, offs, ids, out=out, max_tokens_per_group=c.max_tokens)
+    cases = [Case(c.name, run, nbytes, flops, copies)]
+
+    def baseline():
+        from oracle import ref
+        gz = 8  # the first 8 groups, whole
+        t0 = time.perf_counter()
+        ref.fp8_grouped(c.w, c.x[: int(c.a_offsets[gz])], c.a_offsets[: gz + 1], c.expert_ids[:gz])
+        el = time.perf_counter() - t0
+        act = [z for z in range(gz) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
+        b = len(act) * n * k + int(c.a_offsets[gz]) * (k + n) * 2
+        return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"groups 0-7 ({int(c.a_offsets[gz])} tokens, {len(act)} active experts, {el:.1f} s)"}
+
+    return dict(metric="Grouped MoE W8A16 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
+                dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS,
+                kernel="gemm_grouped_fp8_kernel (64 experts, N=1536, K=2048, 4096 tokens)", dtype="bf16",
+                config={"workload": f"grouped_moe_w8a16: E=64 [64,1536,2048] E4M3, T=4096 bf16 tokens, Zipf(1.2) "
+                                    f"groups, {len(active)} active experts, {rows_active} active tokens"},
+                baseline=baseline)
+
+
+def build_int8(dev, q, synth, np, torch):
+    m, k = 4096, 3072
+    cases = []
+    c0 = synth.config5_case(3072)
+    x = bf16_dev(c0.x, dev, np, torch)
+    qa = torch.empty((m, k), dtype=torch.int8, device=dev)
+    sa = torch.empty((m,), dtype=torch.float32, device=dev)
+
+    def quant(copy):
+        q.int8_quantize_act(x, q=qa, a_scale=sa)
+    cases.append(Case("int8 quantize m=4096 k=3072", quant, m * k * 2 + m * k + m * 4, 0))
+    for n in (3072, 12288):
+        c = synth.config5_case(n)
+        copies = copies_for(c.b.nbytes)
+        pb = [torch.from_numpy(c.b).to(dev) for _ in range(copies)]
+        sb = torch.from_numpy(c.b_scale).to(dev)
+        bias = bf16_dev(c.bias, dev, np, torch)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+        def run(copy, pb=pb, sb=sb, bias=bias, out=out):
+            q.int8_gemm(qa, pb[copy % len(pb)], sa, sb, bias, out=out)
+        cases.append(Case(f"int8 gemm m={m} n={n} k={k}", run, m * k + n * k + m * 4 + n * 4 + n * 2 + m * n * 2,
+                          2 * m * n * k, copies))
+
+    def baseline():
+        from oracle import ref
+        rows = 256
+        t0 = time.perf_counter()
+        qx, sx = ref.int8_quantize_act(c0.x)
+        ops = 0
+        for n in (3072, 12288):
+            c = synth.config5_case(n)
+            acc = ref.int8_accumulate(qx[:rows], c.b)
+            ref.int8_epilogue(acc, sx[:rows], c.b_scale, c.bias)
+            ops += 2 * rows * n * k
+        el = time.perf_counter() - t0
+        return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"quantiser on all 4096 rows + GEMM on the first {rows} rows for both N ({el:.1f} s)"}
+
+    return dict(metric="W8A8 int8 GEMM TOPS (quantiser + GEMM + dequant epilogue)", unit="TOPS", per="work",
+                cases=cases, dominant=cases[2], bound="mfma", peak=INT8_PEAK_TOPS,
+                kernel="int8_gemm_kernel (M=4096, N=12288, K=3072)", dtype="i8",
+                config={"workload": "w8a8_int8: quantise bf16 [4096,3072] + int8 GEMM N in {3072,12288}, bf16 out"},
+                baseline=baseline)
+
+
+WORKLOADS = {"decode": build_decode, "gemv2048": build_gemv2048, "nvfp4": build_nvfp4,
+             "grouped": build_grouped, "int8": build_int8}
+
+
+# ---------------------------------------------------------------- timing
+
+def capture(torch, fn):
+    """Capture fn() (launches on the current stream) into a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, replays):
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / replays  # ms per replay
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -109,112 +354,86 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
     t_gen = time.perf_counter()
-    weights, scales, xs, outs, heads = {}, {}, {}, {}, {}
-    cpu_rows = 2048
-    for si, (n, k) in enumerate(SHAPES):
-        codes, s = synth.fp8_weight((2, si, 0), n, k)
-        weights[si] = torch.from_numpy(codes).to(dev)
-        scales[si] = float(s)
-        heads[si] = codes[:cpu_rows].copy()
-        del codes
-        for m in MS:
-            xs[(m, si)] = bf16(synth.bf16_activation((2, si, 1, m), m, k))
-            outs[(m, si)] = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    wl = WORKLOADS[args.workload](dev, q, synth, np, torch)
     torch.cuda.synchronize()
-    print(f"[bench] inputs generated and resident in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {args.workload}: inputs generated and resident in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    cases = wl["cases"]
+    r = max(c.copies for c in cases)  # steps per graph: consecutive steps read different copies
 
-    cases = [(m, si) for m in MS for si in range(len(SHAPES))]
-    step_bytes = sum(alg_bytes(m, *SHAPES[si]) for m, si in cases)
-    ev_pairs = []
+    def steps_fn():
+        for i in range(r):
+            for c in cases:
+                c.run(i)
 
-    def run(m, si):
-        q.fp8_gemm(weights[si], xs[(m, si)], out=outs[(m, si)], out_dtype=torch.bfloat16, alpha=scales[si])
-
-    def step(record):
-        for m, si in cases:
-            if record and (m, si) == DOMINANT:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                run(m, si)
-                b.record()
-                ev_pairs.append((a, b))
-            else:
-                run(m, si)
-
-    for _ in range(args.warmup):
-        step(False)
+    g = capture(torch, steps_fn)
+    for _ in range(max(1, -(-args.warmup // r))):
+        g.replay()
     torch.cuda.synchronize()
-
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    replays = max(1, -(-args.steps // r))
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        step(True)
-    end.record()
-    torch.cuda.synchronize()
+    ms_graph = time_graph(torch, g, replays)
     wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(end)
-    ms_per_step = gpu_ms / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ms_per_step = ms_graph / r
+    steps_timed = replays * r
+    per = wl["per"]
+    step_amount = sum((c.bytes if per == "bytes" else c.work) for c in cases)
+    scale = 1e9 if wl["unit"] == "GB/s" else 1e12
+    value = step_amount / (ms_per_step * 1e-3) / scale
+    del g
 
-    dom_ms = sum(a.elapsed_time(b) for a, b in ev_pairs) / len(ev_pairs)
-    dm, dsi = DOMINANT
-    dom_bytes = alg_bytes(dm, *SHAPES[dsi])
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-
-    # per-case breakdown: extra (untimed) steps in the same case order, with
-    # events around every launch, so each read is as cold as in the timed steps
-    reps = 3
-    marks = {c: [] for c in cases}
-    for _ in range(reps):
-        for c in cases:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            run(*c)
-            b.record()
-            marks[c].append((a, b))
-    torch.cuda.synchronize()
+    # per-case and dominant-kernel durations: a graph of back-to-back launches
+    # of one case (cycling its copies), timed with events on its stream
     per_case = []
-    for (m, si) in cases:
-        us = sum(a.elapsed_time(b) for a, b in marks[(m, si)]) * 1e3 / reps
-        n, k = SHAPES[si]
-        per_case.append({"m": m, "n": n, "k": k, "us": round(us, 2),
-                         "gbs": round(alg_bytes(m, n, k) / (us * 1e-6) / 1e9, 1)})
+    dom_ms = None
+    for c in cases:
+        reps = max(8, c.copies)
+
+        def one(c=c, reps=reps):
+            for i in range(reps):
+                c.run(i)
+        gc = capture(torch, one)
+        gc.replay()
+        us = time_graph(torch, gc, 3) * 1e3 / reps
+        entry = {"case": c.name, "us": round(us, 2), "gbs": round(c.bytes / (us * 1e-6) / 1e9, 1)}
+        if c.work:
+            entry["tflops"] = round(c.work / (us * 1e-6) / 1e12, 2)
+        per_case.append(entry)
+        if c is wl["dominant"]:
+            dom_ms = us * 1e-3
+        del gc
     print(f"[bench] per case: {json.dumps(per_case)}", file=sys.stderr, flush=True)
 
-    traffic = measured_traffic()
+    dom = wl["dominant"]
+    if wl["bound"] == "hbm":
+        achieved = dom.bytes / (dom_ms * 1e-3) / 1e9
+        unit, alg_key, alg = "GB/s", "algorithmic_bytes", dom.bytes
+    else:
+        achieved = dom.work / (dom_ms * 1e-3) / 1e12
+        unit, alg_key, alg = ("TFLOP/s" if wl["unit"] == "TFLOP/s" else "TOPS"), "algorithmic_ops", dom.work
     line = {
-        "metric": "FP8 W8A16 GEMV M=1 achieved HBM GB/s; dequant-GEMM TFLOP/s; % of roofline",
-        "value": round(value, 1),
-        "unit": "GB/s",
+        "metric": wl["metric"],
+        "value": round(value, 2),
+        "unit": wl["unit"],
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps_timed,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": wl["dtype"],
         "data": "synthetic",
-        "config": {"workload": "fp8_w8a16_decode: M in {1,4,16} x (N,K) in {(4096,4096),(14336,4096),"
-                               "(4096,14336),(128256,4096)}, E4M3 weight, bf16 activation, bf16 out",
-                   "bytes_per_step": step_bytes, "wall_s": round(wall, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "fp8_gemv_wide_kernel (M=1, N=128256, K=4096)",
-                     "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "config": dict(wl["config"], step_amount=step_amount, graph_steps=r, wall_s=round(wall, 3)),
+        "roofline": {"bound": wl["bound"], "achieved": round(achieved, 1), "peak": wl["peak"], "unit": unit,
+                     "frac": round(achieved / wl["peak"], 4), "traffic": measured_traffic(args.workload),
+                     "kernel": wl["kernel"], alg_key: alg, "avg_launch_us": round(dom_ms * 1e3, 2)},
         "cases": per_case,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(heads, scales, cpu_rows)
+        line["cpu_baseline"] = wl["baseline"]()
     print(json.dumps(line), flush=True)
 
 

@@ -66,6 +66,8 @@ DYADIC = [
     ("skinny", 1, 17, 16), ("skinny", 2, 300, 64), ("skinny", 4, 1000, 4096), ("skinny", 5, 33, 4112),
     ("skinny", 16, 1000, 1040), ("skinny", 16, 4111, 4096), ("skinny", 11, 2000, 14336),
     ("auto", 16, 4096, 4096),
+    # wide-N skinny kernels (4x4x4 matrix-core path for M <= 4, LDS-staged path for M > 4)
+    ("skinny", 4, 65600, 64), ("auto", 3, 70000, 256), ("skinny", 16, 65601, 528), ("auto", 7, 66000, 1024),
 ]
 
 

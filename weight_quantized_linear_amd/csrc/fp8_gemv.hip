@@ -4,13 +4,20 @@
 // What is computed follows the "fp8_gemv" documentation page (summary,
 // "Structure", "Scale contract"): at M = 1 there is one activation row, so
 // the product is a matrix-vector product with nothing for a matrix core to
-// do; the work is reading the 1-byte weights, widening them exactly to
-// float32 and accumulating in float32.  The page's kernel gives one 32-lane
-// warp to each output; here each 64-lane wave owns ROWS output rows at once,
-// so one activation chunk in registers serves ROWS weight rows, and every
-// lane issues ROWS x U independent 16-byte weight loads before it consumes
-// any (the kernel is bound by HBM bandwidth, and bytes in flight per CU are
-// what keep it there).
+// do; the work is reading the 1-byte weights, widening them exactly and
+// accumulating in float32.  The page's kernel gives one 32-lane warp to each
+// output; here each 64-lane wave owns ROWS output rows at once and every lane
+// issues ROWS x U independent 16-byte weight loads before it consumes any:
+// the kernel is bound by HBM bandwidth, and on MI355X it is the burst of
+// whole contiguous rows per wave that keeps it near the bandwidth roof (two
+// rows per wave measured best on the 128256 x 4096 weight).
+//
+// Arithmetic: pairs of E4M3 bytes are widened to pairs of bfloat16 with the
+// hardware conversion (exact: every E4M3 value fits bfloat16) and multiplied
+// by the bfloat16 activation pairs with v_dot2c_f32_bf16, which accumulates
+// in float32.  Every product of two bfloat16 values is exact in float32, so
+// this computes the same products as widening both operands to float32 and
+// using FMAs, at half the vector-ALU instructions per weight.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -63,23 +70,18 @@ __global__ __launch_bounds__(256) void fp8_gemv_wide_kernel(
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {  // dword d of the chunk = elements 4d .. 4d+3
-        float xf[M][4];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const u32x4& xa = xv[u][m][d >> 1];
-          const uint32_t x01 = (d & 1) ? xa.z : xa.x;
-          const uint32_t x23 = (d & 1) ? xa.w : xa.y;
-          xf[m][0] = bf16lo(x01); xf[m][1] = bf16hi(x01);
-          xf[m][2] = bf16lo(x23); xf[m][3] = bf16hi(x23);
-        }
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-          float wf[4];
-          e4m3x4_to_f32(wv[u][r][d], wf);
+          const v2bf w01 = __builtin_bit_cast(v2bf, e4m3x2_to_bf16x2<false>(wv[u][r][d]));
+          const v2bf w23 = __builtin_bit_cast(v2bf, e4m3x2_to_bf16x2<true>(wv[u][r][d]));
 #pragma unroll
-          for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[m][r] = fmaf(xf[m][e], wf[e], acc[m][r]);
+          for (int m = 0; m < M; ++m) {
+            const u32x4& xa = xv[u][m][d >> 1];
+            const v2bf x01 = __builtin_bit_cast(v2bf, (d & 1) ? xa.z : xa.x);
+            const v2bf x23 = __builtin_bit_cast(v2bf, (d & 1) ? xa.w : xa.y);
+            acc[m][r] = __builtin_amdgcn_fdot2_f32_bf16(w01, x01, acc[m][r], false);
+            acc[m][r] = __builtin_amdgcn_fdot2_f32_bf16(w23, x23, acc[m][r], false);
+          }
         }
       }
     }
@@ -156,14 +158,14 @@ hipError_t launch_rows(bool wide, const uint8_t* w, const uint16_t* x, void* out
   constexpr int kRowsPerBlock = ROWS * (kThreads / kWave);
   const int64_t blocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
   if (wide) {
-    // one pass of U chunks covers K = U * 1 KiB; pick U so that short rows are
-    // not padded with idle loads
+    // U chunks of 1 KiB per row are in flight per lane-group; short rows take
+    // U = 2 so that no loads are padding, longer rows U = 4 (M = 1) or 2.
     const int64_t per_lane = ((K >> 4) + kWave - 1) / kWave;
-    if (per_lane <= 2)
+    if (M > 1 || per_lane <= 2)
       return launch(fp8_gemv_wide_kernel<M, ROWS, 2>, dim3(blocks), dim3(kThreads), 0, s, w, x, out,
                     out_bf16, N, K, alpha);
-    return launch(fp8_gemv_wide_kernel<M, ROWS, (M > 2 ? 2 : 4)>, dim3(blocks), dim3(kThreads), 0, s,
-                  w, x, out, out_bf16, N, K, alpha);
+    return launch(fp8_gemv_wide_kernel<M, ROWS, 4>, dim3(blocks), dim3(kThreads), 0, s, w, x, out,
+                  out_bf16, N, K, alpha);
   }
   return launch(fp8_gemv_any_kernel<M, ROWS>, dim3(blocks), dim3(kThreads), 0, s, w, x, out,
                 out_bf16, N, K, alpha);
@@ -172,11 +174,8 @@ hipError_t launch_rows(bool wide, const uint8_t* w, const uint16_t* x, void* out
 template <int M>
 hipError_t launch_m(bool wide, const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                     int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s) {
-  // Enough waves to put several on every SIMD: 4 rows per wave when N is
-  // large, fewer when that would leave CUs idle.
-  const int64_t target_waves = int64_t(num_cus) * 8;
-  if (N >= target_waves * 4) return launch_rows<M, 4>(wide, w, x, out, out_bf16, N, K, alpha, s);
-  if (N >= target_waves * 2) return launch_rows<M, 2>(wide, w, x, out, out_bf16, N, K, alpha, s);
+  // Two rows per wave once that still gives every SIMD several waves.
+  if (N >= int64_t(num_cus) * 16) return launch_rows<M, 2>(wide, w, x, out, out_bf16, N, K, alpha, s);
   return launch_rows<M, 1>(wide, w, x, out, out_bf16, N, K, alpha, s);
 }
 

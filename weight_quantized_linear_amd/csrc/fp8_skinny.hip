@@ -3,23 +3,42 @@
 //
 // What is computed is the "Matmul2dFp8" page's W8A16 GEMM (bf16 activation,
 // float8_e4m3fn weight, float32 accumulation).  At M <= 16 the product is
-// still bound by the weight read, but M float32 FMAs per weight byte exceed
-// the vector ALU budget, so each 16 x 32 weight slice goes through one
-// v_mfma_f32_16x16x32_bf16 with the M activation rows (zero-padded to 16)
-// as the other operand.  The E4M3 -> bf16 widening is exact, so the matrix
-// core sees exactly the decoded weight.
+// still bound by the weight read, but M multiply-adds per weight byte exceed
+// what the vector ALU can sustain at full HBM bandwidth, so the products run
+// on the matrix cores.  The E4M3 -> bf16 widening is exact, so the matrix
+// cores see exactly the decoded weight; accumulation is float32.
 //
-// Work split: a 256-thread block owns 16*G output columns; its four waves
-// take interleaved 64-byte K steps, each lane loading one 16-byte chunk per
-// row group per step (row l % 16, bytes 16*(l/16) .. +15 of the step), and
-// the four partial accumulators are summed through LDS at the end.  The
-// same k-slot assignment is used for both operands, so the pairing of
-// activation and weight elements does not depend on how the matrix core
-// orders the k-slots internally.
+// Three kernels, chosen by shape (all measured on the decode shapes):
+//
+// * fp8_skinny_kernel (v_mfma_f32_16x16x32_bf16): a 256-thread block owns
+//   16*G output columns; its four waves take interleaved 64-byte K steps,
+//   each lane loading one 16-byte chunk per 16-row group per step (row
+//   l % 16, bytes 16*(l/16) .. +15 of the step); the M activation rows
+//   (zero-padded to 16) are the other operand and the four partial
+//   accumulators are summed through LDS at the end.
+// * fp8_skinny_lds_kernel: the same matrix-core work, but the block first
+//   reads a 64-row x 512-byte weight tile with fully contiguous 16-byte loads
+//   (64 lanes over 1 KiB of two rows) into LDS and the waves take their
+//   operands from there; on the 128256-row weight this beats reading the
+//   operand layout straight from HBM (106 vs 120 us at M = 16).
+// * fp8_skinny4_kernel (v_mfma_f32_4x4x4bf16_1k, M <= 4): the instruction is
+//   16 independent 4x4x4 products, one per group of four lanes, so lane
+//   4b + j can read 16 contiguous bytes of weight row j at offset 16b: one
+//   load instruction covers four rows x 256 contiguous bytes.  Block b of the
+//   instruction accumulates the k-range 16b .. of every step, and the 16
+//   block partials are summed across lanes at the end.
+//
+// In every kernel the same k-slot assignment is used for both operands, so
+// the pairing of activation and weight elements does not depend on how the
+// matrix core orders k-slots internally.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace qlinear {
+
+namespace {
+
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
 template <int G, int U>
 __global__ __launch_bounds__(256) void fp8_skinny_kernel(
@@ -57,7 +76,7 @@ __global__ __launch_bounds__(256) void fp8_skinny_kernel(
       const int64_t kb = (s0 + int64_t(u) * kWaves) * 64 + kq * 16;
       const bool ok = kb < K;  // K % 16 == 0: a chunk is wholly inside or outside
 #pragma unroll
-      for (int g = 0; g < G; ++g) wv[u][g] = ok ? ld16_stream(wrow[g] + kb) : u32x4{0u, 0u, 0u, 0u};
+      for (int g = 0; g < G; ++g) wv[u][g] = ok ? ld16(wrow[g] + kb) : u32x4{0u, 0u, 0u, 0u};
       const bool xok = ok && xrow_ok;
       xv[u][0] = xok ? ld16(xrow + kb) : u32x4{0u, 0u, 0u, 0u};
       xv[u][1] = xok ? ld16(xrow + kb + 8) : u32x4{0u, 0u, 0u, 0u};
@@ -93,18 +112,193 @@ __global__ __launch_bounds__(256) void fp8_skinny_kernel(
   }
 }
 
+// LDS-staged variant: block = 16*G rows x all of K in tiles of KT bytes per
+// row.  Thread t loads chunk id = t + 256 i of the tile: row id / (KT/16),
+// bytes 16 (id % (KT/16)), so one load instruction covers 1 KiB of
+// contiguous weight.  Wave w then takes bytes [w KT/4, (w+1) KT/4) of every
+// row of the tile in 64-byte matrix-core steps.  The next tile's loads are
+// issued before the current tile's matrix-core work.
+template <int G, int KT>
+__global__ __launch_bounds__(256) void fp8_skinny_lds_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
+    int out_bf16, int M, int64_t N, int64_t K, float alpha) {
+  constexpr int kRow = KT + 16;                        // padded LDS row (bytes)
+  constexpr int kChunksPerRow = KT / 16;
+  constexpr int kLoads = 16 * G * kChunksPerRow / 256;  // 16-byte loads per thread per tile
+  static_assert(kLoads * 256 == 16 * G * kChunksPerRow, "tile must split evenly over the block");
+  __shared__ __attribute__((aligned(16))) char tile[16 * G * kRow];
+  __shared__ v4f red[4][G][kWave];
+
+  const int t = threadIdx.x, lane = t & (kWave - 1), wid = t / kWave;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int64_t n0 = int64_t(blockIdx.x) * 16 * G;
+  const bool xrow_ok = r16 < M;
+  const uint16_t* xrow = x + int64_t(xrow_ok ? r16 : 0) * K;
+
+  v4f acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 pre[kLoads];
+  auto load_tile = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int id = t + 256 * i;
+      int64_t n = n0 + id / kChunksPerRow;
+      if (n >= N) n = N - 1;
+      const int64_t k = k0 + 16 * (id % kChunksPerRow);
+      pre[i] = k < K ? ld16(w + n * K + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  const int64_t ntiles = (K + KT - 1) / KT;
+  load_tile(0);
+  for (int64_t tt = 0; tt < ntiles; ++tt) {
+    __syncthreads();  // previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int id = t + 256 * i;
+      *reinterpret_cast<u32x4*>(tile + (id / kChunksPerRow) * kRow + 16 * (id % kChunksPerRow)) = pre[i];
+    }
+    __syncthreads();
+    if (tt + 1 < ntiles) load_tile((tt + 1) * KT);
+    constexpr int kSteps = KT / 4 / 64;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int kl = wid * (KT / 4) + 64 * s + 16 * kq;
+      const int64_t kg = tt * KT + kl;
+      const bool ok = kg < K && xrow_ok;
+      const v8bf a0 = __builtin_bit_cast(v8bf, ok ? ld16(xrow + kg) : u32x4{0u, 0u, 0u, 0u});
+      const v8bf a1 = __builtin_bit_cast(v8bf, ok ? ld16(xrow + kg + 8) : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(tile + (16 * g + r16) * kRow + kl);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, e4m3x8_to_bf16x8(wv.x, wv.y), acc[g], 0, 0, 0);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, e4m3x8_to_bf16x8(wv.z, wv.w), acc[g], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) red[wid][g][lane] = acc[g];
+  __syncthreads();
+  const int m = 4 * (lane >> 4) + wid;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += red[q][g][lane][wid];
+    const int64_t n = n0 + 16 * g + r16;
+    if (m < M && n < N) store_out(out, int64_t(m) * N + n, s, alpha, out_bf16);
+  }
+}
+
+// 4x4x4 variant for M <= 4: each wave owns 4*G rows and all of K; lane
+// l = 4b + j loads weight row n0 + 4g + j and activation row j at byte/element
+// offset 256 s + 16 b of every 256-wide K step s.
+template <int G, int U>
+__global__ __launch_bounds__(256) void fp8_skinny4_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
+    int out_bf16, int M, int64_t N, int64_t K, float alpha) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t n0 = wave * 4 * G;
+  if (n0 >= N) return;  // uniform per wave; no block-level synchronisation below
+  const int b = lane >> 2, j = lane & 3;
+
+  const uint8_t* wrow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    int64_t n = n0 + 4 * g + j;
+    if (n >= N) n = N - 1;
+    wrow[g] = w + n * K;
+  }
+  const bool xok = j < M;
+  const uint16_t* xrow = x + int64_t(xok ? j : 0) * K;
+
+  v4f acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nsteps = (K + 255) / 256;
+  for (int64_t s0 = 0; s0 < nsteps; s0 += U) {
+    u32x4 wv[U][G];
+    u32x4 xv[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t kb = (s0 + u) * 256 + 16 * b;
+      const bool ok = kb < K;
+#pragma unroll
+      for (int g = 0; g < G; ++g) wv[u][g] = ok ? ld16_stream(wrow[g] + kb) : u32x4{0u, 0u, 0u, 0u};
+      xv[u][0] = ok && xok ? ld16(xrow + kb) : u32x4{0u, 0u, 0u, 0u};
+      xv[u][1] = ok && xok ? ld16(xrow + kb + 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // k = 16 b + 4 q .. +3 of the step
+        const u32x4& xa = xv[u][q >> 1];
+        const u32x2 xp = (q & 1) ? u32x2{xa.z, xa.w} : u32x2{xa.x, xa.y};
+        const v4bf ax = __builtin_bit_cast(v4bf, xp);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t d = wv[u][g][q];
+          const u32x2 wp{e4m3x2_to_bf16x2<false>(d), e4m3x2_to_bf16x2<true>(d)};
+          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ax, __builtin_bit_cast(v4bf, wp), acc[g], 0, 0, 0);
+        }
+      }
+  }
+
+  // acc[g][i] in lane 4b + j = partial out[i][n0 + 4g + j] over block b's
+  // k-range; sum the 16 blocks (lanes j, j + 4, ..., j + 60).
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[g][i];
+      v += __shfl_xor(v, 4, kWave);
+      v += __shfl_xor(v, 8, kWave);
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      acc[g][i] = v;
+    }
+  if (lane < 4) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t n = n0 + 4 * g + j;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < M) store_out(out, int64_t(i) * N + n, acc[g][i], alpha, out_bf16);
+    }
+  }
+}
+
+}  // namespace
+
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s) {
-  // Wider column groups per block once there are enough blocks to go round.
-  const int64_t blocks16 = (N + 15) / 16;
-  if (blocks16 >= int64_t(num_cus) * 16) {
-    const int64_t blocks = (N + 63) / 64;
-    return launch(fp8_skinny_kernel<4, 2>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16,
-                  int(M), N, K, alpha);
+  (void)num_cus;
+  const bool wide_n = N >= 65536;
+  if (M <= 4) {
+    if (wide_n) {
+      const int64_t blocks = (N + 63) / 64;  // 4 waves x 16 rows
+      return launch(fp8_skinny4_kernel<4, 2>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16, int(M), N,
+                    K, alpha);
+    }
+    const int64_t blocks = (N + 15) / 16;  // 4 waves x 4 rows
+    return launch(fp8_skinny4_kernel<1, 4>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16, int(M), N, K,
+                  alpha);
   }
-  return launch(fp8_skinny_kernel<1, 4>, dim3(blocks16), dim3(256), 0, s, w, x, out, out_bf16,
-                int(M), N, K, alpha);
+  if (wide_n)
+    return launch(fp8_skinny_lds_kernel<4, 512>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out, out_bf16,
+                  int(M), N, K, alpha);
+  if (N >= 8192)
+    return launch(fp8_skinny_kernel<4, 2>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out, out_bf16, int(M), N,
+                  K, alpha);
+  return launch(fp8_skinny_kernel<1, 4>, dim3((N + 15) / 16), dim3(256), 0, s, w, x, out, out_bf16, int(M), N, K,
+                alpha);
 }
 
 }  // namespace qlinear

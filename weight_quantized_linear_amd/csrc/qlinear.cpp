@@ -76,9 +76,12 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   if (!aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
   const bool wide = K % 16 == 0 && aligned(w, 16) && aligned(x, 16);
   if (path == QLINEAR_PATH_AUTO) {
+    // Measured on the decode shapes: the vector-ALU GEMV wins for M = 1 and
+    // for M <= 4 below 65536 output features; the matrix-core skinny kernels
+    // win above that and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
     if (M == 1) path = QLINEAR_PATH_GEMV;
+    else if (M <= 4) path = (wide && N >= 65536) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
     else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
-    else if (M <= 4) path = QLINEAR_PATH_GEMV;
     else path = QLINEAR_PATH_TILED;
   }
   switch (path) {
