@@ -19,7 +19,9 @@
 // the current strip's matrix-core work, so HBM traffic overlaps compute.
 // Blocks are mapped to tiles so that each XCD works on a contiguous range of
 // tiles, walked in groups of 8 row tiles per column tile (L2 reuse of the
-// weight tile).
+// weight tile).  This kernel serves any K and alignment and the grouped
+// MoE call; K % 64 == 0 with aligned operands goes to the pipelined
+// direct-to-LDS kernel of gemm_lds.hip.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -297,7 +299,8 @@ __global__ __launch_bounds__(kThreads) void gemm_grouped_fp8_kernel(
 }  // namespace
 
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
-                            int64_t N, int64_t K, float alpha, hipStream_t s) {
+                            int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s) {
+  if (gemm_lds_supported(x, w, w, M, N, K)) return launch_fp8_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
   const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const ActTile A{x, M, K, vec};
@@ -307,7 +310,10 @@ hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int 
 }
 
 hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
-                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, hipStream_t s) {
+                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
+                              hipStream_t s) {
+  if (gemm_lds_supported(x, packed, scales, M, N, K))
+    return launch_nvfp4_gemm_lds(packed, scales, x, out, out_bf16, M, N, K, alpha, num_cus, s);
   const bool vec = (K % 32 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const ActTile A{x, M, K, vec};

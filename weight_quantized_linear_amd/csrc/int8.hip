@@ -16,10 +16,11 @@
 // (an all-zero row gives scale 0 and zero codes).  Rows longer than the
 // register budget are read a second time for the quantisation pass.
 //
-// GEMM: a 256-thread block computes a 128 x 128 int32 tile in 128-byte K
-// strips staged in LDS; four waves (2 x 2, 64 x 64) each run 4 x 4
-// v_mfma_i32_16x16x64_i8 per 64-byte K step.  The next strip's loads are
-// issued before the current strip's matrix-core work.
+// GEMM: K % 128 == 0 with aligned operands runs the pipelined direct-to-LDS
+// kernel of gemm_lds.hip.  This file's kernel serves every other shape: a
+// 256-thread block computes a 128 x 128 int32 tile in 128-byte K strips
+// staged in LDS through registers (zero-filled past K); four waves (2 x 2,
+// 64 x 64) each run 4 x 4 v_mfma_i32_16x16x64_i8 per 64-byte K step.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -283,7 +284,9 @@ hipError_t launch_int8_quantize(const uint16_t* x, int8_t* q, float* a_scale, in
 
 hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, const float* a_scale, const float* b_scale,
                             const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
-                            hipStream_t s) {
+                            int num_cus, hipStream_t s) {
+  if (int8_lds_supported(a, b, M, N, K))
+    return launch_int8_gemm_lds(a, b, a_scale, b_scale, bias, out, out_mode, M, N, K, num_cus, s);
   const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(b) % 16 == 0);
   const I8Operand A{a, M, K, vec}, B{b, N, K, vec};

@@ -106,7 +106,7 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
     return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
   if (path == QLINEAR_PATH_SKINNY)
     return finish(launch_fp8_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, s));
+  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
 }
 
 int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, int out_dtype, int64_t M,
@@ -131,7 +131,7 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
   const int bf16 = out_dtype == QLINEAR_BF16;
   if (path == QLINEAR_PATH_GEMV)
     return finish(launch_nvfp4_gemv(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  return finish(launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, s));
+  return finish(launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s));
 }
 
 }  // namespace
@@ -247,7 +247,7 @@ int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const 
   if (int st = current_device(&num_cus)) return st;
   return finish(launch_int8_gemm(static_cast<const int8_t*>(a), static_cast<const int8_t*>(b), a_scale, b_scale,
                                  mode == 2 ? nullptr : static_cast<const uint16_t*>(bias), out, mode, M, N, K,
-                                 static_cast<hipStream_t>(stream)));
+                                 num_cus, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
