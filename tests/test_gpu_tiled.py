@@ -110,8 +110,9 @@ def test_grouped_untouched_rows_and_guards(q):
 
 
 def test_grouped_single_group_equals_tiled(q):
-    w = synth.fp8_weight((43,), 3 * 512, 1024)[0].reshape(3, 512, 1024)
-    x = synth.bf16_activation((44,), 777, 1024)
+    # Exactly representable sums: the two kernels add in different orders.
+    w = synth.dyadic_fp8_weight((43,), 3 * 512, 1024).reshape(3, 512, 1024)
+    x = synth.dyadic_activation((44,), 777, 1024)
     show("grouped single")
     g = _grouped(q, w, x, np.array([0, 777]), np.array([2]), out_dtype=torch.float32)
     d = q.fp8_gemm(to_dev_u8(np.ascontiguousarray(w[2])), to_dev_bf16(x), out_dtype=torch.float32, path="tiled")

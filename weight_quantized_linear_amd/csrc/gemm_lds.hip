@@ -1,33 +1,51 @@
-// Pipelined LDS GEMMs for large problems:
+// Pipelined LDS GEMMs for large aligned problems:
 //   * W8A16 / W4A16:  out[m, n] = alpha * sum_k x[m, k] * dec(W[n, k]),  K % 64 == 0
-//     ("Matmul2dFp8" page, W8A16 GEMM; "fp4_matmul" page, W4A16 GEMM with the
-//     weight sub-tile dequantised to bfloat16 once per K strip, cooperatively
-//     by the whole block, into on-chip memory)
+//     ("Matmul2dFp8" page, W8A16 GEMM; "fp4_matmul" page, W4A16 GEMM: the
+//     quantized weight tile is staged on chip in its stored form and decoded
+//     to bfloat16 for the matrix cores)
 //   * W8A8 int8:      acc = a @ b^T (int32), out = acc * a_scale[m] * b_scale[n] + bias[n],
-//     K % 128 == 0 ("int8_matmul" page)
+//     K % 64 == 0 ("int8_matmul" page)
 // These are the fast paths for aligned operands; gemm_bf16.hip / int8.hip
 // serve every other shape.
 //
 // gfx950 structure:
-// * A 256-thread block (2 x 2 waves) owns a BM x BN output tile and walks K
-//   in strips of 128 bytes per activation row (64 bf16 or 128 int8 values)
-//   through an S-stage ring of LDS buffers.
-// * Strips are fetched with global_load_lds_dwordx4: the load unit writes
-//   each lane's 16 bytes straight into LDS (lane i at base + 16 i), so no
-//   registers stage the data and S - 1 strips are in flight while the
-//   matrix cores work on the current one.  Which global chunk each lane
-//   fetches is chosen so that the 16-byte chunks of a row land XOR-swizzled
-//   by row index (slot = chunk ^ (row % 8)), which keeps the 16-row fragment
-//   reads free of LDS bank conflicts.  Each lane's address is a uniform
-//   strip base plus a 32-bit offset computed once per block.
-// * The quantized weight strip lands in its stored form (fp8 bytes, or packed
-//   fp4 + E4M3 scales); all 256 threads then decode it once into a bfloat16
-//   tile in the same swizzled layout (exact decode, FP4 block scale applied in
-//   float32), and the waves read both operands with 16-byte LDS reads for
-//   v_mfma_f32_16x16x32_bf16.  int8 strips need no decode and feed
-//   v_mfma_i32_16x16x64_i8 directly.
+// * A 256-thread block (4 waves, WY along M x 4/WY along N) owns a BM x BN
+//   output tile; each wave owns a (BM/WY) x (BN*WY/4) part made of 32 x 32
+//   accumulator blocks for v_mfma_f32_32x32x16_bf16 / v_mfma_i32_32x32x32_i8
+//   (the 32 x 32 forms sustain a higher fraction of the matrix-core peak than
+//   the 16 x 16 ones).
+// * K is walked in strips of 64 values through an S-stage ring of LDS
+//   buffers.  Strips are fetched with global_load_lds_dwordx4 (the load unit
+//   writes each lane's 16 bytes straight into LDS), up to S - 1 strips ahead
+//   of the strip being multiplied, so no registers stage global data.  The
+//   slot of strip s is refilled with strip s + S as soon as every wave has
+//   read strip s.
+// * Rows of every LDS tile are stored with their 16-byte chunks permuted:
+//   chunk c of row r sits in slot c ^ swz(r), swz chosen per row length so
+//   that the 16 rows one ds_read_b128 pass touches hit 16 distinct bank
+//   groups.  The DMA realises the permutation by choosing which global chunk
+//   each lane fetches.
+// * Each strip is two steps; while the matrix cores run step s, the wave
+//   already reads the operands of step s + 1 from LDS (double-buffered
+//   fragment registers).  One block barrier per strip, at the step that
+//   crosses into the next strip.  Scheduling hints spread the DMA issue, the
+//   LDS reads and the weight decode between the MFMAs of a step: with one
+//   wave per SIMD nothing else covers a stalled wave.
+// * The quantized weight is decoded in registers: each lane reads the stored
+//   bytes of its own operand fragment (fp8 bytes, or packed fp4 plus the
+//   E4M3 block scale) and widens them to bfloat16 exactly.  Inside a strip
+//   the contraction index is permuted identically on both operands so that
+//   each lane's stored bytes are one contiguous chunk; the permutation does
+//   not change the sum.
 // * Rows past M or N are fetched from the last valid row (the DMA cannot
-//   zero-fill); they only feed outputs that are not stored.
+//   zero-fill); they only feed outputs that are not stored.  Strips past the
+//   end of K are re-fetches of the last strip, so every wave issues the same
+//   number of loads per strip and the wait counts stay constant.
+// * Output rows are staged through LDS so that full tiles leave with 16-byte
+//   stores.
+#include <type_traits>
+#include <utility>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -39,7 +57,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kRow = 128;  // bytes per row of every LDS operand tile (8 chunks of 16 B)
+constexpr int kMaxLds = 160 * 1024;
 
 __device__ __forceinline__ void dma16(const char* g, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
@@ -48,174 +66,264 @@ __device__ __forceinline__ void dma4(const char* g, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 4, 0, 0);
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
+// Raw buffer over `bytes` bytes at p (stride 0; the last dword is the
+// gfx9-family raw-buffer format word).  Buffer loads address it with a
+// 32-bit per-lane offset plus a uniform offset, so no 64-bit per-lane
+// address registers are needed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const int n = bytes >= (int64_t(1) << 31) - 1 ? 0x7FFFFFFF : int(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
+// Buffer load of 16 (4) bytes per lane straight into LDS (lane i at lds + 16 i (4 i)).
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 4, voff, soff, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding.  The memory clobber keeps the compiler from moving LDS
+// accesses across the wait.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// Wait until every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // the fences would wait for every outstanding vector-memory operation,
-// including the strips still in flight.  The DMA writes of the strip being
-// consumed are complete (wait_vm before the barrier) and the asm statements
-// keep the compiler from moving LDS accesses across the barrier.
+// including the strips still in flight.  Callers wait for what must be
+// complete (their share of the next strip, their own LDS reads) first; the
+// asm statements keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// ---------------------------------------------------------------- 128-byte-row strips
+__device__ __forceinline__ u32x4 lds16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Per-lane DMA offsets for a strip of 128 bytes per row of a row-major
-// operand (row stride `row_bytes`), rows r0 .. r0 + ROWS - 1 clipped to `rows`:
-// instruction q of wave w covers rows 8 (4q + w) .. +7; lane i -> row +i/8,
-// LDS slot i%8 holding global chunk slot ^ (row % 8).
-template <int ROWS>
-struct Rows128 {
-  static constexpr int kInst = ROWS / 32;  // DMA instructions per wave per strip
+// Slot permutation of a row with CPR 16-byte chunks (CPR in {2, 4, 8}): rows
+// r and r' of one 16-row group collide in a bank group only if they also
+// agree in r / (16 / CPR), which the XOR then separates.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  return (r / (16 / CPR)) & (CPR - 1);
+}
+
+// ---------------------------------------------------------------- scheduling hints
+
+// Items of `total` given to slot m when spread evenly over slots [lo, hi).
+constexpr int share(int total, int lo, int hi, int m) {
+  return (m < lo || m >= hi) ? 0 : (m - lo + 1) * total / (hi - lo) - (m - lo) * total / (hi - lo);
+}
+
+template <int NM, int NV, int ND, int NA, int M>
+__device__ __forceinline__ void sched_slot() {
+  // Consecutive ranges of MFMA slots for the LDS reads, the VMEM loads and
+  // the VALU work, in that order; absent classes take no slots.
+  constexpr int parts = (ND > 0) + (NV > 0) + (NA > 0);
+  constexpr int len = parts ? NM / parts : NM;
+  constexpr int d_end = ND ? (NV || NA ? len : NM) : 0;
+  constexpr int v_end = NV ? (NA ? d_end + len : NM) : d_end;
+  constexpr int nd = share(ND, 0, d_end, M);
+  constexpr int nv = share(NV, d_end, v_end, M);
+  constexpr int na = share(NA, v_end, NM, M);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);  // LDS reads
+  if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // VMEM loads
+  if constexpr (na > 0) __builtin_amdgcn_sched_group_barrier(0x002, na, 0);  // VALU
+}
+
+template <int NM, int NV, int ND, int NA, int... Ms>
+__device__ __forceinline__ void sched_region(std::integer_sequence<int, Ms...>) {
+  (sched_slot<NM, NV, ND, NA, Ms>(), ...);
+}
+
+// Order the current scheduling region as NM MFMAs with ND LDS reads spread
+// over the first of them, then NV VMEM loads, then NA VALU instructions (the
+// weight decode, which needs the LDS reads).
+template <int NM, int NV, int ND, int NA>
+__device__ __forceinline__ void interleave() {
+  sched_region<NM, NV, ND, NA>(std::make_integer_sequence<int, NM>{});
+}
+
+// ---------------------------------------------------------------- strip DMA
+
+// One strip of ROWS rows x SB bytes of a row-major operand (row stride `ld`
+// bytes), rows r0 .. r0 + ROWS - 1 clipped to `rows`.  DMA instruction q of
+// wave w fills 1 KB of the tile: rows (64 / CPR)(4q + w) .. +(64 / CPR - 1).
+template <int ROWS, int SB>
+struct StripDma {
+  static constexpr int kCpr = SB / 16;
+  static constexpr int kRowsPerInst = 64 / kCpr;
+  static constexpr int kTotal = ROWS / kRowsPerInst;
+  static_assert(kTotal % 4 == 0, "every wave issues the same number of DMA instructions");
+  static constexpr int kInst = kTotal / 4;  // per wave per strip
   uint32_t off[kInst];
-  __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t row_bytes) {
+  __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t ld) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
     for (int q = 0; q < kInst; ++q) {
-      const int r = 8 * (4 * q + wid) + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
+      const int r = kRowsPerInst * (4 * q + wid) + lane / kCpr;
+      const int c = (lane % kCpr) ^ swz<kCpr>(r);
       int64_t row = r0 + r;
       if (row >= rows) row = rows - 1;
-      off[q] = uint32_t(row * row_bytes + 16 * c);
+      off[q] = uint32_t(row * ld + 16 * c);
     }
   }
   // base = operand start + the strip's byte offset within a row (uniform)
-  __device__ __forceinline__ void fetch(char* lds, const char* base) const {
+  __device__ __forceinline__ void fetch(char* tile, const char* base) const {
     const int wid = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < kInst; ++q) dma16(base + off[q], lds + 8 * (4 * q + wid) * kRow);
+    for (int q = 0; q < kInst; ++q) dma16(base + off[q], tile + (4 * q + wid) * 1024);
   }
-};
-
-// Fragment read of a 128-byte-row tile: lane (r16, g) of 16-row group i,
-// k-step ks reads chunk 4 ks + g of row row0 + 16 i + r16.  (row0 is a
-// multiple of 8, so the swizzle only depends on r16.)
-struct FragAddr {
-  uint32_t base[2];
-  __device__ __forceinline__ void init(int row0, int r16, int g) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) base[ks] = uint32_t((row0 + r16) * kRow + 16 * ((4 * ks + g) ^ (r16 & 7)));
-  }
-  __device__ __forceinline__ u32x4 read(const char* tile, int ks, int i) const {
-    return *reinterpret_cast<const u32x4*>(tile + base[ks] + 16 * kRow * i);
-  }
-};
-
-// ---------------------------------------------------------------- weight strips (bf16 GEMM)
-
-// fp8 strip: 64 bytes per row.  Instruction q of wave w covers rows
-// 16 (4q + w) .. +15: lane i -> row +i/4, raw chunk i%4 (unswizzled: the raw
-// strip is only read by the decode pass).
-template <int BN>
-struct Fp8Strip {
-  static constexpr int kBytes = BN * 64;
-  static constexpr int kInst = BN / 64;
-  uint32_t off[kInst];
-  __device__ __forceinline__ void init(int64_t n0, int64_t N, int64_t K) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-    for (int q = 0; q < kInst; ++q) {
-      const int r = 16 * (4 * q + wid) + (lane >> 2);
-      int64_t n = n0 + r;
-      if (n >= N) n = N - 1;
-      off[q] = uint32_t(n * K + 16 * (lane & 3));
-    }
-  }
-  __device__ __forceinline__ void fetch(char* lds, const uint8_t* w, const uint8_t*, int64_t k0) const {
+  // The same through a buffer resource; soff = the strip's byte offset.
+  __device__ __forceinline__ void fetch(char* tile, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) const {
     const int wid = threadIdx.x >> 6;
-    const char* base = reinterpret_cast<const char*>(w) + k0;
 #pragma unroll
-    for (int q = 0; q < kInst; ++q) dma16(base + off[q], lds + 16 * (4 * q + wid) * 64);
-  }
-  // Decode the raw strip into the swizzled bf16 tile, one raw 16-byte chunk
-  // (two bf16 chunks) per thread per step.
-  __device__ __forceinline__ void decode(char* dst, const char* raw) const {
-#pragma unroll
-    for (int p = 0; p < BN * 4 / kThreads; ++p) {
-      const int id = threadIdx.x + kThreads * p;  // raw chunk id
-      const int r = id >> 2, c = id & 3;          // row, raw chunk (k = 16 c .. +15)
-      const u32x4 v = *reinterpret_cast<const u32x4*>(raw + r * 64 + 16 * c);
-      const u32x4 lo{e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x),
-                     e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y)};
-      const u32x4 hi{e4m3x2_to_bf16x2<false>(v.z), e4m3x2_to_bf16x2<true>(v.z),
-                     e4m3x2_to_bf16x2<false>(v.w), e4m3x2_to_bf16x2<true>(v.w)};
-      *reinterpret_cast<u32x4*>(dst + r * kRow + 16 * ((2 * c) ^ (r & 7))) = lo;
-      *reinterpret_cast<u32x4*>(dst + r * kRow + 16 * ((2 * c + 1) ^ (r & 7))) = hi;
-    }
+    for (int q = 0; q < kInst; ++q) bdma16(rsrc, tile + (4 * q + wid) * 1024, off[q], soff);
   }
 };
 
-// NVFP4 strip: 32 packed bytes + 4 scale bytes per row.  Packed: instruction
-// q of wave w covers rows 32 (4q + w) .. +31, lane i -> row +i/2, raw chunk
-// i%2.  Scales: 32 rows per instruction with lanes 0..31 (one dword each).
-template <int BN>
-struct Nvfp4Strip {
-  static constexpr int kPacked = BN * 32;
-  static constexpr int kBytes = BN * 36;
-  static constexpr int kInst = 2 * (BN / 128);  // packed + scale instructions per wave
-  uint32_t poff[BN / 128], soff[BN / 128];
-  __device__ __forceinline__ void init(int64_t n0, int64_t N, int64_t K) {
+// Four bytes per row (the NVFP4 block scales of one strip); wave w fills
+// rows (ROWS / 4) w .. +(ROWS / 4 - 1), one dword per lane.
+template <int ROWS>
+struct ScaleDma {
+  static constexpr int kPer = ROWS / 4;
+  static_assert(kPer <= 64, "one instruction per wave");
+  static constexpr int kInst = 1;
+  uint32_t off;
+  __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t ld) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-    for (int q = 0; q < BN / 128; ++q) {
-      const int r = 32 * (4 * q + wid) + (lane >> 1);
-      int64_t n = n0 + r;
-      if (n >= N) n = N - 1;
-      poff[q] = uint32_t(n * (K >> 1) + 16 * (lane & 1));
-      int64_t ns = n0 + 32 * (4 * q + wid) + (lane & 31);
-      if (ns >= N) ns = N - 1;
-      soff[q] = uint32_t(ns * (K >> 4));
-    }
+    int64_t row = r0 + kPer * wid + (lane < kPer ? lane : 0);
+    if (row >= rows) row = rows - 1;
+    off = uint32_t(row * ld);
   }
-  __device__ __forceinline__ void fetch(char* lds, const uint8_t* packed, const uint8_t* scales, int64_t k0) const {
+  __device__ __forceinline__ void fetch(char* tile, const char* base) const {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const char* pb = reinterpret_cast<const char*>(packed) + (k0 >> 1);
-    const char* sb = reinterpret_cast<const char*>(scales) + (k0 >> 4);
-#pragma unroll
-    for (int q = 0; q < BN / 128; ++q) {
-      dma16(pb + poff[q], lds + 32 * (4 * q + wid) * 32);
-      if (lane < 32) dma4(sb + soff[q], lds + kPacked + 32 * (4 * q + wid) * 4);
-    }
-  }
-  // Thread t decodes 16 packed bytes (32 weights, two scale blocks) into
-  // four bf16 chunks of the swizzled tile.
-  __device__ __forceinline__ void decode(char* dst, const char* raw) const {
-#pragma unroll
-    for (int p = 0; p < BN * 2 / kThreads; ++p) {
-      const int id = threadIdx.x + kThreads * p;
-      const int r = id >> 1, h = id & 1;  // row, half of the 64-wide strip
-      const u32x4 v = *reinterpret_cast<const u32x4*>(raw + r * 32 + 16 * h);
-      const uint32_t sc = *reinterpret_cast<const uint16_t*>(raw + kPacked + r * 4 + 2 * h);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {  // dword d = weights 8 d .. 8 d + 7 of the half
-        const float s = e4m3_to_f32((sc >> (8 * (d >> 1))) & 0xFFu);
-        const u32x4 o{e2m1x2_to_bf16x2<0>(v[d], s), e2m1x2_to_bf16x2<1>(v[d], s),
-                      e2m1x2_to_bf16x2<2>(v[d], s), e2m1x2_to_bf16x2<3>(v[d], s)};
-        *reinterpret_cast<u32x4*>(dst + r * kRow + 16 * ((4 * h + d) ^ (r & 7))) = o;
-      }
-    }
+    if (lane < kPer) dma4(base + off, tile + kPer * wid * 4);
   }
 };
+
+// ---------------------------------------------------------------- weight policies (bf16 GEMM)
+//
+// A strip covers 64 values of k.  Step t in {0, 1} of a strip runs two MFMA
+// k-slices e in {0, 1} of 8 values per lane; lane half h = lane / 32 holds
+// values k = kmap(t, h, e) .. +7.  The activation fragment of (t, h, e) is
+// the 16-byte chunk kmap / 8 of the activation row.  A policy reads the
+// stored weight bytes of the wave's FN column fragments (`col0` = first
+// column of the wave inside the tile) and decodes them to bfloat16.
 
 struct Fp8Args { const uint8_t* w; };
 struct Nvfp4Args { const uint8_t* packed; const uint8_t* scales; };
 
-template <class WA, int BN> struct StripOf;
-template <int BN> struct StripOf<Fp8Args, BN> { using type = Fp8Strip<BN>; };
-template <int BN> struct StripOf<Nvfp4Args, BN> { using type = Nvfp4Strip<BN>; };
-__device__ __forceinline__ const uint8_t* wptr(Fp8Args a) { return a.w; }
-__device__ __forceinline__ const uint8_t* wptr(Nvfp4Args a) { return a.packed; }
-__device__ __forceinline__ const uint8_t* sptr(Fp8Args) { return nullptr; }
-__device__ __forceinline__ const uint8_t* sptr(Nvfp4Args a) { return a.scales; }
+// fp8: 64 bytes per row per strip (4 chunks).  Step t, half h reads chunk
+// 2t + h (16 values) and feeds bytes 8e .. 8e + 7 to k-slice e.
+template <int BN, int FN>
+struct Fp8Weight {
+  using Args = Fp8Args;
+  static constexpr int kBytes = BN * 64;
+  using Dma = StripDma<BN, 64>;
+  static constexpr int kLoads = Dma::kInst;
+  static constexpr int kReads[2] = {FN, FN};  // LDS reads per step
+  static constexpr int kValu = 8 * FN;        // decode instructions per step
+  __device__ static constexpr int a_chunk(int t, int h, int e) { return 2 * (2 * t + h) + e; }
+
+  Dma dma;
+  const char* w;
+  uint32_t foff[2];
+  u32x4 raw[FN];
+
+  __device__ __forceinline__ void init(Args a, int64_t n0, int64_t N, int64_t K, int col0, int r, int h) {
+    dma.init(n0, N, K);
+    w = reinterpret_cast<const char*>(a.w);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) foff[t] = uint32_t((col0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+  }
+  __device__ __forceinline__ void fetch(char* tile, int64_t strip) const { dma.fetch(tile, w + strip * 64); }
+  template <int T>
+  __device__ __forceinline__ void read(const char* tile) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) raw[j] = lds16(tile + foff[T] + j * 32 * 64);
+  }
+  template <int T>
+  __device__ __forceinline__ void decode(v8bf (&b)[2][FN]) const {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      b[0][j] = e4m3x8_to_bf16x8(raw[j].x, raw[j].y);
+      b[1][j] = e4m3x8_to_bf16x8(raw[j].z, raw[j].w);
+    }
+  }
+};
+
+// NVFP4: 32 packed bytes (64 values) + 4 E4M3 scale bytes per row per strip.
+// Half h reads packed chunk h (k = 32h .. 32h + 31) once per strip; step t
+// uses its bytes 8t .. 8t + 7 (k = 32h + 16t .. +15, scale block 2h + t) and
+// k-slice e the dword 2t + e.
+template <int BN, int FN>
+struct Nvfp4Weight {
+  using Args = Nvfp4Args;
+  static constexpr int kPacked = BN * 32;
+  static constexpr int kBytes = BN * 36;
+  using Dma = StripDma<BN, 32>;
+  using SDma = ScaleDma<BN>;
+  static constexpr int kLoads = Dma::kInst + SDma::kInst;
+  static constexpr int kReads[2] = {2 * FN, 0};
+  static constexpr int kValu = 34 * FN;
+  __device__ static constexpr int a_chunk(int t, int h, int e) { return 4 * h + 2 * t + e; }
+
+  Dma dma;
+  SDma sdma;
+  const char* packed;
+  const char* scales;
+  uint32_t foff, soff, shift;
+  u32x4 raw[FN];
+  uint32_t sc[FN];
+
+  __device__ __forceinline__ void init(Args a, int64_t n0, int64_t N, int64_t K, int col0, int r, int h) {
+    dma.init(n0, N, K / 2);
+    sdma.init(n0, N, K / 16);
+    packed = reinterpret_cast<const char*>(a.packed);
+    scales = reinterpret_cast<const char*>(a.scales);
+    foff = uint32_t((col0 + r) * 32 + 16 * (h ^ swz<2>(r)));
+    soff = uint32_t(kPacked + (col0 + r) * 4);
+    shift = 16 * h;
+  }
+  __device__ __forceinline__ void fetch(char* tile, int64_t strip) const {
+    dma.fetch(tile, packed + strip * 32);
+    sdma.fetch(tile + kPacked, scales + strip * 4);
+  }
+  template <int T>
+  __device__ __forceinline__ void read(const char* tile) {
+    if constexpr (T == 0) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        raw[j] = lds16(tile + foff + j * 32 * 32);
+        sc[j] = *reinterpret_cast<const uint32_t*>(tile + soff + j * 32 * 4);
+      }
+    }
+  }
+  template <int T>
+  __device__ __forceinline__ void decode(v8bf (&b)[2][FN]) const {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float s = e4m3_to_f32((sc[j] >> (shift + 8 * T)) & 0xFFu);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t d = raw[j][2 * T + e];
+        const u32x4 o{e2m1x2_to_bf16x2<0>(d, s), e2m1x2_to_bf16x2<1>(d, s), e2m1x2_to_bf16x2<2>(d, s),
+                      e2m1x2_to_bf16x2<3>(d, s)};
+        b[e][j] = __builtin_bit_cast(v8bf, o);
+      }
+    }
+  }
+};
 
 // Block b -> (row tile, column tile).  Blocks are dealt to the 8 XCDs round
 // robin, so XCD x runs blocks x, x + 8, ...; give it a contiguous range of
@@ -236,288 +344,567 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_m, int64_
   tn = in_group / gm;
 }
 
-// ---------------------------------------------------------------- bf16 GEMM with decoded weight
+// The same mapping in 32-bit arithmetic with the results moved to scalar
+// registers (for kernels that change tiles inside their main loop).
+__device__ __forceinline__ void tile_of_block32(uint32_t b, uint32_t tiles_m, uint32_t tiles_n, int& tm_out,
+                                                int& tn_out) {
+  constexpr uint32_t kXcd = 8, kGroupM = 8;
+  const uint32_t total = tiles_m * tiles_n;
+  const uint32_t q = total / kXcd, r = total % kXcd;
+  const uint32_t xcd = b % kXcd, local = b / kXcd;
+  const uint32_t t = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const uint32_t group = kGroupM * tiles_n;
+  const uint32_t g = t / group;
+  const uint32_t first_m = g * kGroupM;
+  const uint32_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const uint32_t in_group = t - g * group;
+  const uint32_t tn = in_group / gm;
+  const uint32_t tm = first_m + (in_group - tn * gm);
+  tm_out = __builtin_amdgcn_readfirstlane(int(tm));
+  tn_out = __builtin_amdgcn_readfirstlane(int(tn));
+}
 
-template <int BM, int BN, int S, class WS>
-struct Layout {
-  static constexpr int kA = BM * kRow;
-  static constexpr int kStage = kA + WS::kBytes;
-  static constexpr int kDec = S * kStage;  // decoded bf16 weight tile after the ring
-  static constexpr int kLds = kDec + BN * kRow;
-  static constexpr int kLoads = Rows128<BM>::kInst + WS::kInst;
+// ---------------------------------------------------------------- output staging
+
+// OUT: 0 = float32, 1 = bfloat16 (round to nearest even; gfx950 converts in
+// hardware), 2 = int32.
+template <int OUT>
+struct OutT {
+  static constexpr int kBytes = OUT == 1 ? 2 : 4;
 };
 
-template <class WA, int BM, int BN, int S>
-__global__ __launch_bounds__(kThreads) void gemm_lds_kernel(const uint16_t* __restrict__ x, WA wa,
-                                                            void* __restrict__ out, int out_bf16, int64_t M,
-                                                            int64_t N, int64_t K, float alpha) {
-  using WS = typename StripOf<WA, BN>::type;
-  using L = Layout<BM, BN, S, WS>;
-  constexpr int TM = BM / 32, TN = BN / 32;
+template <int OUT>
+__device__ __forceinline__ void put_out(void* out, int64_t i, float v) {
+  if constexpr (OUT == 1) reinterpret_cast<__bf16*>(out)[i] = static_cast<__bf16>(v);
+  else reinterpret_cast<float*>(out)[i] = v;
+}
+
+// ROWS rows of a wave's output part (ROWS x 32 FN elements) staged in LDS
+// so that they leave as 16-byte row segments.  Row stride: the two lane
+// halves of one ds_write (rows 4 apart) hit disjoint banks.
+template <int OUT, int FN, int ROWS>
+struct Slab {
+  static constexpr int kEs = OutT<OUT>::kBytes;
+  static constexpr int kCols = 32 * FN;
+  static constexpr int kStride = kEs * kCols + (kEs == 2 ? 16 : 32);
+  static constexpr int kBytes = ROWS * kStride;
+  static constexpr int kLanesPerRow = kCols * kEs / 16;
+  static constexpr int kChunks = ROWS * kLanesPerRow;  // 16-byte pieces
+  static constexpr int kInst = (kChunks + 63) / 64;
+  static_assert(kLanesPerRow <= 64, "slab row layout");
+
+  char* base;
+  int lane;  // 0 .. 63
+  __device__ __forceinline__ char* at(int row, int col) const { return base + row * kStride + col * kEs; }
+  __device__ __forceinline__ void put_f(int row, int col, float x) const {
+    if constexpr (OUT == 1) *reinterpret_cast<__bf16*>(at(row, col)) = static_cast<__bf16>(x);
+    else *reinterpret_cast<float*>(at(row, col)) = x;
+  }
+  __device__ __forceinline__ void put_i(int row, int col, int32_t x) const {
+    *reinterpret_cast<int32_t*>(at(row, col)) = x;
+  }
+  // Copy the slab to out rows row0 .. row0 + ROWS - 1, columns col0 ..
+  // (row-major, leading dimension N elements, 16-byte aligned rows).  LDS
+  // accesses of one wave complete in order, so the reads see the writes;
+  // the asm barriers keep the compiler from reordering them.
+  __device__ __forceinline__ void flush(void* out, int64_t N, int64_t row0, int64_t col0) const {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int idx = q * 64 + lane;
+      if (kChunks % 64 == 0 || idx < kChunks) {
+        const int row = idx / kLanesPerRow, cb = (idx % kLanesPerRow) * 16;
+        const u32x4 d = lds16(base + row * kStride + cb);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) + ((row0 + row) * N + col0) * kEs + cb) = d;
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+};
+
+// One L2 prefetch per wave: touch one 128-byte line in each of ROWS / 4 rows
+// of a row-major operand with a 4-byte load into a scratch LDS word per lane
+// (the value is never read).
+template <int ROWS>
+struct LinePrefetch {
+  static constexpr int kPer = ROWS / 4;
+  static_assert(kPer <= 64, "one instruction per wave");
+  uint32_t off;
+  __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t ld) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int64_t row = r0 + kPer * wid + (lane < kPer ? lane : 0);
+    if (row >= rows) row = rows - 1;
+    off = uint32_t(row * ld);
+  }
+  __device__ __forceinline__ void touch(char* scratch, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) const {
+    const int lane = threadIdx.x & 63;
+    if (lane < kPer) bdma4(rsrc, scratch + (threadIdx.x >> 6) * 256, off, soff);
+  }
+};
+
+// Raise the kernel's dynamic LDS limit once per kernel, then launch.
+template <auto Kernel, class... Args>
+hipError_t launch_big_lds(int lds_bytes, int64_t blocks, hipStream_t s, Args... args) {
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  return launch(Kernel, dim3(blocks), dim3(kThreads), lds_bytes, s, args...);
+}
+
+int64_t tiles(int64_t M, int64_t N, int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// LDS offset of the output slabs (the int8 epilogue keeps its scales below).
+constexpr int kSlabBase = 4096;
+
+// ---------------------------------------------------------------- bf16 x quantized-weight GEMM
+
+template <template <int, int> class WP, int BM, int BN, int S, int WY>
+struct WqLayout {
+  static constexpr int WX = 4 / WY;
+  static constexpr int FM = BM / WY / 32, FN = BN / WX / 32;
+  using W = WP<BN, FN>;
+  using ADma = StripDma<BM, 128>;
+  static constexpr int kA = BM * 128;
+  static constexpr int kStage = kA + W::kBytes;
+  static constexpr int kLds = S * kStage;
+  static constexpr int kLoads = ADma::kInst + W::kLoads;
+  static_assert(kLds <= kMaxLds, "LDS budget");
+  static_assert((S - 1) * kLoads < 64, "vmcnt range");
+  static_assert(kSlabBase + 4 * Slab<0, FN, 32>::kBytes <= kLds, "output staging fits");
+};
+
+// OUT: 0 = float32, 1 = bfloat16 output.  vec: full tiles may use 16-byte
+// stores (out 16-byte aligned, N * element size a multiple of 16).
+template <template <int, int> class WP, int BM, int BN, int S, int WY, int OUT>
+__global__ __launch_bounds__(kThreads) void wq_gemm_kernel(const uint16_t* __restrict__ x,
+                                                           typename WP<BN, 1>::Args wa, void* __restrict__ out,
+                                                           int64_t M, int64_t N, int64_t K, float alpha, int vec) {
+  using L = WqLayout<WP, BM, BN, S, WY>;
+  using W = typename L::W;
+  constexpr int FM = L::FM, FN = L::FN;
+  constexpr int NM = 2 * FM * FN;  // MFMAs per step
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wy = wid >> 1, wx = wid & 1;
-  const int r16 = lane & 15, g = lane >> 4;
+  const int wy = wid / L::WX, wx = wid % L::WX;
+  const int r = lane & 31, h = lane >> 5;
+  const int row0 = wy * (BM / WY), col0 = wx * (BN / L::WX);
 
-  Rows128<BM> afetch;
-  afetch.init(m0, M, 2 * K);
-  WS wfetch;
-  wfetch.init(n0, N, K);
-  FragAddr fa, fb;
-  fa.init(wy * (BM / 2), r16, g);
-  fb.init(wx * (BN / 2), r16, g);
+  typename L::ADma adma;
+  adma.init(m0, M, 2 * K);
+  W wq;
+  wq.init(wa, n0, N, K, col0, r, h);
+  uint32_t aoff[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      aoff[t][e] = uint32_t((row0 + r) * 128 + 16 * (W::a_chunk(t, h, e) ^ swz<8>(r)));
   const char* xb = reinterpret_cast<const char*>(x);
-  const uint8_t* wp = wptr(wa);
-  const uint8_t* sp = sptr(wa);
-  char* dec = lds + L::kDec;
-
-  v4f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
   const int64_t nk = K / 64;
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s) {
-    if (s < nk) {
-      char* st = lds + s * L::kStage;
-      afetch.fetch(st, xb + int64_t(s) * 128);
-      wfetch.fetch(st + L::kA, wp, sp, int64_t(s) * 64);
-    }
-  }
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    if (nk - 1 - kt >= S - 2) wait_vm<(S - 2) * L::kLoads>();
-    else wait_vm<0>();
-    block_barrier();  // strip kt has landed for every wave; the decoded tile of strip kt-1 is no longer read
-    if (kt + S - 1 < nk) {
-      char* st = lds + ((kt + S - 1) % S) * L::kStage;
-      afetch.fetch(st, xb + (kt + S - 1) * 128);
-      wfetch.fetch(st + L::kA, wp, sp, (kt + S - 1) * 64);
-    }
-    const char* sa = lds + (kt % S) * L::kStage;
-    wfetch.decode(dec, sa + L::kA);
-    block_barrier();  // decoded weight tile complete
-    u32x4 a[2][TM], b[2][TN];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) a[ks][i] = fa.read(sa, ks, i);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) b[ks][j] = fb.read(dec, ks, j);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[ks][i]),
-                                                              __builtin_bit_cast(v8bf, b[ks][j]), acc[i][j], 0, 0,
-                                                              0);
-  }
 
-  // acc[i][j][v] = C[m0 + (BM/2) wy + 16 i + 4 g + v][n0 + (BN/2) wx + 16 j + r16]
+  // Strip s goes to slot s % S; past the end of K it re-fetches the last strip.
+  auto fetch = [&](int64_t s) {
+    char* st = lds + (s % S) * L::kStage;
+    const int64_t src = s < nk ? s : nk - 1;
+    adma.fetch(st, xb + src * 128);
+    wq.fetch(st + L::kA, src);
+  };
+
+  v16f acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + wy * (BM / 2) + 16 * i + 4 * g + v;
-      if (m >= M) continue;
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+
+  u32x4 aX[2][FM], aY[2][FM];
+  v8bf bX[2][FN], bY[2][FN];
+  auto read_a = [&](u32x4 (&a)[2][FM], const char* st, int t) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wx * (BN / 2) + 16 * j + r16;
-        if (n < N) store_out(out, m * N + n, acc[i][j][v], alpha, out_bf16);
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[e][i] = lds16(st + aoff[t][e] + i * 32 * 128);
+  };
+  auto mma = [&](const u32x4 (&a)[2][FM], const v8bf (&b)[2][FN]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a[e][i]), b[e][j], acc[i][j],
+                                                              0, 0, 0);
+  };
+
+#pragma unroll
+  for (int s = 0; s < S; ++s) fetch(s);
+  wait_vm<(S - 1) * L::kLoads>();
+  block_barrier();
+  read_a(aX, lds, 0);
+  wq.template read<0>(lds + L::kA);
+  wq.template decode<0>(bX);
+
+  for (int64_t kt = 0; kt < nk - 1; ++kt) {
+    const char* st = lds + (kt % S) * L::kStage;
+    // step 0: read step 1 of this strip, multiply step 0
+    read_a(aY, st, 1);
+    wq.template read<1>(st + L::kA);
+    mma(aX, bX);
+    wq.template decode<1>(bY);
+    interleave<NM, 0, 2 * FM + W::kReads[1], W::kValu>();
+    // step 1: cross into strip kt + 1 (landed for every wave after the
+    // barrier); slot kt % S is free once every wave's reads of it returned
+    wait_lds();
+    wait_vm<(S - 2) * L::kLoads>();
+    block_barrier();
+    fetch(kt + S);
+    const char* sn = lds + ((kt + 1) % S) * L::kStage;
+    read_a(aX, sn, 0);
+    wq.template read<0>(sn + L::kA);
+    mma(aY, bY);
+    wq.template decode<0>(bX);
+    interleave<NM, L::kLoads, 2 * FM + W::kReads[0], W::kValu>();
+  }
+  {
+    const char* st = lds + ((nk - 1) % S) * L::kStage;
+    read_a(aY, st, 1);
+    wq.template read<1>(st + L::kA);
+    mma(aX, bX);
+    wq.template decode<1>(bY);
+    mma(aY, bY);
+  }
+  wait_vm<0>();  // no LDS write may land after the block ends
+
+  // acc[i][j][v] = C[m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + col0 + 32 j + r]
+  if (vec && m0 + BM <= M && n0 + BN <= N) {
+    block_barrier();  // every wave is done reading the last strip
+    const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) slab.put_f(8 * (v / 4) + 4 * h + (v % 4), 32 * j + r, acc[i][j][v] * alpha);
+      slab.flush(out, N, m0 + row0 + 32 * i, n0 + col0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab reads done before it is rewritten
+    }
+  } else {
+    const int64_t mw = m0 + row0 + 4 * h, nw = n0 + col0 + r;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = mw + 32 * i + 8 * (v / 4) + (v % 4);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = nw + 32 * j;
+          if (n < N) put_out<OUT>(out, m * N + n, acc[i][j][v] * alpha);
+        }
       }
-    }
-}
-
-template <class WA, int BM, int BN, int S>
-hipError_t launch_cfg(const uint16_t* x, WA wa, void* out, int out_bf16, int64_t M, int64_t N, int64_t K,
-                      float alpha, hipStream_t s) {
-  using L = Layout<BM, BN, S, typename StripOf<WA, BN>::type>;
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_lds_kernel<WA, BM, BN, S>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, L::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
   }
-  const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return launch(gemm_lds_kernel<WA, BM, BN, S>, dim3(blocks), dim3(kThreads), L::kLds, s, x, wa, out, out_bf16, M,
-                N, K, alpha);
 }
 
-template <class WA>
-hipError_t launch_shape(const uint16_t* x, WA wa, void* out, int out_bf16, int64_t M, int64_t N, int64_t K,
-                        float alpha, int num_cus, hipStream_t s) {
-  // Largest tile that still gives every CU a block.
-  const int64_t t256 = ((M + 255) / 256) * ((N + 127) / 128);
-  if (t256 >= num_cus) return launch_cfg<WA, 256, 128, 3>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (t128 >= num_cus) return launch_cfg<WA, 128, 128, 4>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  return launch_cfg<WA, 64, 128, 4>(x, wa, out, out_bf16, M, N, K, alpha, s);
+template <template <int, int> class WP, int BM, int BN, int S, int WY>
+hipError_t launch_wq(const uint16_t* x, typename WP<BN, 1>::Args wa, void* out, int out_bf16, int64_t M, int64_t N,
+                     int64_t K, float alpha, hipStream_t s) {
+  using L = WqLayout<WP, BM, BN, S, WY>;
+  const int64_t blocks = tiles(M, N, BM, BN);
+  const int es = out_bf16 ? 2 : 4;
+  const int vec = aligned16(out) && (N * es) % 16 == 0;
+  if (out_bf16)
+    return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, 1>>(L::kLds, blocks, s, x, wa, out, M, N, K, alpha, vec);
+  return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, 0>>(L::kLds, blocks, s, x, wa, out, M, N, K, alpha, vec);
 }
 
 // ---------------------------------------------------------------- W8A8 int8
+//
+// Strips are 64 bytes per row (4 chunks); step t, half h reads chunk 2t + h
+// (k = 32t + 16h .. +15) of both operands.  With every strip fetch a wave
+// also touches, in L2, the lines of the strip D further ahead (A lines for
+// even strips, B lines for odd ones): the blocks of an XCD that share a row
+// or column tile then find it in L2 instead of all waiting for HBM at once.
+template <int BM, int BN, int S, int WY>
+struct I8Layout {
+  static constexpr int WX = 4 / WY;
+  static constexpr int FM = BM / WY / 32, FN = BN / WX / 32;
+  static constexpr int kPrefetchAhead = 4;
+  static constexpr bool kPrefetch = false;
+  using ADma = StripDma<BM, 64>;
+  using BDma = StripDma<BN, 64>;
+  static constexpr int kA = BM * 64;
+  static constexpr int kStage = kA + BN * 64;
+  static constexpr int kRing = S * kStage;
+  static constexpr int kLoads = ADma::kInst + BDma::kInst + (kPrefetch ? 1 : 0);  // + the L2 line prefetch
+  static constexpr int kTouch = kRing;                                           // 1 KB prefetch scratch
+  static constexpr int kLds = kRing + 1024;
+  static_assert(kLds <= kMaxLds, "LDS budget");
+  static_assert((S - 1) * kLoads < 64, "vmcnt range");
+  static_assert((BM + 2 * BN) * 4 <= kSlabBase, "epilogue scales fit");
+  static_assert(kSlabBase + 4 * Slab<0, FN, 32>::kBytes <= kRing, "output staging fits");
+};
 
-// out_mode 0 = fp32, 1 = bf16 (dequantised), 2 = raw int32 accumulators.
-template <int BM, int BN, int S>
+// OUT: 0 = float32, 1 = bfloat16 (dequantised), 2 = raw int32 accumulators.
+template <int BM, int BN, int S, int WY, int OUT>
 __global__ __launch_bounds__(kThreads) void int8_gemm_lds_kernel(const int8_t* __restrict__ a,
                                                                  const int8_t* __restrict__ b,
                                                                  const float* __restrict__ a_scale,
                                                                  const float* __restrict__ b_scale,
                                                                  const uint16_t* __restrict__ bias,
-                                                                 void* __restrict__ out, int out_mode, int64_t M,
-                                                                 int64_t N, int64_t K) {
-  constexpr int kA = BM * kRow, kB = BN * kRow, kStage = kA + kB;
-  constexpr int kLoads = Rows128<BM>::kInst + Rows128<BN>::kInst;
-  constexpr int TM = BM / 32, TN = BN / 32;
+                                                                 void* __restrict__ out, int64_t M, int64_t N,
+                                                                 int64_t K, int vec) {
+  using L = I8Layout<BM, BN, S, WY>;
+  constexpr int FM = L::FM, FN = L::FN;
+  constexpr int NM = FM * FN;  // MFMAs per step
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wy = wid >> 1, wx = wid & 1;
-  const int r16 = lane & 15, g = lane >> 4;
+  const int wy = wid / L::WX, wx = wid % L::WX;
+  const int r = lane & 31, h = lane >> 5;
+  const int row0 = wy * (BM / WY), col0 = wx * (BN / L::WX);
 
-  Rows128<BM> afetch;
-  afetch.init(m0, M, K);
-  Rows128<BN> bfetch;
-  bfetch.init(n0, N, K);
-  FragAddr fa, fb;
-  fa.init(wy * (BM / 2), r16, g);
-  fb.init(wx * (BN / 2), r16, g);
-  const char* pa = reinterpret_cast<const char*>(a);
-  const char* pb = reinterpret_cast<const char*>(b);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, M * K), rb = make_rsrc(b, N * K);
+  typename L::ADma adma;
+  adma.init(m0, M, K);
+  typename L::BDma bdma;
+  bdma.init(n0, N, K);
+  LinePrefetch<BM> pfa;
+  pfa.init(m0, M, K);
+  LinePrefetch<BN> pfb;
+  pfb.init(n0, N, K);
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    aoff[t] = uint32_t((row0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+    boff[t] = uint32_t(L::kA + (col0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+  }
+  const int nk = int(K / 64);
 
-  v4i acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  // Strip s goes to slot s % S; past the end of K it re-fetches the last
+  // strip, so every wave issues kLoads loads per call.
+  auto fetch = [&](int s) {
+    char* st = lds + (s % S) * L::kStage;
+    const int src = s < nk ? s : nk - 1;
+    adma.fetch(st, ra, uint32_t(src) * 64);
+    bdma.fetch(st + L::kA, rb, uint32_t(src) * 64);
+    if constexpr (L::kPrefetch) {
+      int u = src + L::kPrefetchAhead;
+      if (u >= nk) u = nk - 1;
+      if (u & 1) pfb.touch(lds + L::kTouch, rb, uint32_t(u & ~1) * 64);
+      else pfa.touch(lds + L::kTouch, ra, uint32_t(u) * 64);
+    }
+  };
 
-  const int64_t nk = K / 128;
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s) {
-    if (s < nk) {
-      char* st = lds + s * kStage;
-      afetch.fetch(st, pa + int64_t(s) * 128);
-      bfetch.fetch(st + kA, pb + int64_t(s) * 128);
+  // Epilogue scales of this tile, loaded before the main loop so their
+  // latency hides behind it: thread t holds row m0 + t and column n0 + t.
+  float pre_as = 0.f, pre_bs = 0.f, pre_bb = 0.f;
+  if constexpr (OUT != 2) {
+    const int t = threadIdx.x;
+    if (t < BM) pre_as = a_scale[m0 + t < M ? m0 + t : M - 1];
+    if (t < BN) {
+      const int64_t n = n0 + t < N ? n0 + t : N - 1;
+      pre_bs = b_scale[n];
+      pre_bb = bias ? bf16_to_f32(bias[n]) : 0.f;
     }
   }
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    if (nk - 1 - kt >= S - 2) wait_vm<(S - 2) * kLoads>();
-    else wait_vm<0>();
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+
+  u32x4 aX[FM], bX[FN], aY[FM], bY[FN];
+  auto read = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], const char* st, int t) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = lds16(st + aoff[t] + i * 32 * 64);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = lds16(st + boff[t] + j * 32 * 64);
+  };
+  auto mma = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, fa[i]), __builtin_bit_cast(v4i, fb[j]),
+                                                          acc[i][j], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int s = 0; s < S; ++s) fetch(s);
+  wait_vm<(S - 1) * L::kLoads>();
+  block_barrier();
+  read(aX, bX, lds, 0);
+
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const char* st = lds + (kt % S) * L::kStage;
+    read(aY, bY, st, 1);
+    mma(aX, bX);
+    interleave<NM, 0, FM + FN, 0>();
+    // Cross into strip kt + 1 (landed for every wave after the barrier); the
+    // slot of strip kt is free once every wave's reads of it have returned.
+    wait_lds();
+    wait_vm<(S - 2) * L::kLoads>();
     block_barrier();
-    if (kt + S - 1 < nk) {
-      char* st = lds + ((kt + S - 1) % S) * kStage;
-      afetch.fetch(st, pa + (kt + S - 1) * 128);
-      bfetch.fetch(st + kA, pb + (kt + S - 1) * 128);
-    }
-    const char* sa = lds + (kt % S) * kStage;
-    const char* sb = sa + kA;
-    u32x4 xa[2][TM], xb[2][TN];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) xa[ks][i] = fa.read(sa, ks, i);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) xb[ks][j] = fb.read(sb, ks, j);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xa[ks][i]),
-                                                            __builtin_bit_cast(v4i, xb[ks][j]), acc[i][j], 0, 0, 0);
+    fetch(kt + S);
+    read(aX, bX, lds + ((kt + 1) % S) * L::kStage, 0);
+    mma(aY, bY);
+    interleave<NM, L::kLoads, FM + FN, 0>();
   }
+  read(aY, bY, lds + ((nk - 1) % S) * L::kStage, 1);
+  mma(aX, bX);
+  mma(aY, bY);
+  wait_vm<0>();  // no LDS write may land after the block ends
 
-  float bs[TN], bb[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t n = n0 + wx * (BN / 2) + 16 * j + r16;
-    bs[j] = (out_mode != 2 && n < N) ? b_scale[n] : 0.f;
-    bb[j] = (out_mode != 2 && bias && n < N) ? bf16_to_f32(bias[n]) : 0.f;
+  // Scales through LDS (free now): as[BM], bs[BN], bb[BN].
+  float* sh_as = reinterpret_cast<float*>(lds);
+  float* sh_bs = sh_as + BM;
+  float* sh_bb = sh_bs + BN;
+  block_barrier();  // every wave is done reading the last strip
+  if constexpr (OUT != 2) {
+    const int t = threadIdx.x;
+    if (t < BM) sh_as[t] = pre_as;
+    if (t < BN) {
+      sh_bs[t] = pre_bs;
+      sh_bb[t] = pre_bb;
+    }
+    __syncthreads();
   }
+  float bs[FN], bb[FN];
+  if constexpr (OUT != 2) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < FN; ++j) {
+      bs[j] = sh_bs[col0 + r + 32 * j];
+      bb[j] = sh_bb[col0 + r + 32 * j];
+    }
+  }
+  // Element (i, j, v): row m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4, column n0 + col0 + 32 j + r.
+  auto value = [&](int i, int j, int v, const v4f& as4) {
+    return float(acc[i][j][v]) * as4[v % 4] * bs[j] + bb[j];
+  };
+  auto scales4 = [&](int i, int q) {  // a_scale of rows 32 i + 8 q + 4 h .. +3 of the wave part
+    v4f t{};
+    if constexpr (OUT != 2) t = *reinterpret_cast<const v4f*>(sh_as + row0 + 32 * i + 8 * q + 4 * h);
+    return t;
+  };
+
+  if (vec && m0 + BM <= M && n0 + BN <= N) {
+    const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + wy * (BM / 2) + 16 * i + 4 * g + v;
-      if (m >= M) continue;
-      const float as = out_mode != 2 ? a_scale[m] : 0.f;
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wx * (BN / 2) + 16 * j + r16;
-        if (n >= N) continue;
-        const int32_t a32 = acc[i][j][v];
-        if (out_mode == 2) {
-          reinterpret_cast<int32_t*>(out)[m * N + n] = a32;
-        } else {
-          const float val = float(a32) * as * bs[j] + bb[j];
-          if (out_mode == 1) reinterpret_cast<uint16_t*>(out)[m * N + n] = f32_to_bf16(val);
-          else reinterpret_cast<float*>(out)[m * N + n] = val;
+      for (int q = 0; q < 4; ++q) {
+        const v4f as4 = scales4(i, q);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int row = 8 * q + 4 * h + p, col = 32 * j + r;
+            if constexpr (OUT == 2) slab.put_i(row, col, acc[i][j][4 * q + p]);
+            else slab.put_f(row, col, value(i, j, 4 * q + p, as4));
+          }
+      }
+      slab.flush(out, N, m0 + row0 + 32 * i, n0 + col0);
+      wait_lds();  // slab reads done before it is rewritten
+    }
+  } else {
+    const int64_t mw = m0 + row0 + 4 * h, nw = n0 + col0 + r;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f as4 = scales4(i, q);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int64_t m = mw + 32 * i + 8 * q + p;
+          if (m >= M) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = nw + 32 * j;
+            if (n >= N) continue;
+            if constexpr (OUT == 2) reinterpret_cast<int32_t*>(out)[m * N + n] = acc[i][j][4 * q + p];
+            else put_out<OUT>(out, m * N + n, value(i, j, 4 * q + p, as4));
+          }
         }
       }
-    }
+  }
 }
 
-template <int BM, int BN, int S>
+template <int BM, int BN, int S, int WY>
 hipError_t launch_int8_cfg(const int8_t* a, const int8_t* b, const float* sa, const float* sb, const uint16_t* bias,
                            void* out, int out_mode, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  constexpr int kLds = S * (BM + BN) * kRow;
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&int8_gemm_lds_kernel<BM, BN, S>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  using L = I8Layout<BM, BN, S, WY>;
+  const int64_t blocks = tiles(M, N, BM, BN);
+  const int es = out_mode == 1 ? 2 : 4;
+  const int vec = aligned16(out) && (N * es) % 16 == 0;
+  switch (out_mode) {
+    case 0:
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, 0>>(L::kLds, blocks, s, a, b, sa, sb, bias, out, M,
+                                                                    N, K, vec);
+    case 1:
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, 1>>(L::kLds, blocks, s, a, b, sa, sb, bias, out, M,
+                                                                    N, K, vec);
+    default:
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, 2>>(L::kLds, blocks, s, a, b, sa, sb, bias, out, M,
+                                                                    N, K, vec);
   }
-  const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return launch(int8_gemm_lds_kernel<BM, BN, S>, dim3(blocks), dim3(kThreads), kLds, s, a, b, sa, sb, bias, out,
-                out_mode, M, N, K);
 }
-
-bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 }  // namespace
 
 // 32-bit per-lane DMA offsets: every operand must span fewer than 2^32 bytes.
 bool gemm_lds_supported(const void* x, const void* w, const void* scales, int64_t M, int64_t N, int64_t K) {
-  return K % 64 == 0 && aligned16(x) && aligned16(w) && reinterpret_cast<uintptr_t>(scales) % 4 == 0 &&
+  return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && reinterpret_cast<uintptr_t>(scales) % 4 == 0 &&
          M * K * 2 < (int64_t(1) << 32) && N * K < (int64_t(1) << 32);
 }
 
 bool int8_lds_supported(const void* a, const void* b, int64_t M, int64_t N, int64_t K) {
-  return K % 128 == 0 && aligned16(a) && aligned16(b) && M * K < (int64_t(1) << 32) && N * K < (int64_t(1) << 32);
+  return K >= 64 && K % 64 == 0 && aligned16(a) && aligned16(b) && M * K < (int64_t(1) << 32) &&
+         N * K < (int64_t(1) << 32);
 }
 
 hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
                                int64_t K, float alpha, int num_cus, hipStream_t s) {
-  return launch_shape(x, Fp8Args{w}, out, out_bf16, M, N, K, alpha, num_cus, s);
+  const Fp8Args wa{w};
+  // Largest tile that still gives every CU a block.
+  if (tiles(M, N, 256, 256) >= num_cus)
+    return launch_wq<Fp8Weight, 256, 256, 3, 2>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  if (tiles(M, N, 256, 128) >= num_cus)
+    return launch_wq<Fp8Weight, 256, 128, 3, 2>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  return launch_wq<Fp8Weight, 128, 128, 4, 2>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
 hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                                  int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                                  hipStream_t s) {
-  return launch_shape(x, Nvfp4Args{packed, scales}, out, out_bf16, M, N, K, alpha, num_cus, s);
+  const Nvfp4Args wa{packed, scales};
+  // The FP4 decode is the expensive part: waves side by side along N (WY = 1)
+  // so that no two waves decode the same weight rows.
+  if (tiles(M, N, 256, 256) >= num_cus)
+    return launch_wq<Nvfp4Weight, 256, 256, 3, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  if (tiles(M, N, 256, 128) >= num_cus)
+    return launch_wq<Nvfp4Weight, 256, 128, 3, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  return launch_wq<Nvfp4Weight, 128, 128, 4, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
                                 const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
                                 int num_cus, hipStream_t s) {
-  const int64_t t256 = ((M + 255) / 256) * ((N + 127) / 128);
-  if (t256 >= 4 * int64_t(num_cus))
-    return launch_int8_cfg<256, 128, 3>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  if (t128 >= num_cus) return launch_int8_cfg<128, 128, 4>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
-  return launch_int8_cfg<64, 128, 4>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  if (tiles(M, N, 256, 256) >= num_cus)
+    return launch_int8_cfg<256, 256, 4, 2>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  if (tiles(M, N, 256, 128) >= num_cus)
+    return launch_int8_cfg<256, 128, 4, 2>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  return launch_int8_cfg<128, 128, 4, 2>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
 }
 
 }  // namespace qlinear
