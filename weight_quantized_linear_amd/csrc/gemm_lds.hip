@@ -481,18 +481,15 @@ struct WqLayout {
 
 // OUT: 0 = float32, 1 = bfloat16 output.  vec: full tiles may use 16-byte
 // stores (out 16-byte aligned, N * element size a multiple of 16).
+// One BM x BN output tile at (m0, n0) of out[M, N] (leading dimension N).
 template <template <int, int> class WP, int BM, int BN, int S, int WY, int OUT>
-__global__ __launch_bounds__(kThreads) void wq_gemm_kernel(const uint16_t* __restrict__ x,
-                                                           typename WP<BN, 1>::Args wa, void* __restrict__ out,
-                                                           int64_t M, int64_t N, int64_t K, float alpha, int vec) {
+__device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ x, typename WP<BN, 1>::Args wa,
+                                        void* __restrict__ out, int64_t M, int64_t N, int64_t K, float alpha,
+                                        int vec, int64_t m0, int64_t n0) {
   using L = WqLayout<WP, BM, BN, S, WY>;
   using W = typename L::W;
   constexpr int FM = L::FM, FN = L::FN;
   constexpr int NM = 2 * FM * FN;  // MFMAs per step
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  int64_t tm, tn;
-  tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wy = wid / L::WX, wx = wid % L::WX;
   const int r = lane & 31, h = lane >> 5;
@@ -610,6 +607,55 @@ __global__ __launch_bounds__(kThreads) void wq_gemm_kernel(const uint16_t* __res
           if (n < N) put_out<OUT>(out, m * N + n, acc[i][j][v] * alpha);
         }
       }
+  }
+}
+
+template <template <int, int> class WP, int BM, int BN, int S, int WY, int OUT>
+__global__ __launch_bounds__(kThreads) void wq_gemm_kernel(const uint16_t* __restrict__ x,
+                                                           typename WP<BN, 1>::Args wa, void* __restrict__ out,
+                                                           int64_t M, int64_t N, int64_t K, float alpha, int vec) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t tm, tn;
+  tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  wq_tile<WP, BM, BN, S, WY, OUT>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN);
+}
+
+// Grouped MoE W8A16 ("Matmul2dFp8" page, run_grouped): group z = blockIdx.z
+// owns tokens a_offsets[z] .. a_offsets[z + 1] (clipped to T) and multiplies
+// them by expert expert_ids[z]; an id outside 0 .. E - 1 writes zeros, an
+// empty group writes nothing.  blockIdx.x = column tile, blockIdx.y strides
+// over the group's row tiles.
+template <int BM, int BN, int S, int WY, int OUT>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
+                                                                const uint8_t* __restrict__ w,
+                                                                const uint32_t* __restrict__ a_offsets,
+                                                                const int32_t* __restrict__ expert_ids,
+                                                                void* __restrict__ out, int64_t T, int64_t N,
+                                                                int64_t K, int64_t E, int vec) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int kEs = OutT<OUT>::kBytes;
+  const int64_t z = blockIdx.z;
+  int64_t start = a_offsets[z], end = a_offsets[z + 1];
+  start = start < T ? start : T;
+  end = end < T ? end : T;
+  if (end <= start) return;
+  const int64_t rows = end - start;
+  const int64_t e = expert_ids[z];
+  const int64_t n0 = int64_t(blockIdx.x) * BN;
+  char* gout = static_cast<char*>(out) + start * N * kEs;
+  for (int64_t m0 = int64_t(blockIdx.y) * BM; m0 < rows; m0 += int64_t(gridDim.y) * BM) {
+    if (e < 0 || e >= E) {
+      for (int idx = threadIdx.x; idx < BM * BN; idx += kThreads) {
+        const int64_t m = m0 + idx / BN, n = n0 + idx % BN;
+        if (m < rows && n < N) put_out<OUT>(gout, m * N + n, 0.f);
+      }
+      continue;
+    }
+    // Row tiles of one block reuse the LDS ring: wait until every wave is
+    // done with the previous tile.
+    if (m0 != int64_t(blockIdx.y) * BM) __syncthreads();
+    wq_tile<Fp8Weight, BM, BN, S, WY, OUT>(lds, x + start * K, Fp8Args{w + e * N * K}, gout, rows, N, K, 1.f,
+                                            vec, m0, n0);
   }
 }
 
@@ -895,6 +941,44 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   if (tiles(M, N, 256, 128) >= num_cus)
     return launch_wq<Nvfp4Weight, 256, 128, 3, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
   return launch_wq<Nvfp4Weight, 128, 128, 4, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
+}
+
+bool grouped_lds_supported(const void* x, const void* w, int64_t T, int64_t N, int64_t K) {
+  return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && T * K * 2 < (int64_t(1) << 32) &&
+         N * K < (int64_t(1) << 32);
+}
+
+hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
+                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t max_tokens,
+                                  int64_t E, int64_t T, int64_t N, int64_t K, hipStream_t s) {
+  constexpr int BM = 128, BN = 256, S = 4, WY = 2;
+  using L = WqLayout<Fp8Weight, BM, BN, S, WY>;
+  int64_t tiles_m = (max_tokens + BM - 1) / BM;
+  if (tiles_m < 1) tiles_m = 1;
+  if (tiles_m > 65535) tiles_m = 65535;
+  const dim3 grid(unsigned((N + BN - 1) / BN), unsigned(tiles_m), unsigned(G));
+  const int es = out_bf16 ? 2 : 4;
+  const int vec = aligned16(out) && (N * es) % 16 == 0;
+  if (out_bf16) {
+    constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, 1>;
+    static bool attr = false;
+    if (!attr) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, L::kLds);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    return launch(k, grid, dim3(kThreads), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
+  }
+  constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, 0>;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, L::kLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  return launch(k, grid, dim3(kThreads), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
 }
 
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
