@@ -16,8 +16,15 @@
  *   stream).  Every call only enqueues work on it and returns; nothing
  *   synchronises.  Outputs are valid once the stream has reached the work.
  * - Ownership: the caller owns every buffer.  The library keeps no pointer
- *   past the call, allocates no device memory and has no workspace.  Its only
- *   state is a per-device cache of the device's properties.
+ *   past the call.  Its state is a per-device cache of the device's
+ *   properties and one 32 MiB float32 workspace per device, allocated with
+ *   hipMalloc by the first tiled fp8/NVFP4 call on that device that is not
+ *   being captured into a graph, and held until the process ends.  Tiled
+ *   calls with few output tiles (small M) split K over several blocks and
+ *   add the partial sums from that workspace; calls made before it exists
+ *   (or if its allocation failed) use whole-K tiles.  Because the workspace
+ *   is shared, tiled fp8/NVFP4 calls on one device must not run
+ *   concurrently: issue them on one stream, or order the streams.
  * - Errors: the return value (a qlinear_status) is the only error channel.
  *   Arguments are validated before anything is enqueued; on an error nothing
  *   is written.  Device-side contents (offsets, ids) are not validated by the

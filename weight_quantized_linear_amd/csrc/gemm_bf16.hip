@@ -299,8 +299,10 @@ __global__ __launch_bounds__(kThreads) void gemm_grouped_fp8_kernel(
 }  // namespace
 
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
-                            int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s) {
-  if (gemm_lds_supported(x, w, w, M, N, K)) return launch_fp8_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+                            int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
+                            hipStream_t s) {
+  if (gemm_lds_supported(x, w, w, M, N, K))
+    return launch_fp8_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s);
   const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const ActTile A{x, M, K, vec};
@@ -310,10 +312,10 @@ hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int 
 }
 
 hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
-                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                              hipStream_t s) {
+                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
+                              size_t ws_bytes, hipStream_t s) {
   if (gemm_lds_supported(x, packed, scales, M, N, K))
-    return launch_nvfp4_gemm_lds(packed, scales, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+    return launch_nvfp4_gemm_lds(packed, scales, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s);
   const bool vec = (K % 32 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const ActTile A{x, M, K, vec};

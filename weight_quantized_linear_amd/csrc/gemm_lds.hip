@@ -56,7 +56,8 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kThreads = 256;
+// Blocks have NW = 4 or 8 waves (one or two per SIMD; with two, one wave's
+// MFMAs cover the other's stalls); the kernels take NW as a parameter.
 constexpr int kMaxLds = 160 * 1024;
 
 __device__ __forceinline__ void dma16(const char* g, char* lds) {
@@ -156,47 +157,53 @@ __device__ __forceinline__ void interleave() {
 // ---------------------------------------------------------------- strip DMA
 
 // One strip of ROWS rows x SB bytes of a row-major operand (row stride `ld`
-// bytes), rows r0 .. r0 + ROWS - 1 clipped to `rows`.  DMA instruction q of
-// wave w fills 1 KB of the tile: rows (64 / CPR)(4q + w) .. +(64 / CPR - 1).
-template <int ROWS, int SB>
+// bytes), rows r0 .. r0 + ROWS - 1 clipped to `rows`.  The strip's 16-byte
+// chunks are split evenly over the waves; DMA instruction q of wave w covers
+// chunks (q NW + w) kLanes .. +kLanes - 1 (row c / CPR, slot c % CPR).
+template <int ROWS, int SB, int NW>
 struct StripDma {
   static constexpr int kCpr = SB / 16;
-  static constexpr int kRowsPerInst = 64 / kCpr;
-  static constexpr int kTotal = ROWS / kRowsPerInst;
-  static_assert(kTotal % 4 == 0, "every wave issues the same number of DMA instructions");
-  static constexpr int kInst = kTotal / 4;  // per wave per strip
+  static constexpr int kChunks = ROWS * kCpr;
+  static_assert(kChunks % NW == 0, "every wave issues the same number of DMA instructions");
+  static constexpr int kPerWave = kChunks / NW;
+  static constexpr int kLanes = kPerWave >= 64 ? 64 : kPerWave;  // active lanes per instruction
+  static_assert(kPerWave % kLanes == 0, "whole instructions");
+  static constexpr int kInst = kPerWave / kLanes;  // per wave per strip
   uint32_t off[kInst];
   __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t ld) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
     for (int q = 0; q < kInst; ++q) {
-      const int r = kRowsPerInst * (4 * q + wid) + lane / kCpr;
-      const int c = (lane % kCpr) ^ swz<kCpr>(r);
+      const int c = (q * NW + wid) * kLanes + (lane < kLanes ? lane : 0);
+      const int r = c / kCpr;
+      const int g = (c % kCpr) ^ swz<kCpr>(r);
       int64_t row = r0 + r;
       if (row >= rows) row = rows - 1;
-      off[q] = uint32_t(row * ld + 16 * c);
+      off[q] = uint32_t(row * ld + 16 * g);
     }
   }
   // base = operand start + the strip's byte offset within a row (uniform)
   __device__ __forceinline__ void fetch(char* tile, const char* base) const {
-    const int wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < kInst; ++q) dma16(base + off[q], tile + (4 * q + wid) * 1024);
+    for (int q = 0; q < kInst; ++q)
+      if (kLanes == 64 || lane < kLanes) dma16(base + off[q], tile + (q * NW + wid) * kLanes * 16);
   }
   // The same through a buffer resource; soff = the strip's byte offset.
   __device__ __forceinline__ void fetch(char* tile, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) const {
-    const int wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
-    for (int q = 0; q < kInst; ++q) bdma16(rsrc, tile + (4 * q + wid) * 1024, off[q], soff);
+    for (int q = 0; q < kInst; ++q)
+      if (kLanes == 64 || lane < kLanes) bdma16(rsrc, tile + (q * NW + wid) * kLanes * 16, off[q], soff);
   }
 };
 
 // Four bytes per row (the NVFP4 block scales of one strip); wave w fills
-// rows (ROWS / 4) w .. +(ROWS / 4 - 1), one dword per lane.
-template <int ROWS>
+// rows (ROWS / NW) w .. +(ROWS / NW - 1), one dword per lane.
+template <int ROWS, int NW>
 struct ScaleDma {
-  static constexpr int kPer = ROWS / 4;
-  static_assert(kPer <= 64, "one instruction per wave");
+  static constexpr int kPer = ROWS / NW;
+  static_assert(kPer >= 1 && kPer <= 64 && ROWS % NW == 0, "one instruction per wave");
   static constexpr int kInst = 1;
   uint32_t off;
   __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t ld) {
@@ -225,11 +232,11 @@ struct Nvfp4Args { const uint8_t* packed; const uint8_t* scales; };
 
 // fp8: 64 bytes per row per strip (4 chunks).  Step t, half h reads chunk
 // 2t + h (16 values) and feeds bytes 8e .. 8e + 7 to k-slice e.
-template <int BN, int FN>
+template <int BN, int FN, int NW>
 struct Fp8Weight {
   using Args = Fp8Args;
   static constexpr int kBytes = BN * 64;
-  using Dma = StripDma<BN, 64>;
+  using Dma = StripDma<BN, 64, NW>;
   static constexpr int kLoads = Dma::kInst;
   static constexpr int kReads[2] = {FN, FN};  // LDS reads per step
   static constexpr int kValu = 8 * FN;        // decode instructions per step
@@ -266,13 +273,13 @@ struct Fp8Weight {
 // Half h reads packed chunk h (k = 32h .. 32h + 31) once per strip; step t
 // uses its bytes 8t .. 8t + 7 (k = 32h + 16t .. +15, scale block 2h + t) and
 // k-slice e the dword 2t + e.
-template <int BN, int FN>
+template <int BN, int FN, int NW>
 struct Nvfp4Weight {
   using Args = Nvfp4Args;
   static constexpr int kPacked = BN * 32;
   static constexpr int kBytes = BN * 36;
-  using Dma = StripDma<BN, 32>;
-  using SDma = ScaleDma<BN>;
+  using Dma = StripDma<BN, 32, NW>;
+  using SDma = ScaleDma<BN, NW>;
   static constexpr int kLoads = Dma::kInst + SDma::kInst;
   static constexpr int kReads[2] = {2 * FN, 0};
   static constexpr int kValu = 34 * FN;
@@ -422,29 +429,9 @@ struct Slab {
   }
 };
 
-// One L2 prefetch per wave: touch one 128-byte line in each of ROWS / 4 rows
-// of a row-major operand with a 4-byte load into a scratch LDS word per lane
-// (the value is never read).
-template <int ROWS>
-struct LinePrefetch {
-  static constexpr int kPer = ROWS / 4;
-  static_assert(kPer <= 64, "one instruction per wave");
-  uint32_t off;
-  __device__ __forceinline__ void init(int64_t r0, int64_t rows, int64_t ld) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int64_t row = r0 + kPer * wid + (lane < kPer ? lane : 0);
-    if (row >= rows) row = rows - 1;
-    off = uint32_t(row * ld);
-  }
-  __device__ __forceinline__ void touch(char* scratch, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) const {
-    const int lane = threadIdx.x & 63;
-    if (lane < kPer) bdma4(rsrc, scratch + (threadIdx.x >> 6) * 256, off, soff);
-  }
-};
-
 // Raise the kernel's dynamic LDS limit once per kernel, then launch.
 template <auto Kernel, class... Args>
-hipError_t launch_big_lds(int lds_bytes, int64_t blocks, hipStream_t s, Args... args) {
+hipError_t launch_big_lds(int lds_bytes, int64_t blocks, int threads, hipStream_t s, Args... args) {
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
@@ -452,7 +439,7 @@ hipError_t launch_big_lds(int lds_bytes, int64_t blocks, hipStream_t s, Args... 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  return launch(Kernel, dim3(blocks), dim3(kThreads), lds_bytes, s, args...);
+  return launch(Kernel, dim3(blocks), dim3(threads), lds_bytes, s, args...);
 }
 
 int64_t tiles(int64_t M, int64_t N, int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
@@ -464,12 +451,12 @@ constexpr int kSlabBase = 4096;
 
 // ---------------------------------------------------------------- bf16 x quantized-weight GEMM
 
-template <template <int, int> class WP, int BM, int BN, int S, int WY>
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
 struct WqLayout {
-  static constexpr int WX = 4 / WY;
+  static constexpr int WX = NW / WY;
   static constexpr int FM = BM / WY / 32, FN = BN / WX / 32;
-  using W = WP<BN, FN>;
-  using ADma = StripDma<BM, 128>;
+  using W = WP<BN, FN, NW>;
+  using ADma = StripDma<BM, 128, NW>;
   static constexpr int kA = BM * 128;
   static constexpr int kStage = kA + W::kBytes;
   static constexpr int kLds = S * kStage;
@@ -482,11 +469,13 @@ struct WqLayout {
 // OUT: 0 = float32, 1 = bfloat16 output.  vec: full tiles may use 16-byte
 // stores (out 16-byte aligned, N * element size a multiple of 16).
 // One BM x BN output tile at (m0, n0) of out[M, N] (leading dimension N).
-template <template <int, int> class WP, int BM, int BN, int S, int WY, int OUT>
-__device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ x, typename WP<BN, 1>::Args wa,
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
+// Strips s0 .. s0 + ns - 1 of K (64 values each) are summed: all of K for
+// the plain GEMM, one slice for split-K partial sums.
+__device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ x, typename WP<BN, 1, NW>::Args wa,
                                         void* __restrict__ out, int64_t M, int64_t N, int64_t K, float alpha,
-                                        int vec, int64_t m0, int64_t n0) {
-  using L = WqLayout<WP, BM, BN, S, WY>;
+                                        int vec, int64_t m0, int64_t n0, int64_t s0, int64_t ns) {
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
   using W = typename L::W;
   constexpr int FM = L::FM, FN = L::FN;
   constexpr int NM = 2 * FM * FN;  // MFMAs per step
@@ -506,12 +495,12 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
     for (int e = 0; e < 2; ++e)
       aoff[t][e] = uint32_t((row0 + r) * 128 + 16 * (W::a_chunk(t, h, e) ^ swz<8>(r)));
   const char* xb = reinterpret_cast<const char*>(x);
-  const int64_t nk = K / 64;
+  const int64_t nk = ns;
 
-  // Strip s goes to slot s % S; past the end of K it re-fetches the last strip.
+  // Strip s goes to slot s % S; past the last strip it re-fetches the last one.
   auto fetch = [&](int64_t s) {
     char* st = lds + (s % S) * L::kStage;
-    const int64_t src = s < nk ? s : nk - 1;
+    const int64_t src = s0 + (s < nk ? s : nk - 1);
     adma.fetch(st, xb + src * 128);
     wq.fetch(st + L::kA, src);
   };
@@ -610,14 +599,50 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
   }
 }
 
-template <template <int, int> class WP, int BM, int BN, int S, int WY, int OUT>
-__global__ __launch_bounds__(kThreads) void wq_gemm_kernel(const uint16_t* __restrict__ x,
-                                                           typename WP<BN, 1>::Args wa, void* __restrict__ out,
-                                                           int64_t M, int64_t N, int64_t K, float alpha, int vec) {
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void wq_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          typename WP<BN, 1, NW>::Args wa, void* __restrict__ out,
+                                                          int64_t M, int64_t N, int64_t K, float alpha, int vec) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  wq_tile<WP, BM, BN, S, WY, OUT>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN);
+  wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0, K / 64);
+}
+
+// Split-K: block b computes slice b % splits of tile b / splits into the
+// float32 partial-sum plane part + slice * M * N; wq_reduce_kernel adds the
+// planes.  For small M, where whole-K tiles would leave most CUs idle.
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
+__global__ __launch_bounds__(64 * NW) void wq_splitk_kernel(const uint16_t* __restrict__ x,
+                                                            typename WP<BN, 1, NW>::Args wa, float* __restrict__ part,
+                                                            int64_t M, int64_t N, int64_t K, int splits, int vec) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int64_t slice = blockIdx.x % splits, tile = blockIdx.x / splits;
+  int64_t tm, tn;
+  tile_of_block(tile, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int64_t nk = K / 64, per = (nk + splits - 1) / splits;
+  const int64_t s0 = slice * per, ns = nk - s0 < per ? nk - s0 : per;
+  wq_tile<WP, BM, BN, S, WY, NW, 0>(lds, x, wa, part + slice * M * N, M, N, K, 1.f, vec, tm * BM, tn * BN, s0, ns);
+}
+
+// out[i] = alpha * sum over the planes of part[plane][i], four elements per thread.
+template <int OUT>
+__global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict__ part, void* __restrict__ out,
+                                                        int64_t count, int splits, float alpha) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  if (i + 4 <= count && count % 4 == 0) {
+    v4f acc = *reinterpret_cast<const v4f*>(part + i);
+    for (int p = 1; p < splits; ++p) acc += *reinterpret_cast<const v4f*>(part + p * count + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) put_out<OUT>(out, i + e, acc[e] * alpha);
+  } else {
+    for (int64_t j = i; j < i + 4 && j < count; ++j) {
+      float acc = part[j];
+      for (int p = 1; p < splits; ++p) acc += part[p * count + j];
+      put_out<OUT>(out, j, acc * alpha);
+    }
+  }
 }
 
 // Grouped MoE W8A16 ("Matmul2dFp8" page, run_grouped): group z = blockIdx.z
@@ -625,8 +650,8 @@ __global__ __launch_bounds__(kThreads) void wq_gemm_kernel(const uint16_t* __res
 // them by expert expert_ids[z]; an id outside 0 .. E - 1 writes zeros, an
 // empty group writes nothing.  blockIdx.x = column tile, blockIdx.y strides
 // over the group's row tiles.
-template <int BM, int BN, int S, int WY, int OUT>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
+template <int BM, int BN, int S, int WY, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
                                                                 const uint8_t* __restrict__ w,
                                                                 const uint32_t* __restrict__ a_offsets,
                                                                 const int32_t* __restrict__ expert_ids,
@@ -645,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const uint16_t* 
   char* gout = static_cast<char*>(out) + start * N * kEs;
   for (int64_t m0 = int64_t(blockIdx.y) * BM; m0 < rows; m0 += int64_t(gridDim.y) * BM) {
     if (e < 0 || e >= E) {
-      for (int idx = threadIdx.x; idx < BM * BN; idx += kThreads) {
+      for (int idx = threadIdx.x; idx < BM * BN; idx += 64 * NW) {
         const int64_t m = m0 + idx / BN, n = n0 + idx % BN;
         if (m < rows && n < N) put_out<OUT>(gout, m * N + n, 0.f);
       }
@@ -654,60 +679,87 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const uint16_t* 
     // Row tiles of one block reuse the LDS ring: wait until every wave is
     // done with the previous tile.
     if (m0 != int64_t(blockIdx.y) * BM) __syncthreads();
-    wq_tile<Fp8Weight, BM, BN, S, WY, OUT>(lds, x + start * K, Fp8Args{w + e * N * K}, gout, rows, N, K, 1.f,
-                                            vec, m0, n0);
+    wq_tile<Fp8Weight, BM, BN, S, WY, NW, OUT>(lds, x + start * K, Fp8Args{w + e * N * K}, gout, rows, N, K, 1.f,
+                                                vec, m0, n0, 0, K / 64);
   }
 }
 
-template <template <int, int> class WP, int BM, int BN, int S, int WY>
-hipError_t launch_wq(const uint16_t* x, typename WP<BN, 1>::Args wa, void* out, int out_bf16, int64_t M, int64_t N,
-                     int64_t K, float alpha, hipStream_t s) {
-  using L = WqLayout<WP, BM, BN, S, WY>;
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
+hipError_t launch_wq(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, void* out, int out_bf16, int64_t M,
+                     int64_t N, int64_t K, float alpha, hipStream_t s) {
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
   const int64_t blocks = tiles(M, N, BM, BN);
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   if (out_bf16)
-    return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, 1>>(L::kLds, blocks, s, x, wa, out, M, N, K, alpha, vec);
-  return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, 0>>(L::kLds, blocks, s, x, wa, out, M, N, K, alpha, vec);
+    return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N, K,
+                                                                     alpha, vec);
+  return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N, K,
+                                                                   alpha, vec);
+}
+
+// Split-K launch: partial planes in the caller's float32 workspace.
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
+hipError_t launch_wq_splitk(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, void* out, int out_bf16, int64_t M,
+                            int64_t N, int64_t K, float alpha, int splits, float* ws, hipStream_t s) {
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
+  const int64_t blocks = tiles(M, N, BM, BN) * splits;
+  const int vec = aligned16(ws) && (N * 4) % 16 == 0;
+  hipError_t e = launch_big_lds<wq_splitk_kernel<WP, BM, BN, S, WY, NW>>(L::kLds, blocks, 64 * NW, s, x, wa, ws, M, N,
+                                                                          K, splits, vec);
+  if (e != hipSuccess) return e;
+  const int64_t count = M * N, rblocks = (count + 1023) / 1024;
+  if (out_bf16) return launch(wq_reduce_kernel<1>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha);
+  return launch(wq_reduce_kernel<0>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha);
+}
+
+// Number of K slices for a grid of `nt` tiles: enough blocks to cover the
+// CUs, slices of at least 4 strips, partial planes within the workspace.
+int splitk_count(int64_t nt, int64_t M, int64_t N, int64_t K, int num_cus, size_t ws_bytes) {
+  if (nt * 2 > num_cus) return 1;
+  int64_t sp = num_cus / nt;
+  const int64_t nk = K / 64;
+  if (sp > nk / 4) sp = nk / 4;
+  while (sp > 1 && size_t(sp) * size_t(M) * size_t(N) * 4 > ws_bytes) --sp;
+  if (sp < 2) return 1;
+  // The kernel gives slice i the strips i * per .. with per = ceil(nk / sp):
+  // use only as many slices as that fills, so that none is empty.
+  const int64_t per = (nk + sp - 1) / sp;
+  sp = (nk + per - 1) / per;
+  return sp < 2 ? 1 : int(sp);
 }
 
 // ---------------------------------------------------------------- W8A8 int8
 //
 // Strips are 64 bytes per row (4 chunks); step t, half h reads chunk 2t + h
-// (k = 32t + 16h .. +15) of both operands.  With every strip fetch a wave
-// also touches, in L2, the lines of the strip D further ahead (A lines for
-// even strips, B lines for odd ones): the blocks of an XCD that share a row
-// or column tile then find it in L2 instead of all waiting for HBM at once.
-template <int BM, int BN, int S, int WY>
+// (k = 32t + 16h .. +15) of both operands.
+template <int BM, int BN, int S, int WY, int NW>
 struct I8Layout {
-  static constexpr int WX = 4 / WY;
+  static constexpr int WX = NW / WY;
   static constexpr int FM = BM / WY / 32, FN = BN / WX / 32;
-  static constexpr int kPrefetchAhead = 4;
-  static constexpr bool kPrefetch = false;
-  using ADma = StripDma<BM, 64>;
-  using BDma = StripDma<BN, 64>;
+  using ADma = StripDma<BM, 64, NW>;
+  using BDma = StripDma<BN, 64, NW>;
   static constexpr int kA = BM * 64;
   static constexpr int kStage = kA + BN * 64;
-  static constexpr int kRing = S * kStage;
-  static constexpr int kLoads = ADma::kInst + BDma::kInst + (kPrefetch ? 1 : 0);  // + the L2 line prefetch
-  static constexpr int kTouch = kRing;                                           // 1 KB prefetch scratch
-  static constexpr int kLds = kRing + 1024;
+  static constexpr int kLds = S * kStage;
+  static constexpr int kLoads = ADma::kInst + BDma::kInst;
   static_assert(kLds <= kMaxLds, "LDS budget");
   static_assert((S - 1) * kLoads < 64, "vmcnt range");
+  static_assert(FM >= 1 && FN >= 1 && BM % (32 * WY) == 0 && BN % (32 * WX) == 0, "wave layout");
   static_assert((BM + 2 * BN) * 4 <= kSlabBase, "epilogue scales fit");
-  static_assert(kSlabBase + 4 * Slab<0, FN, 32>::kBytes <= kRing, "output staging fits");
+  static_assert(kSlabBase + NW * Slab<0, FN, 32>::kBytes <= kLds, "output staging fits");
 };
 
 // OUT: 0 = float32, 1 = bfloat16 (dequantised), 2 = raw int32 accumulators.
-template <int BM, int BN, int S, int WY, int OUT>
-__global__ __launch_bounds__(kThreads) void int8_gemm_lds_kernel(const int8_t* __restrict__ a,
+template <int BM, int BN, int S, int WY, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __restrict__ a,
                                                                  const int8_t* __restrict__ b,
                                                                  const float* __restrict__ a_scale,
                                                                  const float* __restrict__ b_scale,
                                                                  const uint16_t* __restrict__ bias,
                                                                  void* __restrict__ out, int64_t M, int64_t N,
                                                                  int64_t K, int vec) {
-  using L = I8Layout<BM, BN, S, WY>;
+  using L = I8Layout<BM, BN, S, WY, NW>;
   constexpr int FM = L::FM, FN = L::FN;
   constexpr int NM = FM * FN;  // MFMAs per step
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -724,10 +776,6 @@ __global__ __launch_bounds__(kThreads) void int8_gemm_lds_kernel(const int8_t* _
   adma.init(m0, M, K);
   typename L::BDma bdma;
   bdma.init(n0, N, K);
-  LinePrefetch<BM> pfa;
-  pfa.init(m0, M, K);
-  LinePrefetch<BN> pfb;
-  pfb.init(n0, N, K);
   uint32_t aoff[2], boff[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -743,12 +791,6 @@ __global__ __launch_bounds__(kThreads) void int8_gemm_lds_kernel(const int8_t* _
     const int src = s < nk ? s : nk - 1;
     adma.fetch(st, ra, uint32_t(src) * 64);
     bdma.fetch(st + L::kA, rb, uint32_t(src) * 64);
-    if constexpr (L::kPrefetch) {
-      int u = src + L::kPrefetchAhead;
-      if (u >= nk) u = nk - 1;
-      if (u & 1) pfb.touch(lds + L::kTouch, rb, uint32_t(u & ~1) * 64);
-      else pfa.touch(lds + L::kTouch, ra, uint32_t(u) * 64);
-    }
   };
 
   // Epilogue scales of this tile, loaded before the main loop so their
@@ -886,23 +928,23 @@ __global__ __launch_bounds__(kThreads) void int8_gemm_lds_kernel(const int8_t* _
   }
 }
 
-template <int BM, int BN, int S, int WY>
+template <int BM, int BN, int S, int WY, int NW>
 hipError_t launch_int8_cfg(const int8_t* a, const int8_t* b, const float* sa, const float* sb, const uint16_t* bias,
                            void* out, int out_mode, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  using L = I8Layout<BM, BN, S, WY>;
+  using L = I8Layout<BM, BN, S, WY, NW>;
   const int64_t blocks = tiles(M, N, BM, BN);
   const int es = out_mode == 1 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   switch (out_mode) {
     case 0:
-      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, 0>>(L::kLds, blocks, s, a, b, sa, sb, bias, out, M,
-                                                                    N, K, vec);
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
+                                                                        bias, out, M, N, K, vec);
     case 1:
-      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, 1>>(L::kLds, blocks, s, a, b, sa, sb, bias, out, M,
-                                                                    N, K, vec);
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
+                                                                        bias, out, M, N, K, vec);
     default:
-      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, 2>>(L::kLds, blocks, s, a, b, sa, sb, bias, out, M,
-                                                                    N, K, vec);
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 2>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
+                                                                        bias, out, M, N, K, vec);
   }
 }
 
@@ -920,27 +962,35 @@ bool int8_lds_supported(const void* a, const void* b, int64_t M, int64_t N, int6
 }
 
 hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                               int64_t K, float alpha, int num_cus, hipStream_t s) {
+                               int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s) {
   const Fp8Args wa{w};
+  if (ws) {
+    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
+    if (sp > 1) return launch_wq_splitk<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, s);
+  }
   // Largest tile that still gives every CU a block.
   if (tiles(M, N, 256, 256) >= num_cus)
-    return launch_wq<Fp8Weight, 256, 256, 3, 2>(x, wa, out, out_bf16, M, N, K, alpha, s);
+    return launch_wq<Fp8Weight, 256, 256, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
   if (tiles(M, N, 256, 128) >= num_cus)
-    return launch_wq<Fp8Weight, 256, 128, 3, 2>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  return launch_wq<Fp8Weight, 128, 128, 4, 2>(x, wa, out, out_bf16, M, N, K, alpha, s);
+    return launch_wq<Fp8Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  return launch_wq<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
 hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
-                                 int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                                 hipStream_t s) {
+                                 int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
+                                 size_t ws_bytes, hipStream_t s) {
   const Nvfp4Args wa{packed, scales};
+  if (ws) {
+    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
+    if (sp > 1)
+      return launch_wq_splitk<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, s);
+  }
   // The FP4 decode is the expensive part: waves side by side along N (WY = 1)
-  // so that no two waves decode the same weight rows.
-  if (tiles(M, N, 256, 256) >= num_cus)
-    return launch_wq<Nvfp4Weight, 256, 256, 3, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  if (tiles(M, N, 256, 128) >= num_cus)
-    return launch_wq<Nvfp4Weight, 256, 128, 3, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  return launch_wq<Nvfp4Weight, 128, 128, 4, 1>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  // where the tile is wide enough, so that no two waves decode the same
+  // weight rows.
+  if (tiles(M, N, 128, 256) >= num_cus / 2)
+    return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
 bool grouped_lds_supported(const void* x, const void* w, int64_t T, int64_t N, int64_t K) {
@@ -951,8 +1001,8 @@ bool grouped_lds_supported(const void* x, const void* w, int64_t T, int64_t N, i
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                                   const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t max_tokens,
                                   int64_t E, int64_t T, int64_t N, int64_t K, hipStream_t s) {
-  constexpr int BM = 128, BN = 256, S = 4, WY = 2;
-  using L = WqLayout<Fp8Weight, BM, BN, S, WY>;
+  constexpr int BM = 128, BN = 256, S = 4, WY = 2, NW = 8;
+  using L = WqLayout<Fp8Weight, BM, BN, S, WY, NW>;
   int64_t tiles_m = (max_tokens + BM - 1) / BM;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_m > 65535) tiles_m = 65535;
@@ -960,7 +1010,7 @@ hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uin
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   if (out_bf16) {
-    constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, 1>;
+    constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, NW, 1>;
     static bool attr = false;
     if (!attr) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -968,9 +1018,9 @@ hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uin
       if (e != hipSuccess) return e;
       attr = true;
     }
-    return launch(k, grid, dim3(kThreads), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
+    return launch(k, grid, dim3(64 * NW), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
   }
-  constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, 0>;
+  constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, NW, 0>;
   static bool attr = false;
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -978,17 +1028,19 @@ hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uin
     if (e != hipSuccess) return e;
     attr = true;
   }
-  return launch(k, grid, dim3(kThreads), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
+  return launch(k, grid, dim3(64 * NW), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
 }
 
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
                                 const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
                                 int num_cus, hipStream_t s) {
-  if (tiles(M, N, 256, 256) >= num_cus)
-    return launch_int8_cfg<256, 256, 4, 2>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
-  if (tiles(M, N, 256, 128) >= num_cus)
-    return launch_int8_cfg<256, 128, 4, 2>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
-  return launch_int8_cfg<128, 128, 4, 2>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  // 256 x 256 tiles halve the L2 -> LDS traffic of 256 x 128 ones, which
+  // pays even when some CUs get no tile.
+  if (tiles(M, N, 256, 256) >= num_cus / 2)
+    return launch_int8_cfg<256, 256, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  if (tiles(M, N, 256, 128) >= num_cus / 2)
+    return launch_int8_cfg<256, 128, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  return launch_int8_cfg<128, 128, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
 }
 
 }  // namespace qlinear

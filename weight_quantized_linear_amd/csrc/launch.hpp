@@ -31,22 +31,24 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
 
 // gemm_bf16.hip (dispatches to gemm_lds.hip when K % 64 == 0 and operands are aligned)
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
-                            int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s);
+                            int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
+                            hipStream_t s);
 hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
-                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                              hipStream_t s);
+                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
+                              size_t ws_bytes, hipStream_t s);
 
 // gemm_lds.hip
 bool gemm_lds_supported(const void* x, const void* w, const void* scales, int64_t M, int64_t N, int64_t K);
+// ws / ws_bytes: float32 workspace for split-K partial sums (null: whole-K tiles only).
 hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                               int64_t K, float alpha, int num_cus, hipStream_t s);
+                               int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s);
 bool int8_lds_supported(const void* a, const void* b, int64_t M, int64_t N, int64_t K);
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
                                 const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
                                 int num_cus, hipStream_t s);
 hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
-                                 int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                                 hipStream_t s);
+                                 int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
+                                 size_t ws_bytes, hipStream_t s);
 bool grouped_lds_supported(const void* x, const void* w, int64_t T, int64_t N, int64_t K);
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                                   const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t max_tokens,

@@ -18,15 +18,24 @@ using namespace qlinear;
 
 constexpr int kMaxDevices = 64;
 
+// Split-K partial sums of small-M tiled GEMMs need a float32 workspace; the
+// library holds one per device for the life of the process.  Tiled calls on
+// one device therefore must not run concurrently (one stream, or streams
+// ordered by events), as the header states.
+constexpr size_t kWorkspaceBytes = size_t(32) << 20;
+
 struct DeviceInfo {
   std::atomic<int> state{0};  // 0 unknown, 1 gfx950, 2 other arch, 3 query failed
   int num_cus = 0;
+  std::atomic<float*> ws{nullptr};
+  bool ws_failed = false;
 };
 DeviceInfo g_devices[kMaxDevices];
 std::mutex g_device_mutex;
 
-// Status of the current device, cached per device index; fills num_cus.
-int current_device(int* num_cus) {
+// Status of the current device, cached per device index; fills num_cus (and
+// the device slot, for the workspace).
+int current_device(int* num_cus, DeviceInfo** info = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLINEAR_ERR_DEVICE;
   DeviceInfo& d = g_devices[dev];
@@ -48,7 +57,31 @@ int current_device(int* num_cus) {
   if (st == 3) return QLINEAR_ERR_DEVICE;
   if (st == 2) return QLINEAR_ERR_UNSUPPORTED;
   *num_cus = d.num_cus > 0 ? d.num_cus : 256;
+  if (info) *info = &d;
   return QLINEAR_OK;
+}
+
+// The device's split-K workspace, allocated on the first tiled call that is
+// not being captured into a graph.  Null (whole-K tiles only) before that or
+// if the allocation failed.
+float* workspace(DeviceInfo* d, hipStream_t s) {
+  float* w = d->ws.load(std::memory_order_acquire);
+  if (w) return w;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  std::lock_guard<std::mutex> lock(g_device_mutex);
+  w = d->ws.load(std::memory_order_relaxed);
+  if (!w && !d->ws_failed) {
+    void* p = nullptr;
+    if (hipMalloc(&p, kWorkspaceBytes) == hipSuccess) {
+      w = static_cast<float*>(p);
+      d->ws.store(w, std::memory_order_release);
+    } else {
+      d->ws_failed = true;
+      (void)hipGetLastError();
+    }
+  }
+  return w;
 }
 
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
@@ -97,7 +130,8 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
       return QLINEAR_ERR_INVALID_ARG;
   }
   int num_cus = 0;
-  if (int st = current_device(&num_cus)) return st;
+  DeviceInfo* dev = nullptr;
+  if (int st = current_device(&num_cus, &dev)) return st;
   auto s = static_cast<hipStream_t>(stream);
   auto* wp = static_cast<const uint8_t*>(w);
   auto* xp = static_cast<const uint16_t*>(x);
@@ -106,7 +140,7 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
     return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
   if (path == QLINEAR_PATH_SKINNY)
     return finish(launch_fp8_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
 }
 
 int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, int out_dtype, int64_t M,
@@ -123,7 +157,8 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
     return QLINEAR_ERR_INVALID_ARG;
   }
   int num_cus = 0;
-  if (int st = current_device(&num_cus)) return st;
+  DeviceInfo* dev = nullptr;
+  if (int st = current_device(&num_cus, &dev)) return st;
   auto s = static_cast<hipStream_t>(stream);
   auto* p = static_cast<const uint8_t*>(wp);
   auto* sc = static_cast<const uint8_t*>(ws);
@@ -131,7 +166,8 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
   const int bf16 = out_dtype == QLINEAR_BF16;
   if (path == QLINEAR_PATH_GEMV)
     return finish(launch_nvfp4_gemv(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  return finish(launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  return finish(
+      launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
 }
 
 }  // namespace
