@@ -329,8 +329,8 @@ hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G,
                               int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
                               int num_cus, hipStream_t s) {
-  if (grouped_lds_supported(x, w, T, N, K))
-    return launch_fp8_grouped_lds(w, x, a_offsets, expert_ids, out, out_bf16, G, max_tokens, E, T, N, K, s);
+  if (grouped_lds_supported(x, w, G, T, N, K))
+    return launch_fp8_grouped_lds(w, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
   const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   int64_t tiles_m = (max_tokens + BM - 1) / BM;

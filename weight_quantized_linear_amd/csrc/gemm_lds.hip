@@ -645,30 +645,72 @@ __global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict_
   }
 }
 
-// Grouped MoE W8A16 ("Matmul2dFp8" page, run_grouped): group z = blockIdx.z
-// owns tokens a_offsets[z] .. a_offsets[z + 1] (clipped to T) and multiplies
-// them by expert expert_ids[z]; an id outside 0 .. E - 1 writes zeros, an
-// empty group writes nothing.  blockIdx.x = column tile, blockIdx.y strides
-// over the group's row tiles.
+// Grouped MoE W8A16 ("Matmul2dFp8" page, run_grouped): group z owns tokens
+// a_offsets[z] .. a_offsets[z + 1] (clipped to T) and multiplies them by
+// expert expert_ids[z]; an id outside 0 .. E - 1 writes zeros, an empty group
+// writes nothing.  The work is the list of (row tile of some group, column
+// tile) pairs; the block first builds the exclusive prefix sum of the
+// groups' row-tile counts in LDS (after the strip ring), then walks the list
+// with a grid stride, so only tiles that exist are launched.
 template <int BM, int BN, int S, int WY, int NW, int OUT>
 __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
                                                                 const uint8_t* __restrict__ w,
                                                                 const uint32_t* __restrict__ a_offsets,
                                                                 const int32_t* __restrict__ expert_ids,
-                                                                void* __restrict__ out, int64_t T, int64_t N,
-                                                                int64_t K, int64_t E, int vec) {
+                                                                void* __restrict__ out, int64_t G, int64_t T,
+                                                                int64_t N, int64_t K, int64_t E, int vec) {
+  using L = WqLayout<Fp8Weight, BM, BN, S, WY, NW>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int kEs = OutT<OUT>::kBytes;
-  const int64_t z = blockIdx.z;
-  int64_t start = a_offsets[z], end = a_offsets[z + 1];
-  start = start < T ? start : T;
-  end = end < T ? end : T;
-  if (end <= start) return;
-  const int64_t rows = end - start;
-  const int64_t e = expert_ids[z];
-  const int64_t n0 = int64_t(blockIdx.x) * BN;
-  char* gout = static_cast<char*>(out) + start * N * kEs;
-  for (int64_t m0 = int64_t(blockIdx.y) * BM; m0 < rows; m0 += int64_t(gridDim.y) * BM) {
+  int* cum = reinterpret_cast<int*>(lds + L::kLds);  // cum[z] = row tiles of groups 0 .. z-1; cum[G] = total
+  auto group_span = [&](int64_t z, int64_t& start, int64_t& rows) {
+    int64_t b = a_offsets[z], e = a_offsets[z + 1];
+    b = b < T ? b : T;
+    e = e < T ? e : T;
+    start = b;
+    rows = e > b ? e - b : 0;
+  };
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int64_t z0 = 0; z0 <= G; z0 += 64) {
+      const int64_t z = z0 + lane;
+      int t = 0;
+      if (z < G) {
+        int64_t st, rows;
+        group_span(z, st, rows);
+        t = int((rows + BM - 1) / BM);
+      }
+      int incl = t;  // inclusive prefix sum over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      if (z <= G) cum[z] = carry + incl - t;
+      carry += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  const int64_t n_tiles = (N + BN - 1) / BN;
+  const int64_t work = int64_t(cum[G]) * n_tiles;
+  bool first = true;
+  for (int64_t wi = blockIdx.x; wi < work; wi += gridDim.x) {
+    const int mt = int(wi / n_tiles);
+    const int64_t n0 = (wi % n_tiles) * BN;
+    // Group of row tile mt: the last z with cum[z] <= mt (binary search).
+    int64_t lo = 0, hi = G;  // cum[lo] <= mt < cum[hi]
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (cum[mid] <= mt) lo = mid;
+      else hi = mid;
+    }
+    const int64_t z = lo;
+    int64_t start, rows;
+    group_span(z, start, rows);
+    const int64_t m0 = int64_t(mt - cum[z]) * BM;
+    const int64_t e = expert_ids[z];
+    char* gout = static_cast<char*>(out) + start * N * kEs;
     if (e < 0 || e >= E) {
       for (int idx = threadIdx.x; idx < BM * BN; idx += 64 * NW) {
         const int64_t m = m0 + idx / BN, n = n0 + idx % BN;
@@ -676,9 +718,10 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* _
       }
       continue;
     }
-    // Row tiles of one block reuse the LDS ring: wait until every wave is
-    // done with the previous tile.
-    if (m0 != int64_t(blockIdx.y) * BM) __syncthreads();
+    // Tiles of one block reuse the LDS ring: wait until every wave is done
+    // with the previous tile.
+    if (!first) __syncthreads();
+    first = false;
     wq_tile<Fp8Weight, BM, BN, S, WY, NW, OUT>(lds, x + start * K, Fp8Args{w + e * N * K}, gout, rows, N, K, 1.f,
                                                 vec, m0, n0, 0, K / 64);
   }
@@ -993,42 +1036,42 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
-bool grouped_lds_supported(const void* x, const void* w, int64_t T, int64_t N, int64_t K) {
+// Grouped tile: 64 x 128 with four waves (32 x 64 each); small groups waste
+// little of it, and the weight column tile is shared by every row tile.
+constexpr int kGrpBM = 64, kGrpBN = 128, kGrpS = 4, kGrpWY = 2, kGrpNW = 4;
+using GrpLayout = WqLayout<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
+
+bool grouped_lds_supported(const void* x, const void* w, int64_t G, int64_t T, int64_t N, int64_t K) {
   return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && T * K * 2 < (int64_t(1) << 32) &&
-         N * K < (int64_t(1) << 32);
+         N * K < (int64_t(1) << 32) && GrpLayout::kLds + 4 * (G + 1) <= kMaxLds &&
+         (T + G) * ((N + kGrpBN - 1) / kGrpBN) < (int64_t(1) << 31);
 }
 
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
-                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t max_tokens,
-                                  int64_t E, int64_t T, int64_t N, int64_t K, hipStream_t s) {
-  constexpr int BM = 128, BN = 256, S = 4, WY = 2, NW = 8;
-  using L = WqLayout<Fp8Weight, BM, BN, S, WY, NW>;
-  int64_t tiles_m = (max_tokens + BM - 1) / BM;
-  if (tiles_m < 1) tiles_m = 1;
-  if (tiles_m > 65535) tiles_m = 65535;
-  const dim3 grid(unsigned((N + BN - 1) / BN), unsigned(tiles_m), unsigned(G));
+                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
+                                  int64_t N, int64_t K, int num_cus, hipStream_t s) {
+  constexpr int BM = kGrpBM, BN = kGrpBN, S = kGrpS, WY = kGrpWY, NW = kGrpNW;
+  using L = GrpLayout;
+  // At most ceil(T / BM) + G row tiles exist; two blocks per CU walk them.
+  const int64_t upper = ((T + BM - 1) / BM + G) * ((N + BN - 1) / BN);
+  const int64_t blocks = upper < 2 * int64_t(num_cus) ? (upper > 0 ? upper : 1) : 2 * int64_t(num_cus);
+  const int lds_bytes = int(L::kLds + 4 * (G + 1));
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
-  if (out_bf16) {
-    constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, NW, 1>;
+  auto go = [&](auto kernel) -> hipError_t {
+    // The LDS size depends on G: raise the kernel's limit to the maximum once.
     static bool attr = false;
     if (!attr) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, L::kLds);
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
       if (e != hipSuccess) return e;
       attr = true;
     }
-    return launch(k, grid, dim3(64 * NW), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
-  }
-  constexpr auto k = grouped_gemm_kernel<BM, BN, S, WY, NW, 0>;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, L::kLds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  return launch(k, grid, dim3(64 * NW), L::kLds, s, x, w, a_offsets, expert_ids, out, T, N, K, E, vec);
+    return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, x, w, a_offsets, expert_ids, out, G, T, N, K, E,
+                  vec);
+  };
+  if (out_bf16) return go(grouped_gemm_kernel<BM, BN, S, WY, NW, 1>);
+  return go(grouped_gemm_kernel<BM, BN, S, WY, NW, 0>);
 }
 
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,

@@ -49,10 +49,10 @@ hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* s
 hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                                  int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
                                  size_t ws_bytes, hipStream_t s);
-bool grouped_lds_supported(const void* x, const void* w, int64_t T, int64_t N, int64_t K);
+bool grouped_lds_supported(const void* x, const void* w, int64_t G, int64_t T, int64_t N, int64_t K);
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
-                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t max_tokens,
-                                  int64_t E, int64_t T, int64_t N, int64_t K, hipStream_t s);
+                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
+                                  int64_t N, int64_t K, int num_cus, hipStream_t s);
 hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G,
                               int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
