@@ -58,18 +58,77 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
 def measured_traffic(workload):
     """HBM bytes per dominant launch from the committed rocprofv3 counter
     summary, if it was taken from the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
-        with open(path) as f:
+        with open(traffic_path(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+COPY_BYTES = 256 << 20  # the calibration copy: 256 MiB read + 256 MiB written
+
+
+def counter_per_dispatch(csv_path, counter, name_pred, last=None):
+    """Median over the dispatches whose kernel name satisfies name_pred (the
+    `last` ones by dispatch id, if given) of the counter's value, summed over
+    its instances, in a rocprofv3 counter_collection.csv."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter or not name_pred(row["Kernel_Name"]):
+                continue
+            key = int(row["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for the kernel in {csv_path}")
+    ids = sorted(per)
+    if last:
+        ids = ids[-last:]
+    vals = sorted(per[i] for i in ids)
+    return vals[len(vals) // 2], len(vals)
+
+
+def write_traffic(workload, fetch_csv, write_csv, kernel_substr):
+    """profiles/traffic_<workload>.json from two rocprofv3 --pmc runs of
+    ``bench.py --profile`` (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch):
+    each counter is scaled by what it reads for the calibration copy of
+    COPY_BYTES, so the result is in bytes of HBM traffic per launch."""
+    # The calibration copies are the runtime's device-to-device blit kernel,
+    # the last three of its dispatches (earlier ones are input uploads).
+    is_copy = lambda k: "copyBuffer" in k
+    is_dom = lambda k: kernel_substr in k
+    f_dom, n_f = counter_per_dispatch(fetch_csv, "FETCH_SIZE", is_dom)
+    w_dom, n_w = counter_per_dispatch(write_csv, "WRITE_SIZE", is_dom)
+    f_cp, _ = counter_per_dispatch(fetch_csv, "FETCH_SIZE", is_copy, last=3)
+    w_cp, _ = counter_per_dispatch(write_csv, "WRITE_SIZE", is_copy, last=3)
+    kf = COPY_BYTES / (f_cp * 1024)
+    kw = COPY_BYTES / (w_cp * 1024)
+    fetch_b, write_b = f_dom * 1024 * kf, w_dom * 1024 * kw
+    runs = [f"cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <outdir_{c}> -o p -- python3 <repo>/bench.py "
+            f"--workload {workload} --profile 20" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    runs.append(f"python3 bench.py --workload {workload} --traffic-from <outdir_FETCH_SIZE>/p_counter_collection.csv "
+                f"<outdir_WRITE_SIZE>/p_counter_collection.csv")
+    out = {"workload": workload, "kernel": kernel_substr, "kernel_source_hash": kernel_source_hash(), "commands": runs,
+           "dispatches": {"fetch": n_f, "write": n_w},
+           "fetch_kib_per_dispatch": round(f_dom, 1), "write_kib_per_dispatch": round(w_dom, 1),
+           "copy_fetch_kib": round(f_cp, 1), "copy_write_kib": round(w_cp, 1),
+           "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
+           "traffic_bytes_per_launch": int(round(fetch_b + write_b))}
+    with open(traffic_path(workload), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def blas_threads():
@@ -142,7 +201,8 @@ def build_decode(dev, q, synth, np, torch):
     return dict(
         metric="FP8 W8A16 GEMV M=1 achieved HBM GB/s; dequant-GEMM TFLOP/s; % of roofline",
         unit="GB/s", per="bytes", cases=cases, dominant=dominant, bound="hbm", peak=HBM_PEAK_GBS,
-        kernel="fp8_gemv_wide_kernel<1,2,4> (M=1, N=128256, K=4096)", dtype="f32",
+        kernel="fp8_gemv_wide_kernel<1,2,4> (M=1, N=128256, K=4096)",
+        dtype="f32",
         config={"workload": "fp8_w8a16_decode: M in {1,4,16} x (N,K) in {(4096,4096),(14336,4096),"
                             "(4096,14336),(128256,4096)}, E4M3 weight, bf16 activation, bf16 out"},
         baseline=baseline)
@@ -212,7 +272,8 @@ def build_nvfp4(dev, q, synth, np, torch):
 
     return dict(metric="W4A16 NVFP4 dequant-GEMM TFLOP/s", unit="TFLOP/s", per="work", cases=cases,
                 dominant=cases[2], bound="mfma", peak=BF16_PEAK_TFLOPS,
-                kernel="gemm_dense_kernel<Nvfp4Tile> (M=2048, N=K=4096)", dtype="bf16",
+                kernel="wq_gemm_kernel<Nvfp4Weight, 128, 256> (M=2048, N=K=4096)",
+                dtype="bf16",
                 config={"workload": "nvfp4_w4a16: M in {1,128,2048}, N=K=4096, E2M1 + E4M3 per-16 scales, bf16 out"},
                 baseline=baseline)
 
@@ -249,7 +310,7 @@ def build_grouped(dev, q, synth, np, torch):
 
     return dict(metric="Grouped MoE W8A16 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
                 dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS,
-                kernel="gemm_grouped_fp8_kernel (64 experts, N=1536, K=2048, 4096 tokens)", dtype="bf16",
+                kernel="grouped_gemm_kernel<64, 128> (64 experts, N=1536, K=2048, 4096 tokens)", dtype="bf16",
                 config={"workload": f"grouped_moe_w8a16: E=64 [64,1536,2048] E4M3, T=4096 bf16 tokens, Zipf(1.2) "
                                     f"groups, {len(active)} active experts, {rows_active} active tokens"},
                 baseline=baseline)
@@ -296,7 +357,7 @@ def build_int8(dev, q, synth, np, torch):
 
     return dict(metric="W8A8 int8 GEMM TOPS (quantiser + GEMM + dequant epilogue)", unit="TOPS", per="work",
                 cases=cases, dominant=cases[2], bound="mfma", peak=INT8_PEAK_TOPS,
-                kernel="int8_gemm_kernel (M=4096, N=12288, K=3072)", dtype="i8",
+                kernel="int8_gemm_lds_kernel<256, 256> (M=4096, N=12288, K=3072)", dtype="i8",
                 config={"workload": "w8a8_int8: quantise bf16 [4096,3072] + int8 GEMM N in {3072,12288}, bf16 out"},
                 baseline=baseline)
 
@@ -340,11 +401,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", type=int, default=0, metavar="N",
+                    help="for rocprofv3 counter runs: launch the dominant case N times eagerly plus the "
+                         "calibration copy, print nothing else")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two --profile counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the quantized linear kernels run on a single device "
               f"and this build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.traffic_from:
+        kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
+                   "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel"}
+        write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
+        return
 
     import numpy as np
     import torch
@@ -360,6 +432,18 @@ def main():
     print(f"[bench] {args.workload}: inputs generated and resident in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
     cases = wl["cases"]
+    if args.profile:
+        dom = wl["dominant"]
+        for i in range(args.profile):
+            dom.run(i)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] profile: {args.profile} launches of {dom.name} and 3 calibration copies",
+              file=sys.stderr, flush=True)
+        return
     r = max(c.copies for c in cases)  # steps per graph: consecutive steps read different copies
 
     def steps_fn():
