@@ -31,6 +31,8 @@
 // In every kernel the same k-slot assignment is used for both operands, so
 // the pairing of activation and weight elements does not depend on how the
 // matrix core orders k-slots internally.
+#include <algorithm>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -274,12 +276,209 @@ __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
   }
 }
 
+// Activation-resident variant (K % 256 == 0, the padded activation fits in
+// LDS): v_mfma_f32_4x4x4bf16_1k again, but
+// * a wave owns 4 weight rows at a time and streams 4 KiB of each row per
+//   stage (16 loads of 16 bytes per lane, all issued before any is used), so
+//   every stage requests whole 4 KiB row segments at once, the access that
+//   keeps HBM near its peak; the block's waves walk 4-row groups with a
+//   grid stride;
+// * the activation rows (zero-padded to 4 * MG) are copied once per block
+//   into LDS in the order the matrix cores take them, so that they are read
+//   from HBM/L2 once per block instead of once per weight chunk; 16-byte unit
+//   ((c * MG + p) * 2 + h) * 64 + 4 b + j holds x[4 p + j][256 c + 16 b + 8 h
+//   .. + 8], which lane 4 b + j reads with one conflict-free ds_read_b128;
+// * the 16 instruction blocks' partial sums (one per 16-byte k offset b) are
+//   combined with a reduce-scatter across lanes: each exchange halves the
+//   values a lane holds, so 4 MG values take 4 MG - 1 exchanges, after which
+//   lane 4 b + j holds one finished output.
+template <int MG, int NWB>
+__global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
+    int out_bf16, int M, int N, int K, float alpha) {
+  extern __shared__ __attribute__((aligned(16))) char xs[];
+  constexpr int kU = 16;          // 16-byte loads per lane per stage (4 KiB per row)
+  constexpr int kV = 4 * MG;      // accumulator values per lane
+  constexpr int kChains = 4 / MG; // independent accumulators per m-group
+  constexpr int kLogV = MG == 1 ? 2 : 3;
+  static_assert(MG == 1 || MG == 2, "m-groups");
+
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int b = lane >> 2, j = lane & 3;
+  const int nch = K >> 8;            // 256-wide k chunks (K % 256 == 0)
+  const int groups = (N + 3) >> 2;   // 4-row weight groups
+  const int gstride = gridDim.x * NWB;
+  int g = blockIdx.x * NWB + wid;
+
+  u32x4 wv[kU];
+  auto load_stage = [&](int grp, int c0) {
+    const int n = min(4 * grp + j, N - 1);  // rows past N re-read the last row; never stored
+    const uint8_t* wr = w + int64_t(n) * K + 16 * b;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      wv[u] = c0 + u < nch ? ld16_stream(wr + int64_t(c0 + u) * 256) : u32x4{0u, 0u, 0u, 0u};
+  };
+  if (g < groups) load_stage(g, 0);
+
+  // Activation -> LDS in operand order; rows past M are zeros.
+  {
+    const int units = nch * MG * 128;
+    constexpr int kT = NWB * kWave, kBatch = 4;
+    for (int base = threadIdx.x; base < units; base += kT * kBatch) {
+      u32x4 v[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int u = base + t * kT;
+        const int I = u >> 6, l = u & 63;
+        const int h = I & 1, p = (I >> 1) % MG, c = (I >> 1) / MG;
+        const int m = 4 * p + (l & 3);
+        v[t] = u < units && m < M ? ld16(x + int64_t(m) * K + 256 * c + 16 * (l >> 2) + 8 * h)
+                                  : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int u = base + t * kT;
+        if (u < units) *reinterpret_cast<u32x4*>(xs + 16 * u) = v[t];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (; g < groups; g += gstride) {
+    v4f acc[MG][kChains];
+#pragma unroll
+    for (int p = 0; p < MG; ++p)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) acc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = 0; c0 < nch; c0 += kU) {
+      if (c0 > 0) load_stage(g, c0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (c0 + u < nch) {
+          const char* xp = xs + (int64_t(c0 + u) * MG * 2 * 64 + lane) * 16;
+#pragma unroll
+          for (int p = 0; p < MG; ++p) {
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + p * 2048);
+            const u32x4 xb = *reinterpret_cast<const u32x4*>(xp + p * 2048 + 1024);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4& xh = q < 2 ? xa : xb;
+              const u32x2 ap = (q & 1) ? u32x2{xh.z, xh.w} : u32x2{xh.x, xh.y};
+              const uint32_t d = wv[u][q];
+              const u32x2 bp{e4m3x2_to_bf16x2<false>(d), e4m3x2_to_bf16x2<true>(d)};
+              acc[p][q % kChains] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                  __builtin_bit_cast(v4bf, ap), __builtin_bit_cast(v4bf, bp), acc[p][q % kChains], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    // v[4 p + e] = partial out[4 p + e][4 g + j] over this lane's k offsets.
+    float v[kV];
+#pragma unroll
+    for (int p = 0; p < MG; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) t += acc[p][c][e];
+        v[4 * p + e] = t;
+      }
+    // Reduce-scatter over the 16 blocks (lane bits 2..5, high bit first).
+    int len = kV;
+#pragma unroll
+    for (int bit = 5; bit >= 2; --bit) {
+      const int mask = 1 << bit;
+      const bool upper = (lane & mask) != 0;
+      if (len > 1) {
+        const int half = len >> 1;
+#pragma unroll
+        for (int e = 0; e < kV / 2; ++e) {
+          if (e < half) {
+            const float send = upper ? v[e] : v[e + half];
+            const float keep = upper ? v[e + half] : v[e];
+            v[e] = keep + __shfl_xor(send, mask, kWave);
+          }
+        }
+        len = half;
+      } else {
+        v[0] += __shfl_xor(v[0], mask, kWave);
+      }
+    }
+    // Lane 4 b + j now holds out[b >> (4 - log2 V)][4 g + j] (every 2^(4 - log2 V)-th b stores).
+    const int m = b >> (4 - kLogV);
+    const int n = 4 * g + j;
+    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N)
+      store_out(out, int64_t(m) * N + n, v[0], alpha, out_bf16);
+
+    if (g + gstride < groups) load_stage(g + gstride, 0);
+  }
+}
+
 }  // namespace
+
+namespace {
+
+constexpr int kMaxLds = 160 * 1024;
+
+// Largest activation copy (bytes) the LDS holds: 4 MG padded rows x K bf16.
+int xlds_groups(int64_t M) { return M <= 4 ? 1 : 2; }
+
+template <int MG, int NWB>
+hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
+                           float alpha, int num_cus, hipStream_t s) {
+  auto kern = fp8_skinny_xlds_kernel<MG, NWB>;
+  static bool attr_set = false;  // one flag per instantiation
+  if (!attr_set) {
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds))
+      return e;
+    attr_set = true;
+  }
+  const int64_t lds = int64_t(K / 256) * MG * 2048;
+  const int64_t groups = (int64_t(N) + 3) / 4;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kMaxLds / lds, 16 / NWB));
+  const int64_t blocks = std::min<int64_t>((groups + NWB - 1) / NWB, int64_t(num_cus) * per_cu);
+  return launch(kern, dim3(unsigned(blocks)), dim3(NWB * kWave), size_t(lds), s, w, x, out, out_bf16, M, N, K,
+                alpha);
+}
+
+template <int MG>
+hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
+                       float alpha, int num_cus, hipStream_t s) {
+  // About a dozen waves per CU in total: one large block per CU when there
+  // are enough 4-row groups, otherwise smaller blocks over more CUs.  With
+  // two m-groups the accumulators and activation operands need more than
+  // the 128 registers a 16-wave block leaves each wave, so 12 waves.
+  constexpr int kBig = MG == 1 ? 16 : 12;
+  const int64_t groups = (int64_t(N) + 3) / 4;
+  if (groups >= int64_t(num_cus) * kBig)
+    return launch_xlds_nwb<MG, kBig>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+  if (groups >= int64_t(num_cus) * 8)
+    return launch_xlds_nwb<MG, 8>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+  return launch_xlds_nwb<MG, 4>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+}
+
+}  // namespace
+
+bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&
+         int64_t(xlds_groups(M)) * K * 8 <= kMaxLds;
+}
 
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s) {
-  (void)num_cus;
+  // Measured: for 5 <= M <= 8 the activation-in-LDS kernel wins only at
+  // very many output features, where its whole-row weight bursts matter most.
+  if (fp8_skinny_xlds_supported(M, N, K) && (M <= 4 || N >= 65536)) {
+    switch (xlds_groups(M)) {
+      case 1: return launch_xlds<1>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
+      default: return launch_xlds<2>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
+    }
+  }
   const bool wide_n = N >= 65536;
   if (M <= 4) {
     if (wide_n) {

@@ -650,8 +650,13 @@ __global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict_
 // expert expert_ids[z]; an id outside 0 .. E - 1 writes zeros, an empty group
 // writes nothing.  The work is the list of (row tile of some group, column
 // tile) pairs; the block first builds the exclusive prefix sum of the
-// groups' row-tile counts in LDS (after the strip ring), then walks the list
-// with a grid stride, so only tiles that exist are launched.
+// groups' row-tile counts in LDS (after the strip ring), then walks the list,
+// so only tiles that exist are launched.  The list (group-major, then row
+// tile, then column tile) is cut into 8 contiguous ranges, one per XCD
+// (blocks are dealt to the XCDs round robin, so block b runs on XCD b % 8);
+// the XCD's blocks walk their range with a stride.  All row tiles of one
+// expert then meet its weight tiles in the same L2, which each weight tile
+// is fetched into once.
 template <int BM, int BN, int S, int WY, int NW, int OUT>
 __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
                                                                 const uint8_t* __restrict__ w,
@@ -694,8 +699,12 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* _
   __syncthreads();
   const int64_t n_tiles = (N + BN - 1) / BN;
   const int64_t work = int64_t(cum[G]) * n_tiles;
+  // gridDim.x is a multiple of 8: every XCD has gridDim.x / 8 blocks.
+  constexpr int kXcd = 8;
+  const int64_t xcd = blockIdx.x % kXcd, per_xcd = gridDim.x / kXcd;
+  const int64_t lo = xcd * work / kXcd, hi = (xcd + 1) * work / kXcd;
   bool first = true;
-  for (int64_t wi = blockIdx.x; wi < work; wi += gridDim.x) {
+  for (int64_t wi = lo + blockIdx.x / kXcd; wi < hi; wi += per_xcd) {
     const int mt = int(wi / n_tiles);
     const int64_t n0 = (wi % n_tiles) * BN;
     // Group of row tile mt: the last z with cum[z] <= mt (binary search).
@@ -1053,8 +1062,10 @@ hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uin
   constexpr int BM = kGrpBM, BN = kGrpBN, S = kGrpS, WY = kGrpWY, NW = kGrpNW;
   using L = GrpLayout;
   // At most ceil(T / BM) + G row tiles exist; two blocks per CU walk them.
+  // The kernel splits the work over 8 XCDs: a multiple of 8 blocks.
   const int64_t upper = ((T + BM - 1) / BM + G) * ((N + BN - 1) / BN);
-  const int64_t blocks = upper < 2 * int64_t(num_cus) ? (upper > 0 ? upper : 1) : 2 * int64_t(num_cus);
+  const int64_t want = upper < 2 * int64_t(num_cus) ? upper : 2 * int64_t(num_cus);
+  const int64_t blocks = (want + 7) / 8 * 8;
   const int lds_bytes = int(L::kLds + 4 * (G + 1));
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;

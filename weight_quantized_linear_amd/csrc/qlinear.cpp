@@ -110,10 +110,13 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   const bool wide = K % 16 == 0 && aligned(w, 16) && aligned(x, 16);
   if (path == QLINEAR_PATH_AUTO) {
     // Measured on the decode shapes: the vector-ALU GEMV wins for M = 1 and
-    // for M <= 4 below 65536 output features; the matrix-core skinny kernels
-    // win above that and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
+    // for M <= 4 at few output features; the matrix-core skinny kernels win
+    // from 8192 output features when the activation-in-LDS kernel applies
+    // (from 65536 otherwise) and for 5 <= M <= 16; beyond 16 rows the
+    // LDS-tiled GEMM.
+    const bool many_n = N >= 65536 || (N >= 8192 && fp8_skinny_xlds_supported(M, N, K));
     if (M == 1) path = QLINEAR_PATH_GEMV;
-    else if (M <= 4) path = (wide && N >= 65536) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
+    else if (M <= 4) path = (wide && many_n) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
     else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
     else path = QLINEAR_PATH_TILED;
   }
