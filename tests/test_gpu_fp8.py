@@ -71,7 +71,7 @@ DYADIC = [
     # activation-in-LDS skinny kernel (K % 256 == 0): ragged N, every m-group size, partial last
     # stage of 16 chunks, the largest K each m-group accepts, and small N on few blocks
     ("skinny", 1, 4097, 4352), ("skinny", 8, 1001, 512), ("skinny", 9, 333, 5120),
-    ("skinny", 2, 150, 10240), ("skinny", 13, 70001, 256), ("skinny", 4, 7, 20480),
+    ("skinny", 2, 150, 10240), ("skinny", 13, 70001, 256), ("skinny", 4, 7, 19712),
     ("skinny", 12, 66003, 4096), ("skinny", 5, 1, 256),
 ]
 

@@ -8,14 +8,14 @@
 // on the matrix cores.  The E4M3 -> bf16 widening is exact, so the matrix
 // cores see exactly the decoded weight; accumulation is float32.
 //
-// Three kernels, chosen by shape (all measured on the decode shapes):
+// Four kernels, chosen by shape (all measured on the decode shapes):
 //
-// * fp8_skinny_kernel (v_mfma_f32_16x16x32_bf16): a 256-thread block owns
-//   16*G output columns; its four waves take interleaved 64-byte K steps,
-//   each lane loading one 16-byte chunk per 16-row group per step (row
-//   l % 16, bytes 16*(l/16) .. +15 of the step); the M activation rows
-//   (zero-padded to 16) are the other operand and the four partial
-//   accumulators are summed through LDS at the end.
+// * fp8_skinny_kernel (v_mfma_f32_16x16x32_bf16): a block of NWV waves owns
+//   16*G output columns; its waves take interleaved 64-byte K steps, each
+//   lane loading one 16-byte chunk per 16-row group per step (row l % 16,
+//   bytes 16*(l/16) .. +15 of the step); the M activation rows (zero-padded
+//   to 16) are the other operand and the NWV partial accumulators are summed
+//   through LDS at the end.
 // * fp8_skinny_lds_kernel: the same matrix-core work, but the block first
 //   reads a 64-row x 512-byte weight tile with fully contiguous 16-byte loads
 //   (64 lanes over 1 KiB of two rows) into LDS and the waves take their
@@ -27,6 +27,9 @@
 //   load instruction covers four rows x 256 contiguous bytes.  Block b of the
 //   instruction accumulates the k-range 16b .. of every step, and the 16
 //   block partials are summed across lanes at the end.
+// * fp8_skinny_xlds_kernel (the same instruction, M <= 8, K % 256 == 0): the
+//   activation is copied to LDS once per block and every wave streams whole
+//   4 KiB weight row segments; described at the kernel.
 //
 // In every kernel the same k-slot assignment is used for both operands, so
 // the pairing of activation and weight elements does not depend on how the
@@ -42,11 +45,12 @@ namespace {
 
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
-template <int G, int U>
-__global__ __launch_bounds__(256) void fp8_skinny_kernel(
+template <int G, int U, int NWV>
+__global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
     int out_bf16, int M, int64_t N, int64_t K, float alpha) {
-  constexpr int kWaves = 4;
+  constexpr int kWaves = NWV;
+  static_assert(NWV >= 4, "the final sum uses four waves");
   __shared__ v4f red[kWaves][G][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -101,8 +105,10 @@ __global__ __launch_bounds__(256) void fp8_skinny_kernel(
   for (int g = 0; g < G; ++g) red[wid][g][lane] = acc[g];
   __syncthreads();
 
-  // Thread (wid, lane) finishes accumulator element v = wid of every lane:
-  // D[i][j] with i = m = 4*(lane/16) + wid and j = column n0 + 16g + lane%16.
+  // Thread (wid, lane) of the first four waves finishes accumulator element
+  // v = wid of every lane: D[i][j] with i = m = 4*(lane/16) + wid and
+  // j = column n0 + 16g + lane%16.
+  if (wid >= 4) return;
   const int m = 4 * (lane >> 4) + wid;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -276,13 +282,25 @@ __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
   }
 }
 
+// One reduce-scatter step over lane bit `mask`: the lower lane keeps the
+// sums of v[0 .. H), the upper lane those of v[H .. 2H), both in v[0 .. H).
+template <int H>
+__device__ __forceinline__ void rs_halve(float* v, int lane, int mask) {
+  const bool upper = (lane & mask) != 0;
+#pragma unroll
+  for (int e = 0; e < H; ++e) {
+    const float send = upper ? v[e] : v[e + H];
+    const float keep = upper ? v[e + H] : v[e];
+    v[e] = keep + __shfl_xor(send, mask, kWave);
+  }
+}
+
 // Activation-resident variant (K % 256 == 0, the padded activation fits in
 // LDS): v_mfma_f32_4x4x4bf16_1k again, but
 // * a wave owns 4 weight rows at a time and streams 4 KiB of each row per
 //   stage (16 loads of 16 bytes per lane, all issued before any is used), so
 //   every stage requests whole 4 KiB row segments at once, the access that
-//   keeps HBM near its peak; the block's waves walk 4-row groups with a
-//   grid stride;
+//   keeps HBM near its peak;
 // * the activation rows (zero-padded to 4 * MG) are copied once per block
 //   into LDS in the order the matrix cores take them, so that they are read
 //   from HBM/L2 once per block instead of once per weight chunk; 16-byte unit
@@ -292,7 +310,11 @@ __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
 //   combined with a reduce-scatter across lanes: each exchange halves the
 //   values a lane holds, so 4 MG values take 4 MG - 1 exchanges, after which
 //   lane 4 b + j holds one finished output.
-template <int MG, int NWB>
+// With KS == 1 every wave walks 4-row groups on its own with a grid stride.
+// With few rows (KS > 1) the K chunks of a group are split over KS waves of
+// the block, whose partial outputs are added through LDS in a fixed order;
+// the block then walks NWB / KS groups per round.
+template <int MG, int NWB, int KS>
 __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
     int out_bf16, int M, int N, int K, float alpha) {
@@ -301,14 +323,17 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
   constexpr int kV = 4 * MG;      // accumulator values per lane
   constexpr int kChains = 4 / MG; // independent accumulators per m-group
   constexpr int kLogV = MG == 1 ? 2 : 3;
+  constexpr int kGpb = NWB / KS;  // groups a block runs at once
   static_assert(MG == 1 || MG == 2, "m-groups");
+  static_assert(NWB % KS == 0, "whole groups per block");
 
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int b = lane >> 2, j = lane & 3;
+  const int gi = wid / KS, ks = wid % KS;
   const int nch = K >> 8;            // 256-wide k chunks (K % 256 == 0)
   const int groups = (N + 3) >> 2;   // 4-row weight groups
-  const int gstride = gridDim.x * NWB;
-  int g = blockIdx.x * NWB + wid;
+  const int c_lo = ks * nch / KS, c_hi = (ks + 1) * nch / KS;  // this wave's chunks
+  const int gstride = gridDim.x * kGpb;
 
   u32x4 wv[kU];
   auto load_stage = [&](int grp, int c0) {
@@ -316,9 +341,74 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
     const uint8_t* wr = w + int64_t(n) * K + 16 * b;
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      wv[u] = c0 + u < nch ? ld16_stream(wr + int64_t(c0 + u) * 256) : u32x4{0u, 0u, 0u, 0u};
+      wv[u] = c0 + u < c_hi ? ld16_stream(wr + int64_t(c0 + u) * 256) : u32x4{0u, 0u, 0u, 0u};
   };
-  if (g < groups) load_stage(g, 0);
+
+  // Partial out[m][4 grp + j] over this wave's chunks, for the lane that
+  // ends up holding it (m = b >> (4 - kLogV)); the first stage is loaded.
+  auto run_group = [&](int grp) {
+    v4f acc[MG][kChains];
+#pragma unroll
+    for (int p = 0; p < MG; ++p)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) acc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = c_lo; c0 < c_hi; c0 += kU) {
+      if (c0 > c_lo) load_stage(grp, c0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (c0 + u < c_hi) {
+          const char* xp = xs + (int64_t(c0 + u) * MG * 2 * 64 + lane) * 16;
+#pragma unroll
+          for (int p = 0; p < MG; ++p) {
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + p * 2048);
+            const u32x4 xb = *reinterpret_cast<const u32x4*>(xp + p * 2048 + 1024);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4& xh = q < 2 ? xa : xb;
+              const u32x2 ap = (q & 1) ? u32x2{xh.z, xh.w} : u32x2{xh.x, xh.y};
+              const uint32_t d = wv[u][q];
+              const u32x2 bp{e4m3x2_to_bf16x2<false>(d), e4m3x2_to_bf16x2<true>(d)};
+              acc[p][q % kChains] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                  __builtin_bit_cast(v4bf, ap), __builtin_bit_cast(v4bf, bp), acc[p][q % kChains], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    // v[4 p + e] = partial out[4 p + e][4 grp + j] over this lane's k offsets.
+    float v[kV];
+#pragma unroll
+    for (int p = 0; p < MG; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) t += acc[p][c][e];
+        v[4 * p + e] = t;
+      }
+    // Reduce-scatter over the 16 blocks (lane bits 2..5, high bit first).
+    rs_halve<kV / 2>(v, lane, 32);
+    rs_halve<kV / 4>(v, lane, 16);
+    if constexpr (kV == 8) {
+      rs_halve<1>(v, lane, 8);
+    } else {
+      v[0] += __shfl_xor(v[0], 8, kWave);
+    }
+    v[0] += __shfl_xor(v[0], 4, kWave);
+    return v[0];
+  };
+  // Lane 4 b + j holds out[b >> (4 - log2 V)][4 grp + j]; every
+  // 2^(4 - log2 V)-th b stores.
+  auto store = [&](int grp, float val) {
+    const int m = b >> (4 - kLogV);
+    const int n = 4 * grp + j;
+    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N) store_out(out, int64_t(m) * N + n, val, alpha, out_bf16);
+  };
+
+  int g = blockIdx.x * kGpb + gi;
+  if (g < groups) load_stage(g, c_lo);
 
   // Activation -> LDS in operand order; rows past M are zeros.
   {
@@ -344,76 +434,30 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
   }
   __syncthreads();
 
-  for (; g < groups; g += gstride) {
-    v4f acc[MG][kChains];
-#pragma unroll
-    for (int p = 0; p < MG; ++p)
-#pragma unroll
-      for (int c = 0; c < kChains; ++c) acc[p][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int c0 = 0; c0 < nch; c0 += kU) {
-      if (c0 > 0) load_stage(g, c0);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (c0 + u < nch) {
-          const char* xp = xs + (int64_t(c0 + u) * MG * 2 * 64 + lane) * 16;
-#pragma unroll
-          for (int p = 0; p < MG; ++p) {
-            const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + p * 2048);
-            const u32x4 xb = *reinterpret_cast<const u32x4*>(xp + p * 2048 + 1024);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const u32x4& xh = q < 2 ? xa : xb;
-              const u32x2 ap = (q & 1) ? u32x2{xh.z, xh.w} : u32x2{xh.x, xh.y};
-              const uint32_t d = wv[u][q];
-              const u32x2 bp{e4m3x2_to_bf16x2<false>(d), e4m3x2_to_bf16x2<true>(d)};
-              acc[p][q % kChains] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
-                  __builtin_bit_cast(v4bf, ap), __builtin_bit_cast(v4bf, bp), acc[p][q % kChains], 0, 0, 0);
-            }
-          }
-        }
-      }
+  if constexpr (KS == 1) {
+    for (; g < groups; g += gstride) {
+      const float val = run_group(g);
+      store(g, val);
+      if (g + gstride < groups) load_stage(g + gstride, c_lo);
     }
-
-    // v[4 p + e] = partial out[4 p + e][4 g + j] over this lane's k offsets.
-    float v[kV];
+  } else {
+    // Partial sums of the KS waves of a group meet in red[wid][lane], after
+    // the activation copy.  The round loop bound is uniform over the block.
+    float* red = reinterpret_cast<float*>(xs + int64_t(nch) * MG * 2048);
+    for (int g0 = blockIdx.x * kGpb; g0 < groups; g0 += gstride) {
+      g = g0 + gi;
+      const float val = g < groups ? run_group(g) : 0.f;
+      red[wid * kWave + lane] = val;
+      if (g + gstride < groups) load_stage(g + gstride, c_lo);
+      __syncthreads();
+      if (ks == 0 && g < groups) {
+        float t = red[wid * kWave + lane];
 #pragma unroll
-    for (int p = 0; p < MG; ++p)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float t = 0.f;
-#pragma unroll
-        for (int c = 0; c < kChains; ++c) t += acc[p][c][e];
-        v[4 * p + e] = t;
+        for (int q = 1; q < KS; ++q) t += red[(wid + q) * kWave + lane];
+        store(g, t);
       }
-    // Reduce-scatter over the 16 blocks (lane bits 2..5, high bit first).
-    int len = kV;
-#pragma unroll
-    for (int bit = 5; bit >= 2; --bit) {
-      const int mask = 1 << bit;
-      const bool upper = (lane & mask) != 0;
-      if (len > 1) {
-        const int half = len >> 1;
-#pragma unroll
-        for (int e = 0; e < kV / 2; ++e) {
-          if (e < half) {
-            const float send = upper ? v[e] : v[e + half];
-            const float keep = upper ? v[e + half] : v[e];
-            v[e] = keep + __shfl_xor(send, mask, kWave);
-          }
-        }
-        len = half;
-      } else {
-        v[0] += __shfl_xor(v[0], mask, kWave);
-      }
+      __syncthreads();  // red is rewritten next round
     }
-    // Lane 4 b + j now holds out[b >> (4 - log2 V)][4 g + j] (every 2^(4 - log2 V)-th b stores).
-    const int m = b >> (4 - kLogV);
-    const int n = 4 * g + j;
-    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N)
-      store_out(out, int64_t(m) * N + n, v[0], alpha, out_bf16);
-
-    if (g + gstride < groups) load_stage(g + gstride, 0);
   }
 }
 
@@ -423,13 +467,21 @@ namespace {
 
 constexpr int kMaxLds = 160 * 1024;
 
+// fp8_skinny_kernel: a block of NWV waves per 16 G output columns.
+template <int G, int U, int NWV>
+hipError_t launch_skinny16(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                           int64_t K, float alpha, hipStream_t s) {
+  return launch(fp8_skinny_kernel<G, U, NWV>, dim3((N + 16 * G - 1) / (16 * G)), dim3(NWV * kWave), 0, s, w, x, out,
+                out_bf16, int(M), N, K, alpha);
+}
+
 // Largest activation copy (bytes) the LDS holds: 4 MG padded rows x K bf16.
 int xlds_groups(int64_t M) { return M <= 4 ? 1 : 2; }
 
-template <int MG, int NWB>
+template <int MG, int NWB, int KS>
 hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
                            float alpha, int num_cus, hipStream_t s) {
-  auto kern = fp8_skinny_xlds_kernel<MG, NWB>;
+  auto kern = fp8_skinny_xlds_kernel<MG, NWB, KS>;
   static bool attr_set = false;  // one flag per instantiation
   if (!attr_set) {
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -437,10 +489,11 @@ hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int o
       return e;
     attr_set = true;
   }
-  const int64_t lds = int64_t(K / 256) * MG * 2048;
+  const int64_t lds = int64_t(K / 256) * MG * 2048 + (KS > 1 ? NWB * kWave * 4 : 0);
   const int64_t groups = (int64_t(N) + 3) / 4;
+  constexpr int kGpb = NWB / KS;
   const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kMaxLds / lds, 16 / NWB));
-  const int64_t blocks = std::min<int64_t>((groups + NWB - 1) / NWB, int64_t(num_cus) * per_cu);
+  const int64_t blocks = std::min<int64_t>((groups + kGpb - 1) / kGpb, int64_t(num_cus) * per_cu);
   return launch(kern, dim3(unsigned(blocks)), dim3(NWB * kWave), size_t(lds), s, w, x, out, out_bf16, M, N, K,
                 alpha);
 }
@@ -449,23 +502,26 @@ template <int MG>
 hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
                        float alpha, int num_cus, hipStream_t s) {
   // About a dozen waves per CU in total: one large block per CU when there
-  // are enough 4-row groups, otherwise smaller blocks over more CUs.  With
+  // are enough 4-row groups, otherwise smaller blocks over more CUs, and
+  // with few groups the K chunks of each group split over four waves.  With
   // two m-groups the accumulators and activation operands need more than
-  // the 128 registers a 16-wave block leaves each wave, so 12 waves.
+  // the 128 registers a 16-wave block leaves each wave, so 12 (or 8) waves.
   constexpr int kBig = MG == 1 ? 16 : 12;
   const int64_t groups = (int64_t(N) + 3) / 4;
   if (groups >= int64_t(num_cus) * kBig)
-    return launch_xlds_nwb<MG, kBig>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+    return launch_xlds_nwb<MG, kBig, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
   if (groups >= int64_t(num_cus) * 8)
-    return launch_xlds_nwb<MG, 8>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
-  return launch_xlds_nwb<MG, 4>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+    return launch_xlds_nwb<MG, 8, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+  if (K >= 4096)
+    return launch_xlds_nwb<MG, 8, 4>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+  return launch_xlds_nwb<MG, 4, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
 }
 
 }  // namespace
 
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&
-         int64_t(xlds_groups(M)) * K * 8 <= kMaxLds;
+         int64_t(xlds_groups(M)) * K * 8 + 16 * kWave * 4 <= kMaxLds;
 }
 
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
@@ -493,11 +549,8 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
   if (wide_n)
     return launch(fp8_skinny_lds_kernel<4, 512>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out, out_bf16,
                   int(M), N, K, alpha);
-  if (N >= 8192)
-    return launch(fp8_skinny_kernel<4, 2>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out, out_bf16, int(M), N,
-                  K, alpha);
-  return launch(fp8_skinny_kernel<1, 4>, dim3((N + 15) / 16), dim3(256), 0, s, w, x, out, out_bf16, int(M), N, K,
-                alpha);
+  if (N >= 8192) return launch_skinny16<4, 2, 16>(w, x, out, out_bf16, M, N, K, alpha, s);
+  return launch_skinny16<1, 4, 16>(w, x, out, out_bf16, M, N, K, alpha, s);
 }
 
 }  // namespace qlinear

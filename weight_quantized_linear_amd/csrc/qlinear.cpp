@@ -109,14 +109,15 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   if (!aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
   const bool wide = K % 16 == 0 && aligned(w, 16) && aligned(x, 16);
   if (path == QLINEAR_PATH_AUTO) {
-    // Measured on the decode shapes: the vector-ALU GEMV wins for M = 1 and
-    // for M <= 4 at few output features; the matrix-core skinny kernels win
-    // from 8192 output features when the activation-in-LDS kernel applies
-    // (from 65536 otherwise) and for 5 <= M <= 16; beyond 16 rows the
-    // LDS-tiled GEMM.
-    const bool many_n = N >= 65536 || (N >= 8192 && fp8_skinny_xlds_supported(M, N, K));
+    // Measured on the decode shapes: the vector-ALU GEMV wins for M <= 2
+    // below 65536 output features and for M <= 4 on small weights; the
+    // matrix-core skinny kernels win above that (for 3 <= M <= 4 from 8192
+    // output features or a K of 8192 when the activation-in-LDS kernel
+    // applies) and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
+    const bool big = N >= 65536 ||
+                     (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K));
     if (M == 1) path = QLINEAR_PATH_GEMV;
-    else if (M <= 4) path = (wide && many_n) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
+    else if (M <= 4) path = (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
     else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
     else path = QLINEAR_PATH_TILED;
   }
