@@ -73,6 +73,8 @@ DYADIC = [
     ("skinny", 1, 4097, 4352), ("skinny", 8, 1001, 512), ("skinny", 9, 333, 5120),
     ("skinny", 2, 150, 10240), ("skinny", 13, 70001, 256), ("skinny", 4, 7, 19712),
     ("skinny", 12, 66003, 4096), ("skinny", 5, 1, 256),
+    # 16x16x32 activation-in-LDS kernel (5 <= M <= 16, K % 64 == 0): the largest K, uneven K split
+    ("skinny", 16, 300, 4864), ("skinny", 6, 2050, 4800),
 ]
 
 

@@ -322,9 +322,9 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
   constexpr int kU = 16;          // 16-byte loads per lane per stage (4 KiB per row)
   constexpr int kV = 4 * MG;      // accumulator values per lane
   constexpr int kChains = 4 / MG; // independent accumulators per m-group
-  constexpr int kLogV = MG == 1 ? 2 : 3;
+  constexpr int kLogV = MG == 1 ? 2 : (MG == 2 ? 3 : 4);
   constexpr int kGpb = NWB / KS;  // groups a block runs at once
-  static_assert(MG == 1 || MG == 2, "m-groups");
+  static_assert(MG == 1 || MG == 2 || MG == 4, "m-groups");
   static_assert(NWB % KS == 0, "whole groups per block");
 
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -359,16 +359,22 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
       for (int u = 0; u < kU; ++u) {
         if (c0 + u < c_hi) {
           const char* xp = xs + (int64_t(c0 + u) * MG * 2 * 64 + lane) * 16;
+          u32x4 xa[MG], xb[MG];
 #pragma unroll
           for (int p = 0; p < MG; ++p) {
-            const u32x4 xa = *reinterpret_cast<const u32x4*>(xp + p * 2048);
-            const u32x4 xb = *reinterpret_cast<const u32x4*>(xp + p * 2048 + 1024);
+            xa[p] = *reinterpret_cast<const u32x4*>(xp + p * 2048);
+            xb[p] = *reinterpret_cast<const u32x4*>(xp + p * 2048 + 1024);
+          }
+          // Weight k-quad q is decoded once and used by every m-group;
+          // consecutive instructions go to different accumulators.
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const u32x4& xh = q < 2 ? xa : xb;
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t d = wv[u][q];
+            const u32x2 bp{e4m3x2_to_bf16x2<false>(d), e4m3x2_to_bf16x2<true>(d)};
+#pragma unroll
+            for (int p = 0; p < MG; ++p) {
+              const u32x4& xh = q < 2 ? xa[p] : xb[p];
               const u32x2 ap = (q & 1) ? u32x2{xh.z, xh.w} : u32x2{xh.x, xh.y};
-              const uint32_t d = wv[u][q];
-              const u32x2 bp{e4m3x2_to_bf16x2<false>(d), e4m3x2_to_bf16x2<true>(d)};
               acc[p][q % kChains] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
                   __builtin_bit_cast(v4bf, ap), __builtin_bit_cast(v4bf, bp), acc[p][q % kChains], 0, 0, 0);
             }
@@ -391,12 +397,10 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
     // Reduce-scatter over the 16 blocks (lane bits 2..5, high bit first).
     rs_halve<kV / 2>(v, lane, 32);
     rs_halve<kV / 4>(v, lane, 16);
-    if constexpr (kV == 8) {
-      rs_halve<1>(v, lane, 8);
-    } else {
-      v[0] += __shfl_xor(v[0], 8, kWave);
-    }
-    v[0] += __shfl_xor(v[0], 4, kWave);
+    if constexpr (kV >= 8) rs_halve<kV / 8>(v, lane, 8);
+    else v[0] += __shfl_xor(v[0], 8, kWave);
+    if constexpr (kV >= 16) rs_halve<1>(v, lane, 4);
+    else v[0] += __shfl_xor(v[0], 4, kWave);
     return v[0];
   };
   // Lane 4 b + j holds out[b >> (4 - log2 V)][4 grp + j]; every
@@ -476,7 +480,7 @@ hipError_t launch_skinny16(const uint8_t* w, const uint16_t* x, void* out, int o
 }
 
 // Largest activation copy (bytes) the LDS holds: 4 MG padded rows x K bf16.
-int xlds_groups(int64_t M) { return M <= 4 ? 1 : 2; }
+int xlds_groups(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
 
 template <int MG, int NWB, int KS>
 hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
@@ -506,7 +510,7 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
   // with few groups the K chunks of each group split over four waves.  With
   // two m-groups the accumulators and activation operands need more than
   // the 128 registers a 16-wave block leaves each wave, so 12 (or 8) waves.
-  constexpr int kBig = MG == 1 ? 16 : 12;
+  constexpr int kBig = MG == 1 ? 16 : (MG == 2 ? 12 : 8);
   const int64_t groups = (int64_t(N) + 3) / 4;
   if (groups >= int64_t(num_cus) * kBig)
     return launch_xlds_nwb<MG, kBig, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
@@ -520,7 +524,7 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
 }  // namespace
 
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
-  return M >= 1 && M <= 8 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&
+  return M >= 1 && M <= 16 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&
          int64_t(xlds_groups(M)) * K * 8 + 16 * kWave * 4 <= kMaxLds;
 }
 
@@ -532,7 +536,8 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
   if (fp8_skinny_xlds_supported(M, N, K) && (M <= 4 || N >= 65536)) {
     switch (xlds_groups(M)) {
       case 1: return launch_xlds<1>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
-      default: return launch_xlds<2>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
+      case 2: return launch_xlds<2>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
+      default: return launch_xlds<4>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
     }
   }
   const bool wide_n = N >= 65536;
