@@ -43,6 +43,7 @@
 //   number of loads per strip and the wait counts stay constant.
 // * Output rows are staged through LDS so that full tiles leave with 16-byte
 //   stores.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -70,10 +71,11 @@ __device__ __forceinline__ void dma4(const char* g, char* lds) {
 // Raw buffer over `bytes` bytes at p (stride 0; the last dword is the
 // gfx9-family raw-buffer format word).  Buffer loads address it with a
 // 32-bit per-lane offset plus a uniform offset, so no 64-bit per-lane
-// address registers are needed.
+// address registers are needed; a lane whose offset lies past the record
+// count reads zeros without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
-  const int n = bytes >= (int64_t(1) << 31) - 1 ? 0x7FFFFFFF : int(bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+  const uint32_t n = bytes >= int64_t(0xFFFFFFFF) ? 0xFFFFFFFFu : uint32_t(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(n), 0x00020000);
 }
 
 // Buffer load of 16 (4) bytes per lane straight into LDS (lane i at lds + 16 i (4 i)).
@@ -180,6 +182,18 @@ struct StripDma {
       int64_t row = r0 + r;
       if (row >= rows) row = rows - 1;
       off[q] = uint32_t(row * ld + 16 * g);
+    }
+  }
+  // The same without clamping, for buffer fetches: rows past `rows` lie
+  // past the buffer's record count and are zero-filled.
+  __device__ __forceinline__ void init_open(int64_t r0, int64_t ld) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int c = (q * NW + wid) * kLanes + (lane < kLanes ? lane : 0);
+      const int r = c / kCpr;
+      const int g = (c % kCpr) ^ swz<kCpr>(r);
+      off[q] = uint32_t((r0 + r) * ld + 16 * g);
     }
   }
   // base = operand start + the strip's byte offset within a row (uniform)
@@ -463,29 +477,31 @@ struct WqLayout {
   static constexpr int kLoads = ADma::kInst + W::kLoads;
   static_assert(kLds <= kMaxLds, "LDS budget");
   static_assert((S - 1) * kLoads < 64, "vmcnt range");
-  static_assert(kSlabBase + 4 * Slab<0, FN, 32>::kBytes <= kLds, "output staging fits");
 };
 
 // OUT: 0 = float32, 1 = bfloat16 output.  vec: full tiles may use 16-byte
 // stores (out 16-byte aligned, N * element size a multiple of 16).
 // One BM x BN output tile at (m0, n0) of out[M, N] (leading dimension N).
-template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
 // Strips s0 .. s0 + ns - 1 of K (64 values each) are summed: all of K for
 // the plain GEMM, one slice for split-K partial sums.
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
 __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ x, typename WP<BN, 1, NW>::Args wa,
                                         void* __restrict__ out, int64_t M, int64_t N, int64_t K, float alpha,
                                         int vec, int64_t m0, int64_t n0, int64_t s0, int64_t ns) {
   using L = WqLayout<WP, BM, BN, S, WY, NW>;
   using W = typename L::W;
   constexpr int FM = L::FM, FN = L::FN;
+  constexpr int kLoads = L::kLoads;  // DMA instructions per wave per strip
   constexpr int NM = 2 * FM * FN;  // MFMAs per step
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wy = wid / L::WX, wx = wid % L::WX;
   const int r = lane & 31, h = lane >> 5;
   const int row0 = wy * (BM / WY), col0 = wx * (BN / L::WX);
 
+  // Activation rows past M are zero-filled by the buffer fetch (no traffic).
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 2);
   typename L::ADma adma;
-  adma.init(m0, M, 2 * K);
+  adma.init_open(m0, 2 * K);
   W wq;
   wq.init(wa, n0, N, K, col0, r, h);
   uint32_t aoff[2][2];
@@ -494,14 +510,13 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 2; ++e)
       aoff[t][e] = uint32_t((row0 + r) * 128 + 16 * (W::a_chunk(t, h, e) ^ swz<8>(r)));
-  const char* xb = reinterpret_cast<const char*>(x);
   const int64_t nk = ns;
 
   // Strip s goes to slot s % S; past the last strip it re-fetches the last one.
   auto fetch = [&](int64_t s) {
     char* st = lds + (s % S) * L::kStage;
     const int64_t src = s0 + (s < nk ? s : nk - 1);
-    adma.fetch(st, xb + src * 128);
+    adma.fetch(st, rx, uint32_t(src * 128));
     wq.fetch(st + L::kA, src);
   };
 
@@ -530,47 +545,63 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
                                                               0, 0, 0);
   };
 
+  // A wave whose rows all lie past M (a short group or the last row tile)
+  // still fetches its share of every strip and meets every barrier, but
+  // reads, decodes and multiplies nothing: LIVE = false.
+  auto main_loop = [&](auto live) {
+    constexpr bool LIVE = decltype(live)::value;
 #pragma unroll
-  for (int s = 0; s < S; ++s) fetch(s);
-  wait_vm<(S - 1) * L::kLoads>();
-  block_barrier();
-  read_a(aX, lds, 0);
-  wq.template read<0>(lds + L::kA);
-  wq.template decode<0>(bX);
-
-  for (int64_t kt = 0; kt < nk - 1; ++kt) {
-    const char* st = lds + (kt % S) * L::kStage;
-    // step 0: read step 1 of this strip, multiply step 0
-    read_a(aY, st, 1);
-    wq.template read<1>(st + L::kA);
-    mma(aX, bX);
-    wq.template decode<1>(bY);
-    interleave<NM, 0, 2 * FM + W::kReads[1], W::kValu>();
-    // step 1: cross into strip kt + 1 (landed for every wave after the
-    // barrier); slot kt % S is free once every wave's reads of it returned
-    wait_lds();
-    wait_vm<(S - 2) * L::kLoads>();
+    for (int s = 0; s < S; ++s) fetch(s);
+    wait_vm<(S - 1) * kLoads>();
     block_barrier();
-    fetch(kt + S);
-    const char* sn = lds + ((kt + 1) % S) * L::kStage;
-    read_a(aX, sn, 0);
-    wq.template read<0>(sn + L::kA);
-    mma(aY, bY);
-    wq.template decode<0>(bX);
-    interleave<NM, L::kLoads, 2 * FM + W::kReads[0], W::kValu>();
-  }
-  {
-    const char* st = lds + ((nk - 1) % S) * L::kStage;
-    read_a(aY, st, 1);
-    wq.template read<1>(st + L::kA);
-    mma(aX, bX);
-    wq.template decode<1>(bY);
-    mma(aY, bY);
-  }
-  wait_vm<0>();  // no LDS write may land after the block ends
+    if constexpr (LIVE) {
+      read_a(aX, lds, 0);
+      wq.template read<0>(lds + L::kA);
+      wq.template decode<0>(bX);
+    }
+
+    for (int64_t kt = 0; kt < nk - 1; ++kt) {
+      const char* st = lds + (kt % S) * L::kStage;
+      // step 0: read step 1 of this strip, multiply step 0
+      if constexpr (LIVE) {
+        read_a(aY, st, 1);
+        wq.template read<1>(st + L::kA);
+        mma(aX, bX);
+        wq.template decode<1>(bY);
+        interleave<NM, 0, 2 * FM + W::kReads[1], W::kValu>();
+      }
+      // step 1: cross into strip kt + 1 (landed for every wave after the
+      // barrier); slot kt % S is free once every wave's reads of it returned
+      wait_lds();
+      wait_vm<(S - 2) * kLoads>();
+      block_barrier();
+      fetch(kt + S);
+      if constexpr (LIVE) {
+        const char* sn = lds + ((kt + 1) % S) * L::kStage;
+        read_a(aX, sn, 0);
+        wq.template read<0>(sn + L::kA);
+        mma(aY, bY);
+        wq.template decode<0>(bX);
+        interleave<NM, kLoads, 2 * FM + W::kReads[0], W::kValu>();
+      }
+    }
+    if constexpr (LIVE) {
+      const char* st = lds + ((nk - 1) % S) * L::kStage;
+      read_a(aY, st, 1);
+      wq.template read<1>(st + L::kA);
+      mma(aX, bX);
+      wq.template decode<1>(bY);
+      mma(aY, bY);
+    }
+    wait_vm<0>();  // no LDS write may land after the block ends
+  };
+  if (m0 + row0 < M) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 
   // acc[i][j][v] = C[m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + col0 + 32 j + r]
-  if (vec && m0 + BM <= M && n0 + BN <= N) {
+  // Full tiles leave through the per-wave LDS slabs when they fit.
+  constexpr bool kSlabFits = kSlabBase + NW * Slab<OUT, FN, 32>::kBytes <= L::kLds;
+  if (kSlabFits && vec && m0 + BM <= M && n0 + BN <= N) {
     block_barrier();  // every wave is done reading the last strip
     const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
 #pragma unroll
@@ -1045,28 +1076,24 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
-// Grouped tile: 64 x 128 with four waves (32 x 64 each); small groups waste
-// little of it, and the weight column tile is shared by every row tile.
-constexpr int kGrpBM = 64, kGrpBN = 128, kGrpS = 4, kGrpWY = 2, kGrpNW = 4;
-using GrpLayout = WqLayout<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
+namespace {
 
-bool grouped_lds_supported(const void* x, const void* w, int64_t G, int64_t T, int64_t N, int64_t K) {
-  return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && T * K * 2 < (int64_t(1) << 32) &&
-         N * K < (int64_t(1) << 32) && GrpLayout::kLds + 4 * (G + 1) <= kMaxLds &&
-         (T + G) * ((N + kGrpBN - 1) / kGrpBN) < (int64_t(1) << 31);
-}
-
-hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
-                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
-                                  int64_t N, int64_t K, int num_cus, hipStream_t s) {
-  constexpr int BM = kGrpBM, BN = kGrpBN, S = kGrpS, WY = kGrpWY, NW = kGrpNW;
-  using L = GrpLayout;
-  // At most ceil(T / BM) + G row tiles exist; two blocks per CU walk them.
-  // The kernel splits the work over 8 XCDs: a multiple of 8 blocks.
-  const int64_t upper = ((T + BM - 1) / BM + G) * ((N + BN - 1) / BN);
-  const int64_t want = upper < 2 * int64_t(num_cus) ? upper : 2 * int64_t(num_cus);
-  const int64_t blocks = (want + 7) / 8 * 8;
+// Grouped tile: BM x BN with NW waves.  Short groups waste little of a
+// tall tile: their missing rows are zero-filled without traffic and waves
+// past a group's last row only fetch.
+template <int BM, int BN, int S, int WY, int NW>
+hipError_t launch_grouped_cfg(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
+                              const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
+                              int64_t N, int64_t K, int num_cus, hipStream_t s) {
+  using L = WqLayout<Fp8Weight, BM, BN, S, WY, NW>;
   const int lds_bytes = int(L::kLds + 4 * (G + 1));
+  if (lds_bytes > kMaxLds) return hipErrorInvalidValue;
+  // At most ceil(T / BM) + G row tiles exist; as many blocks as fit on the
+  // CUs walk them.  The kernel splits the work over 8 XCDs: a multiple of 8.
+  const int64_t upper = ((T + BM - 1) / BM + G) * ((N + BN - 1) / BN);
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kMaxLds / lds_bytes, 16 / NW));
+  const int64_t want = upper < per_cu * num_cus ? upper : per_cu * num_cus;
+  const int64_t blocks = (want + 7) / 8 * 8;
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   auto go = [&](auto kernel) -> hipError_t {
@@ -1083,6 +1110,24 @@ hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uin
   };
   if (out_bf16) return go(grouped_gemm_kernel<BM, BN, S, WY, NW, 1>);
   return go(grouped_gemm_kernel<BM, BN, S, WY, NW, 0>);
+}
+
+constexpr int kGrpBM = 64, kGrpBN = 128, kGrpS = 4, kGrpWY = 2, kGrpNW = 4;
+using GrpLayout = WqLayout<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
+
+}  // namespace
+
+bool grouped_lds_supported(const void* x, const void* w, int64_t G, int64_t T, int64_t N, int64_t K) {
+  return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && T * K * 2 < (int64_t(1) << 32) &&
+         N * K < (int64_t(1) << 32) && GrpLayout::kLds + 4 * (G + 1) <= kMaxLds &&
+         (T + G) * ((N + kGrpBN - 1) / kGrpBN) < (int64_t(1) << 31);
+}
+
+hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
+                                  const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
+                                  int64_t N, int64_t K, int num_cus, hipStream_t s) {
+  return launch_grouped_cfg<kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(w, x, a_offsets, expert_ids, out, out_bf16, G, E,
+                                                                   T, N, K, num_cus, s);
 }
 
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
