@@ -88,6 +88,21 @@ __device__ __forceinline__ void e2m1x2_scaled_f32(uint32_t w, float s, float& lo
   hi *= s;
 }
 
+// A 32-bit word as two packed bfloat16.  Taking the word by value matters:
+// bit-casting a vector element (v.y) in place reads the vector's first
+// element with this compiler.
+__device__ __forceinline__ v2bf as_bf16x2(uint32_t v) { return __builtin_bit_cast(v2bf, v); }
+
+// Eight E2M1 codes (the nibbles of w, the low nibble of each byte first) ->
+// four packed bfloat16 pairs, exact (conversion scale 1; every E2M1 value is
+// a bfloat16).
+__device__ __forceinline__ void e2m1x8_to_bf16x8(uint32_t w, v2bf (&p)[4]) {
+  p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+  p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+  p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+  p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+}
+
 // Two floats that are exactly representable in bfloat16 -> packed bfloat16
 // (the upper halves; no rounding is needed).
 __device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {

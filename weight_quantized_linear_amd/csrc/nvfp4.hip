@@ -9,8 +9,14 @@
 //
 // The GEMV mirrors the FP8 one: each 64-lane wave owns ROWS weight rows;
 // lane l takes the 16-byte packed chunks c = l, l + 64, ... (32 weights and
-// two block scales each), decodes pairs of nibbles to float32, multiplies by
-// the block scale (exact) and accumulates in float32.
+// two block scales each).  Pairs of nibbles are widened exactly to bfloat16
+// (conversion scale 1) and multiplied by the bfloat16 activation pairs with
+// v_dot2_f32_bf16 into a float32 partial sum per 16-value block, which is
+// then scaled by that block's E4M3 scale and added to the row's float32
+// accumulator: one conversion and M/2 dot products per weight pair instead
+// of a conversion, two scale products and M fused multiply-adds per pair.
+// The block scale distributes over the block's sum, so only the rounding
+// order differs from scaling every weight.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -62,30 +68,35 @@ __global__ __launch_bounds__(256) void nvfp4_gemv_wide_kernel(
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + int64_t(u) * kWave + lane;
       const bool ok = c < nchunks;
+      // Activation k = 32 c .. 32 c + 31 as bfloat16 pairs: xv[m][q] holds k = 32 c + 8 q .. + 7.
+      u32x4 xv[M][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // dword q of the chunk = weights 8q .. 8q+7
-        float xf[M][8];
+      for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const u32x4 xa = ok ? ld16(x + m * K + c * 32 + 8 * q) : u32x4{0u, 0u, 0u, 0u};
-          xf[m][0] = bf16lo(xa.x); xf[m][1] = bf16hi(xa.x);
-          xf[m][2] = bf16lo(xa.y); xf[m][3] = bf16hi(xa.y);
-          xf[m][4] = bf16lo(xa.z); xf[m][5] = bf16hi(xa.z);
-          xf[m][6] = bf16lo(xa.w); xf[m][7] = bf16hi(xa.w);
-        }
+        for (int q = 0; q < 4; ++q) xv[m][q] = ok ? ld16(x + m * K + c * 32 + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {  // dwords 2 blk, 2 blk + 1 = weights 16 blk .. 16 blk + 15
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-          const float s = e4m3_to_f32((sv[u][r] >> (8 * (q >> 1))) & 0xFFu);
-          const uint32_t d = wv[u][r][q];
-          float wf[8];
-          e2m1x2_scaled_f32<0>(d, s, wf[0], wf[1]);
-          e2m1x2_scaled_f32<1>(d, s, wf[2], wf[3]);
-          e2m1x2_scaled_f32<2>(d, s, wf[4], wf[5]);
-          e2m1x2_scaled_f32<3>(d, s, wf[6], wf[7]);
+          float part[M];
 #pragma unroll
-          for (int m = 0; m < M; ++m)
+          for (int m = 0; m < M; ++m) part[m] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[m][r] = fmaf(xf[m][e], wf[e], acc[m][r]);
+          for (int d = 0; d < 2; ++d) {
+            v2bf wp[4];  // wp[j] = weights 16 blk + 8 d + 2 j, + 1
+            e2m1x8_to_bf16x8(wv[u][r][2 * blk + d], wp);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              const u32x4& xa = xv[m][2 * blk + d];
+              part[m] = __builtin_amdgcn_fdot2_f32_bf16(wp[0], as_bf16x2(xa.x), part[m], false);
+              part[m] = __builtin_amdgcn_fdot2_f32_bf16(wp[1], as_bf16x2(xa.y), part[m], false);
+              part[m] = __builtin_amdgcn_fdot2_f32_bf16(wp[2], as_bf16x2(xa.z), part[m], false);
+              part[m] = __builtin_amdgcn_fdot2_f32_bf16(wp[3], as_bf16x2(xa.w), part[m], false);
+            }
+          }
+          const float sb = e4m3_to_f32((sv[u][r] >> (8 * blk)) & 0xFFu);
+#pragma unroll
+          for (int m = 0; m < M; ++m) acc[m][r] = fmaf(sb, part[m], acc[m][r]);
         }
       }
     }
