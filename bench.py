@@ -169,7 +169,7 @@ def build_decode(dev, q, synth, np, torch):
         codes, s = synth.fp8_weight((2, si, 0), n, k)
         weights[si] = torch.from_numpy(codes).to(dev)
         scales[si] = float(s)
-        heads[si] = codes[:8192].copy()
+        heads[si] = codes[:12288].copy()
         del codes
     cases = []
     for m in ms:
@@ -195,7 +195,7 @@ def build_decode(dev, q, synth, np, torch):
                 rows = heads[si].shape[0]
                 total += rows * k + m * k * 2 + m * rows * 2
         return {"value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"first 8192 weight rows (all 4096 where N = 4096) of each of the 12 (M, N, K) cases, "
+                "sample": f"first 12288 weight rows (all 4096 where N = 4096) of each of the 12 (M, N, K) cases, "
                           f"full K ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
 
     return dict(
