@@ -27,6 +27,7 @@ __all__ = [
     "fp8_gemm",
     "fp8_materialize",
     "fp8_grouped_gemm",
+    "nvfp4_grouped_gemm",
     "nvfp4_gemm",
     "nvfp4_dequant",
     "int8_quantize_act",
@@ -52,6 +53,7 @@ EXPORTED = {
     "qlinear_fp8_materialize": [_p, _p, _i, _i64, _i64, _p],
     "qlinear_fp8_grouped_gemm": [_p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_nvfp4_gemm": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _p],
+    "qlinear_nvfp4_grouped_gemm": [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_nvfp4_gemm_path": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _i, _p],
     "qlinear_nvfp4_dequant": [_p, _p, _p, _i, _i64, _i64, _p],
     "qlinear_int8_quantize_act": [_p, _p, _p, _i64, _i64, _p],
@@ -61,7 +63,7 @@ EXPORTED = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m weight_quantized_linear_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python weight_quantized_linear_amd/build.py`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, argtypes in EXPORTED.items():
         fn = getattr(handle, name)
@@ -199,6 +201,38 @@ def fp8_grouped_gemm(w: torch.Tensor, x: torch.Tensor, a_offsets: torch.Tensor, 
     st = lib.qlinear_fp8_grouped_gemm(_ptr(w), _ptr(x), _ptr(a_offsets), _ptr(expert_ids), _ptr(out),
                                       _OUT_CODES[out_dtype], g, int(max_tokens_per_group), e, t, n, k, _stream(x))
     _check(st, "qlinear_fp8_grouped_gemm")
+    return out
+
+
+def nvfp4_grouped_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, a_offsets: torch.Tensor,
+                       expert_ids: torch.Tensor, out: torch.Tensor | None = None,
+                       out_dtype: torch.dtype = torch.bfloat16, max_tokens_per_group: int | None = None) -> torch.Tensor:
+    """Grouped MoE W4A16 NVFP4 (``qlinear_nvfp4_grouped_gemm``): rows a_offsets[z] ..
+    a_offsets[z+1]-1 of x times D_e^T, e = expert_ids[z], D_e the expert's NVFP4
+    weight (w_packed [E, N, K/2], w_scale [E, N, K/16]); raw output.  Rows outside
+    every group keep whatever ``out`` held (a new ``out`` starts uninitialised)."""
+    p = _as_u8(w_packed, "w_packed")
+    sc = _as_u8(w_scale, "w_scale")
+    x = _as_bf16(x, "x")
+    for t, name in ((p, "w_packed"), (sc, "w_scale"), (x, "x"), (a_offsets, "a_offsets"), (expert_ids, "expert_ids")):
+        _require(t, name)
+    if a_offsets.dtype not in (torch.int32, torch.uint32) or expert_ids.dtype != torch.int32:
+        raise TypeError("a_offsets must be uint32/int32 and expert_ids int32")
+    if p.dim() != 3 or x.dim() != 2:
+        raise ValueError("w_packed must be [E, N, K/2] and x [T, K]")
+    e, n, _ = p.shape
+    t, k = x.shape
+    if tuple(p.shape) != (e, n, k // 2) or tuple(sc.shape) != (e, n, k // 16):
+        raise ValueError("w_packed must be [E, N, K/2] and w_scale [E, N, K/16]")
+    g = expert_ids.numel()
+    if a_offsets.numel() != g + 1:
+        raise ValueError("a_offsets needs num_groups + 1 entries")
+    if max_tokens_per_group is None:
+        max_tokens_per_group = t
+    out = _out(out, (t, n), out_dtype, x.device)
+    st = lib.qlinear_nvfp4_grouped_gemm(_ptr(p), _ptr(sc), _ptr(x), _ptr(a_offsets), _ptr(expert_ids), _ptr(out),
+                                        _OUT_CODES[out_dtype], g, int(max_tokens_per_group), e, t, n, k, _stream(x))
+    _check(st, "qlinear_nvfp4_grouped_gemm")
     return out
 
 

@@ -1,8 +1,9 @@
 """Build libqlinear.so in-tree: hipcc for gfx950, one object per source,
 linked into ``weight_quantized_linear_amd/libqlinear.so``.
 
-Run ``python -m weight_quantized_linear_amd.build`` (or ``__graft_entry__.build()``).
-Every call recompiles every source.
+Run ``python weight_quantized_linear_amd/build.py`` (or ``__graft_entry__.build()``);
+this file imports nothing from the package, whose import needs the built
+library.  Every call recompiles every source.
 """
 
 from __future__ import annotations
