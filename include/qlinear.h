@@ -158,6 +158,28 @@ int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x,
                        int out_dtype, int64_t M, int64_t N, int64_t K, float alpha,
                        void* stream);
 
+/*
+ * Grouped (MoE) W4A16 NVFP4 matmul: the ragged addressing of page
+ * "Matmul2dFp8" (run_grouped) with the weight format of page "fp4_matmul".
+ * For every group z, rows r in [a_offsets[z], a_offsets[z+1]):
+ *     out[r, n] = sum_k x[r, k] * D_e[n, k],   e = expert_ids[z],
+ *     D_e[n, k] = e2m1(code_e(n, k)) * dec_e4m3(w_scale[e, n, k / 16])
+ * w_packed: uint8 [num_experts, N, K/2] (nibble order as qlinear_nvfp4_gemm);
+ * w_scale: float8_e4m3fn [num_experts, N, K/16]; x: bfloat16 [T, K];
+ * out: [T, N] of out_dtype (F32 or BF16); K % 16 == 0.  The result is raw:
+ * each expert's global scale (weight_scale_2) is applied by the caller.
+ * a_offsets, expert_ids, num_groups, max_tokens_per_group, inactive / empty
+ * groups, untouched rows, precondition and bounds behaviour: exactly as
+ * qlinear_fp8_grouped_gemm.  Returns QLINEAR_ERR_INVALID_ARG for a null
+ * pointer, a non-positive size, K % 16 != 0 or a misaligned x / out /
+ * a_offsets / expert_ids; nothing is written then.
+ */
+int qlinear_nvfp4_grouped_gemm(const void* w_packed, const void* w_scale, const void* x,
+                               const uint32_t* a_offsets, const int32_t* expert_ids, void* out,
+                               int out_dtype, int64_t num_groups, int64_t max_tokens_per_group,
+                               int64_t num_experts, int64_t T, int64_t N, int64_t K,
+                               void* stream);
+
 /* As qlinear_nvfp4_gemm with the kernel family forced: QLINEAR_PATH_GEMV
  * (M <= 4) or QLINEAR_PATH_TILED (any M); others are QLINEAR_ERR_INVALID_ARG. */
 int qlinear_nvfp4_gemm_path(const void* w_packed, const void* w_scale, const void* x,

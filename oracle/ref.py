@@ -81,6 +81,38 @@ def fp8_linear(w_codes, x_bits, alpha: float = 1.0):
     return _linear(lambda lo, hi: e4m3_to_f64(w[lo:hi]), w.shape[0], x, alpha)
 
 
+def _grouped(linear_of_expert, e_count: int, n: int, x_bits, a_offsets, expert_ids):
+    """The ragged group loop shared by the grouped readings below: group z
+    covers rows a_offsets[z] .. a_offsets[z+1]-1 (clipped to T; empty when the
+    end does not exceed the start) and uses expert expert_ids[z]; an id outside
+    0..E-1 writes zeros; rows no group covers stay NaN with written[r] = False.
+    linear_of_expert(e, x_rows) returns (ref, bound) for one expert."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    offs = np.asarray(a_offsets).astype(np.int64)
+    ids = np.asarray(expert_ids).astype(np.int64)
+    t = x.shape[0]
+    if offs.shape[0] != ids.shape[0] + 1:
+        raise ValueError("a_offsets must have one entry more than expert_ids")
+    ref = np.full((t, n), np.nan)
+    bound = np.full((t, n), np.nan)
+    written = np.zeros(t, dtype=bool)
+    for z in range(ids.shape[0]):
+        start = min(int(offs[z]), t)
+        end = min(int(offs[z + 1]), t)
+        if end <= start:
+            continue
+        e = int(ids[z])
+        if 0 <= e < e_count:
+            r, b = linear_of_expert(e, x[start:end])
+        else:
+            r = np.zeros((end - start, n))
+            b = np.zeros((end - start, n))
+        ref[start:end] = r
+        bound[start:end] = b
+        written[start:end] = True
+    return ref, bound, written
+
+
 def fp8_grouped(w_codes, x_bits, a_offsets, expert_ids):
     """Grouped (MoE) W8A16 linear.
 
@@ -99,31 +131,24 @@ def fp8_grouped(w_codes, x_bits, a_offsets, expert_ids):
     expert_ids: [G].  Returns (ref [T, N], bound [T, N], written [T]).
     """
     w = np.asarray(w_codes, dtype=np.uint8)
-    x = np.asarray(x_bits, dtype=np.uint16)
-    offs = np.asarray(a_offsets).astype(np.int64)
-    ids = np.asarray(expert_ids).astype(np.int64)
     e_count, n, _ = w.shape
-    t = x.shape[0]
-    if offs.shape[0] != ids.shape[0] + 1:
-        raise ValueError("a_offsets must have one entry more than expert_ids")
-    ref = np.full((t, n), np.nan)
-    bound = np.full((t, n), np.nan)
-    written = np.zeros(t, dtype=bool)
-    for z in range(ids.shape[0]):
-        start = min(int(offs[z]), t)
-        end = min(int(offs[z + 1]), t)
-        if end <= start:
-            continue
-        e = int(ids[z])
-        if 0 <= e < e_count:
-            r, b = fp8_linear(w[e], x[start:end])
-        else:
-            r = np.zeros((end - start, n))
-            b = np.zeros((end - start, n))
-        ref[start:end] = r
-        bound[start:end] = b
-        written[start:end] = True
-    return ref, bound, written
+    return _grouped(lambda e, xr: fp8_linear(w[e], xr), e_count, n, x_bits, a_offsets, expert_ids)
+
+
+def nvfp4_grouped(w_packed, w_scale_codes, x_bits, a_offsets, expert_ids):
+    """Grouped (MoE) W4A16 NVFP4 linear: the ``run_grouped`` addressing of the
+    Matmul2dFp8 page applied to the fp4_matmul page's weight format.
+
+    Same group readings as fp8_grouped; expert e's weight is the NVFP4 pair
+    (w_packed[e] uint8 [N, K/2], w_scale_codes[e] E4M3 [N, K/16]).  The result
+    is raw: each expert's per-tensor global scale (weight_scale_2) is left to
+    the caller, as the per-expert FP8 weight_scale is for fp8_grouped.
+    Returns (ref [T, N], bound [T, N], written [T]).
+    """
+    p = np.asarray(w_packed, dtype=np.uint8)
+    sc = np.asarray(w_scale_codes, dtype=np.uint8)
+    e_count, n, _ = p.shape
+    return _grouped(lambda e, xr: nvfp4_linear(p[e], sc[e], xr), e_count, n, x_bits, a_offsets, expert_ids)
 
 
 def nvfp4_dequant(w_packed, w_scale_codes) -> np.ndarray:

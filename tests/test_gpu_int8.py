@@ -57,7 +57,9 @@ def test_quantizer_unaligned_view(q):
     assert np.array_equal(qd.cpu().numpy(), want_q) and np.array_equal(sd.cpu().numpy(), want_s)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (130, 70, 100), (257, 129, 4099), (128, 256, 3072), (333, 1000, 64)])
+# (4000, 3000, 1024): 256 x 256 tiles, ragged in both directions
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (130, 70, 100), (257, 129, 4099), (128, 256, 3072), (333, 1000, 64),
+                                   (4000, 3000, 1024)])
 def test_int32_accumulators_bit_exact(q, m, n, k):
     r = np.random.default_rng(m * 7 + n)
     a = r.integers(-127, 128, size=(m, k)).astype(np.int8)
@@ -95,6 +97,24 @@ def test_w8a8_workload(q, n):
     assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), want_acc)
     ref, tau = R.int8_epilogue(want_acc, sx[rows], c.b_scale, c.bias)
     res = C.check_bf16(bf16_bits(out)[rows], ref, tau)
+    assert res and res.n_clause2 <= C.clause2_budget(ref), res
+
+
+def test_epilogue_bf16_at_tile_edges(q):
+    """bf16 epilogue at M = 4000, N = 3000: full 256 x 256 tiles leave through
+    the LDS slab, edge tiles element by element."""
+    r = np.random.default_rng(63)
+    m, n, k = 4000, 3000, 512
+    a = r.integers(-127, 128, size=(m, k)).astype(np.int8)
+    b = r.integers(-127, 128, size=(n, k)).astype(np.int8)
+    sa = (r.random(m).astype(np.float32) * 0.01).astype(np.float32)
+    sb = (r.random(n).astype(np.float32) * 0.01).astype(np.float32)
+    bias = synth.bf16_activation((64,), 1, n)[0]
+    show("int8 epilogue bf16 edges")
+    out = q.int8_gemm(to_dev_i8(a), to_dev_i8(b), torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
+                      to_dev_bf16(bias), out_dtype=torch.bfloat16)
+    ref, tau = R.int8_epilogue(R.int8_accumulate(a, b), sa, sb, bias)
+    res = C.check_bf16(bf16_bits(out), ref, tau)
     assert res and res.n_clause2 <= C.clause2_budget(ref), res
 
 

@@ -190,6 +190,35 @@ def test_nvfp4_linear_fraction_brute_force(m, n, k):
             assert abs(Fraction(float(got[i, j])) - Fraction(3, 4) * acc) <= Fraction(2.0 ** -40) * Fraction(float(bound[i, j]) + 1)
 
 
+def test_nvfp4_grouped_brute_force_and_semantics():
+    """Grouped NVFP4: each active group equals exact rational sums of
+    x * e2m1(code) * e4m3(block scale) with its expert's weight; -1 groups are
+    zeros, empty groups and uncovered rows are untouched."""
+    r = np.random.default_rng(21)
+    e_count, n, k, t = 3, 4, 32, 11
+    codes = r.integers(0, 16, size=(e_count, n, k)).astype(np.uint8)
+    packed = np.stack([synth.pack_nibbles(codes[e]) for e in range(e_count)])
+    scales = r.integers(0, 0x7E, size=(e_count, n, k // 16), dtype=np.uint8)
+    x = synth.bf16_bits_from_f32(r.standard_normal((t, k)).astype(np.float32))
+    offs = np.array([0, 2, 2, 5, 7, 10], np.uint32)   # group 1 empty, row 10 uncovered
+    ids = np.array([1, 0, -1, 2, 0], np.int32)
+    ref, bound, written = R.nvfp4_grouped(packed, scales, x, offs, ids)
+    assert written.tolist() == [True] * 10 + [False]
+    assert np.all(np.isnan(ref[10]))
+    assert np.array_equal(ref[2:5], np.zeros((3, n)))
+    e2 = F.e2m1_to_f64(np.arange(16))
+    e4 = F.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    xd = F.bf16_bits_to_f64(x)
+    for (lo, hi), ex in (((0, 2), 1), ((5, 7), 2), ((7, 10), 0)):
+        for i in range(lo, hi):
+            for j in range(n):
+                acc = Fraction(0)
+                for kk in range(k):
+                    acc += (Fraction(float(xd[i, kk])) * Fraction(float(e2[codes[ex, j, kk]]))
+                            * Fraction(float(e4[scales[ex, j, kk // 16]])))
+                assert abs(Fraction(float(ref[i, j])) - acc) <= Fraction(2.0 ** -40) * Fraction(float(bound[i, j]) + 1)
+
+
 def test_nvfp4_rejects_bad_block_layout():
     with pytest.raises(ValueError):
         R.nvfp4_dequant(np.zeros((2, 8), np.uint8), np.zeros((2, 2), np.uint8))

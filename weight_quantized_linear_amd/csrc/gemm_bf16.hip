@@ -168,6 +168,14 @@ template <class T> struct StageOf;
 template <> struct StageOf<Fp8Tile> { using type = Fp8Stage; };
 template <> struct StageOf<Nvfp4Tile> { using type = Nvfp4Stage; };
 
+// Expert e of a weight stack whose tile `b` addresses expert 0.
+__device__ __forceinline__ Fp8Tile expert_tile(const Fp8Tile& b, int64_t e) {
+  return Fp8Tile{b.w + e * b.N * b.K, b.N, b.K, b.vec};
+}
+__device__ __forceinline__ Nvfp4Tile expert_tile(const Nvfp4Tile& b, int64_t e) {
+  return Nvfp4Tile{b.packed + e * b.N * (b.K >> 1), b.scales + e * b.N * (b.K >> 4), b.N, b.K, b.vec};
+}
+
 // Computes the 128 x 128 tile at (m0, n0) of out[M, N] (row stride N) and
 // stores alpha * acc.  Every thread of the block must call it.
 template <class WTile>
@@ -268,8 +276,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dense_kernel(ActTile A, WTile B
 // the column tile and row tiles of the group are taken blockIdx.y, +gridDim.y, ...
 // An id outside 0..E-1 (-1 marks an inactive group) writes zeros; offsets are
 // clipped to T and a group whose end does not exceed its start does nothing.
-__global__ __launch_bounds__(kThreads) void gemm_grouped_fp8_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ a_offsets,
+// `B` addresses expert 0 of the weight stack (FP8 or NVFP4).
+template <class WTile>
+__global__ __launch_bounds__(kThreads) void gemm_grouped_kernel(
+    const uint16_t* __restrict__ x, WTile B, const uint32_t* __restrict__ a_offsets,
     const int32_t* __restrict__ expert_ids, void* __restrict__ out, int out_bf16, int64_t T,
     int64_t N, int64_t K, int64_t E, bool vec) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
@@ -291,8 +301,8 @@ __global__ __launch_bounds__(kThreads) void gemm_grouped_fp8_kernel(
       continue;
     }
     const ActTile A{x + start * K, rows, K, vec};
-    const Fp8Tile B{w + e * N * K, N, K, vec};
-    gemm_tile(lds, A, B, static_cast<char*>(out) + start * N * (out_bf16 ? 2 : 4), out_bf16, m0, n0, 1.f);
+    gemm_tile(lds, A, expert_tile(B, e), static_cast<char*>(out) + start * N * (out_bf16 ? 2 : 4), out_bf16, m0, n0,
+              1.f);
   }
 }
 
@@ -337,8 +347,26 @@ hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_m > 65535) tiles_m = 65535;
   (void)num_cus;
-  return launch(gemm_grouped_fp8_kernel, dim3((N + BN - 1) / BN, tiles_m, G), dim3(kThreads), 0, s, x, w,
-                a_offsets, expert_ids, out, out_bf16, T, N, K, E, vec);
+  return launch(gemm_grouped_kernel<Fp8Tile>, dim3((N + BN - 1) / BN, tiles_m, G), dim3(kThreads), 0, s, x,
+                Fp8Tile{w, N, K, vec}, a_offsets, expert_ids, out, out_bf16, T, N, K, E, vec);
+}
+
+hipError_t launch_nvfp4_grouped(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
+                                const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
+                                int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
+                                int num_cus, hipStream_t s) {
+  if (nvfp4_grouped_lds_supported(x, packed, scales, G, T, N, K))
+    return launch_nvfp4_grouped_lds(packed, scales, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus,
+                                    s);
+  // The element-wise fallback: vec needs every expert's packed rows 16-byte
+  // aligned (K % 32 == 0 and an aligned base).
+  const bool vec = (K % 32 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  int64_t tiles_m = (max_tokens + BM - 1) / BM;
+  if (tiles_m < 1) tiles_m = 1;
+  if (tiles_m > 65535) tiles_m = 65535;
+  return launch(gemm_grouped_kernel<Nvfp4Tile>, dim3((N + BN - 1) / BN, tiles_m, G), dim3(kThreads), 0, s, x,
+                Nvfp4Tile{packed, scales, N, K, vec}, a_offsets, expert_ids, out, out_bf16, T, N, K, E, vec);
 }
 
 }  // namespace qlinear

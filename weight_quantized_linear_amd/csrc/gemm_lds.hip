@@ -249,6 +249,8 @@ struct Nvfp4Args { const uint8_t* packed; const uint8_t* scales; };
 template <int BN, int FN, int NW>
 struct Fp8Weight {
   using Args = Fp8Args;
+  // Expert e of a stack [E, N, K].
+  __device__ static Args expert(Args a, int64_t e, int64_t N, int64_t K) { return Args{a.w + e * N * K}; }
   static constexpr int kBytes = BN * 64;
   using Dma = StripDma<BN, 64, NW>;
   static constexpr int kLoads = Dma::kInst;
@@ -290,6 +292,10 @@ struct Fp8Weight {
 template <int BN, int FN, int NW>
 struct Nvfp4Weight {
   using Args = Nvfp4Args;
+  // Expert e of stacks [E, N, K/2] (packed) and [E, N, K/16] (scales).
+  __device__ static Args expert(Args a, int64_t e, int64_t N, int64_t K) {
+    return Args{a.packed + e * N * (K / 2), a.scales + e * N * (K / 16)};
+  }
   static constexpr int kPacked = BN * 32;
   static constexpr int kBytes = BN * 36;
   using Dma = StripDma<BN, 32, NW>;
@@ -688,14 +694,16 @@ __global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict_
 // the XCD's blocks walk their range with a stride.  All row tiles of one
 // expert then meet its weight tiles in the same L2, which each weight tile
 // is fetched into once.
-template <int BM, int BN, int S, int WY, int NW, int OUT>
+// WP: the weight format (Fp8Weight, or Nvfp4Weight for W4A16 experts); `wa`
+// addresses expert 0 of the stack.
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
 __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
-                                                                const uint8_t* __restrict__ w,
+                                                                typename WP<BN, 1, NW>::Args wa,
                                                                 const uint32_t* __restrict__ a_offsets,
                                                                 const int32_t* __restrict__ expert_ids,
                                                                 void* __restrict__ out, int64_t G, int64_t T,
                                                                 int64_t N, int64_t K, int64_t E, int vec) {
-  using L = WqLayout<Fp8Weight, BM, BN, S, WY, NW>;
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int kEs = OutT<OUT>::kBytes;
   int* cum = reinterpret_cast<int*>(lds + L::kLds);  // cum[z] = row tiles of groups 0 .. z-1; cum[G] = total
@@ -762,8 +770,8 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* _
     // with the previous tile.
     if (!first) __syncthreads();
     first = false;
-    wq_tile<Fp8Weight, BM, BN, S, WY, NW, OUT>(lds, x + start * K, Fp8Args{w + e * N * K}, gout, rows, N, K, 1.f,
-                                                vec, m0, n0, 0, K / 64);
+    wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x + start * K, WP<BN, 1, NW>::expert(wa, e, N, K), gout, rows, N, K,
+                                         1.f, vec, m0, n0, 0, K / 64);
   }
 }
 
@@ -1081,11 +1089,11 @@ namespace {
 // Grouped tile: BM x BN with NW waves.  Short groups waste little of a
 // tall tile: their missing rows are zero-filled without traffic and waves
 // past a group's last row only fetch.
-template <int BM, int BN, int S, int WY, int NW>
-hipError_t launch_grouped_cfg(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
+hipError_t launch_grouped_cfg(typename WP<BN, 1, NW>::Args wa, const uint16_t* x, const uint32_t* a_offsets,
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
                               int64_t N, int64_t K, int num_cus, hipStream_t s) {
-  using L = WqLayout<Fp8Weight, BM, BN, S, WY, NW>;
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
   const int lds_bytes = int(L::kLds + 4 * (G + 1));
   if (lds_bytes > kMaxLds) return hipErrorInvalidValue;
   // At most ceil(T / BM) + G row tiles exist; as many blocks as fit on the
@@ -1105,15 +1113,16 @@ hipError_t launch_grouped_cfg(const uint8_t* w, const uint16_t* x, const uint32_
       if (e != hipSuccess) return e;
       attr = true;
     }
-    return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, x, w, a_offsets, expert_ids, out, G, T, N, K, E,
-                  vec);
+    return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, x, wa, a_offsets, expert_ids, out, G, T, N, K,
+                  E, vec);
   };
-  if (out_bf16) return go(grouped_gemm_kernel<BM, BN, S, WY, NW, 1>);
-  return go(grouped_gemm_kernel<BM, BN, S, WY, NW, 0>);
+  if (out_bf16) return go(grouped_gemm_kernel<WP, BM, BN, S, WY, NW, 1>);
+  return go(grouped_gemm_kernel<WP, BM, BN, S, WY, NW, 0>);
 }
 
 constexpr int kGrpBM = 64, kGrpBN = 128, kGrpS = 4, kGrpWY = 2, kGrpNW = 4;
 using GrpLayout = WqLayout<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
+using GrpLayoutFp4 = WqLayout<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
 
 }  // namespace
 
@@ -1123,11 +1132,27 @@ bool grouped_lds_supported(const void* x, const void* w, int64_t G, int64_t T, i
          (T + G) * ((N + kGrpBN - 1) / kGrpBN) < (int64_t(1) << 31);
 }
 
+bool nvfp4_grouped_lds_supported(const void* x, const void* packed, const void* scales, int64_t G, int64_t T,
+                                 int64_t N, int64_t K) {
+  return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(packed) &&
+         reinterpret_cast<uintptr_t>(scales) % 4 == 0 && T * K * 2 < (int64_t(1) << 32) &&
+         N * (K / 2) < (int64_t(1) << 32) && GrpLayoutFp4::kLds + 4 * (G + 1) <= kMaxLds &&
+         (T + G) * ((N + kGrpBN - 1) / kGrpBN) < (int64_t(1) << 31);
+}
+
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                                   const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
                                   int64_t N, int64_t K, int num_cus, hipStream_t s) {
-  return launch_grouped_cfg<kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(w, x, a_offsets, expert_ids, out, out_bf16, G, E,
-                                                                   T, N, K, num_cus, s);
+  return launch_grouped_cfg<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(
+      Fp8Args{w}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
+}
+
+hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
+                                    const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
+                                    int64_t G, int64_t E, int64_t T, int64_t N, int64_t K, int num_cus,
+                                    hipStream_t s) {
+  return launch_grouped_cfg<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(
+      Nvfp4Args{packed, scales}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
 }
 
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,

@@ -60,6 +60,17 @@ hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G,
                               int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
                               int num_cus, hipStream_t s);
+bool nvfp4_grouped_lds_supported(const void* x, const void* packed, const void* scales, int64_t G, int64_t T,
+                                 int64_t N, int64_t K);
+hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
+                                    const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
+                                    int64_t G, int64_t E, int64_t T, int64_t N, int64_t K, int num_cus,
+                                    hipStream_t s);
+// Grouped NVFP4 (expert stacks [E, N, K/2] and [E, N, K/16], K % 16 == 0).
+hipError_t launch_nvfp4_grouped(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
+                                const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
+                                int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
+                                int num_cus, hipStream_t s);
 
 // nvfp4.hip
 hipError_t launch_nvfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,

@@ -238,6 +238,26 @@ int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_off
                                    static_cast<hipStream_t>(stream)));
 }
 
+int qlinear_nvfp4_grouped_gemm(const void* w_packed, const void* w_scale, const void* x, const uint32_t* a_offsets,
+                               const int32_t* expert_ids, void* out, int out_dtype, int64_t num_groups,
+                               int64_t max_tokens_per_group, int64_t num_experts, int64_t T, int64_t N, int64_t K,
+                               void* stream) {
+  if (!w_packed || !w_scale || !x || !a_offsets || !expert_ids || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (num_groups <= 0 || num_groups > 65535 || max_tokens_per_group < 0 || num_experts <= 0 || T <= 0 ||
+      N <= 0 || K <= 0 || K % 16 != 0)
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!fits(num_experts, N, K) || !fits(T, K) || !fits(T, N)) return QLINEAR_ERR_INVALID_ARG;
+  if (!float_out_ok(out_dtype) || !aligned(x, 2) || !aligned(out, out_size(out_dtype)) ||
+      !aligned(a_offsets, 4) || !aligned(expert_ids, 4))
+    return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_nvfp4_grouped(static_cast<const uint8_t*>(w_packed), static_cast<const uint8_t*>(w_scale),
+                                     static_cast<const uint16_t*>(x), a_offsets, expert_ids, out,
+                                     out_dtype == QLINEAR_BF16, num_groups, max_tokens_per_group, num_experts, T,
+                                     N, K, num_cus, static_cast<hipStream_t>(stream)));
+}
+
 int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
                        int64_t M, int64_t N, int64_t K, float alpha, void* stream) {
   return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
