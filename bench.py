@@ -11,7 +11,8 @@ weight and no read is served from the 256 MB last-level cache.
 
 Other workloads (--workload): "gemv2048" (M = 1, N = 2048, K = 2048 / 2050,
 fp32 out), "nvfp4" (W4A16 at M in {1, 128, 2048}, N = K = 4096), "grouped"
-(MoE W8A16, 64 experts [64, 1536, 2048], 4096 Zipf-routed tokens), "int8"
+(MoE W8A16, 64 experts [64, 1536, 2048], 4096 Zipf-routed tokens),
+"grouped_nvfp4" (the same routing and shapes with NVFP4 experts), "int8"
 (W8A8: activation quantiser + int8 GEMM at N in {3072, 12288}, M = 4096,
 K = 3072).  Where a workload's weights would fit the last-level cache, the
 timed graph cycles through enough copies of them (>= 1 GiB) that every read
@@ -20,8 +21,8 @@ comes from HBM.
 The step is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
 graph is replayed: host-side launch overhead of the Python binding would
 otherwise exceed the 5-20 us kernels.  Prints ONE JSON line: value =
-algorithmic traffic (decode, gemv2048, grouped: weights + activations +
-outputs once, GB/s) or work (nvfp4: TFLOP/s, int8: TOPS) per step / step
+algorithmic traffic (decode, gemv2048, grouped, grouped_nvfp4: weights +
+activations + outputs once, GB/s) or work (nvfp4: TFLOP/s, int8: TOPS) per step / step
 time; ``roofline`` for the workload's dominant kernel, whose average launch
 duration is measured with HIP events around a graph of back-to-back launches
 of that kernel on its stream; ``cpu_baseline`` = the CPU oracle on a bounded
@@ -316,6 +317,49 @@ def build_grouped(dev, q, synth, np, torch):
                 baseline=baseline)
 
 
+def build_grouped_nvfp4(dev, q, synth, np, torch):
+    c = synth.grouped_nvfp4_case()
+    e, n, kh = c.packed.shape
+    k = 2 * kh
+    t = c.x.shape[0]
+    # two copies of the 113 MB stack alternate so no read is served from the last-level cache
+    copies = 2
+    pp = [torch.from_numpy(c.packed).to(dev) for _ in range(copies)]
+    ps = [torch.from_numpy(c.scales).to(dev) for _ in range(copies)]
+    x = bf16_dev(c.x, dev, np, torch)
+    offs = torch.from_numpy(c.a_offsets.astype(np.int32)).to(dev)
+    ids = torch.from_numpy(c.expert_ids.astype(np.int32)).to(dev)
+    out = torch.empty((t, n), dtype=torch.bfloat16, device=dev)
+    active = [z for z in range(e) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
+    rows_active = int(sum(int(c.a_offsets[z + 1]) - int(c.a_offsets[z]) for z in active))
+    nbytes = len(active) * n * (k // 2 + k // 16) + t * k * 2 + t * n * 2
+    flops = 2 * rows_active * n * k
+
+    def run(copy):
+        q.nvfp4_grouped_gemm(pp[copy % copies], ps[copy % copies], x, offs, ids, out=out,
+                             max_tokens_per_group=c.max_tokens)
+    cases = [Case(c.name, run, nbytes, flops, copies)]
+
+    def baseline():
+        from oracle import ref
+        gz = 8  # the first 8 groups, whole
+        t0 = time.perf_counter()
+        ref.nvfp4_grouped(c.packed, c.scales, c.x[: int(c.a_offsets[gz])], c.a_offsets[: gz + 1], c.expert_ids[:gz])
+        el = time.perf_counter() - t0
+        act = [z for z in range(gz) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
+        b = len(act) * n * (k // 2 + k // 16) + int(c.a_offsets[gz]) * (k + n) * 2
+        return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"groups 0-7 ({int(c.a_offsets[gz])} tokens, {len(act)} active experts, {el:.1f} s)"}
+
+    return dict(metric="Grouped MoE W4A16 NVFP4 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
+                dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS,
+                kernel="grouped_gemm_kernel<Nvfp4Weight, 64, 128> (64 experts, N=1536, K=2048, 4096 tokens)",
+                dtype="bf16",
+                config={"workload": f"grouped_moe_w4a16_nvfp4: E=64 [64,1536,2048] NVFP4, T=4096 bf16 tokens, "
+                                    f"Zipf(1.2) groups, {len(active)} active experts, {rows_active} active tokens"},
+                baseline=baseline)
+
+
 def build_int8(dev, q, synth, np, torch):
     m, k = 4096, 3072
     cases = []
@@ -363,7 +407,7 @@ def build_int8(dev, q, synth, np, torch):
 
 
 WORKLOADS = {"decode": build_decode, "gemv2048": build_gemv2048, "nvfp4": build_nvfp4,
-             "grouped": build_grouped, "int8": build_int8}
+             "grouped": build_grouped, "int8": build_int8, "grouped_nvfp4": build_grouped_nvfp4}
 
 
 # ---------------------------------------------------------------- timing
@@ -414,7 +458,8 @@ def main():
 
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
-                   "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel"}
+                   "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
+                   "grouped_nvfp4": "grouped_gemm_kernel"}
         write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
         return
 

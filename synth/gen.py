@@ -52,6 +52,7 @@ __all__ = [
     "Fp8Case",
     "Nvfp4Case",
     "GroupedCase",
+    "GroupedNvfp4Case",
     "Int8Case",
     "CONFIG2_SHAPES",
     "CONFIG2_M",
@@ -60,6 +61,7 @@ __all__ = [
     "config3_case",
     "config4_case",
     "config5_case",
+    "grouped_nvfp4_case",
 ]
 
 
@@ -263,6 +265,18 @@ class GroupedCase:
 
 
 @dataclass
+class GroupedNvfp4Case:
+    name: str
+    packed: np.ndarray       # uint8 [E, N, K/2]
+    scales: np.ndarray       # uint8 [E, N, K/16] E4M3 codes
+    x: np.ndarray            # uint16 [T, K]
+    a_offsets: np.ndarray    # uint32 [G+1]
+    expert_ids: np.ndarray   # int32 [G]
+    max_tokens: int
+    global_scale: float = 1.0
+
+
+@dataclass
 class Int8Case:
     name: str
     x: np.ndarray            # uint16 [M, K] bfloat16 activation
@@ -308,6 +322,17 @@ def config4_case(num_experts: int = 64, n: int = 1536, k: int = 2048, tokens: in
     offs, ids, counts = grouped_routing((4, 0), num_experts, tokens)
     return GroupedCase(f"grouped_e{num_experts}_n{n}_k{k}_t{tokens}", w.reshape(num_experts, n, k), x,
                        offs, ids, int(counts.max()), weight_scale=float(s))
+
+
+def grouped_nvfp4_case(num_experts: int = 64, n: int = 1536, k: int = 2048, tokens: int = 4096) -> GroupedNvfp4Case:
+    """Grouped MoE W4A16 NVFP4: the grouped workload's routing, activations and
+    shapes with the expert stack quantised to NVFP4 (one global scale)."""
+    packed, sc, g = nvfp4_weight((6, 0, 0), num_experts * n, k)
+    x = bf16_activation((4, 0, 1), tokens, k)
+    offs, ids, counts = grouped_routing((4, 0), num_experts, tokens)
+    return GroupedNvfp4Case(f"grouped_nvfp4_e{num_experts}_n{n}_k{k}_t{tokens}",
+                            packed.reshape(num_experts, n, k // 2), sc.reshape(num_experts, n, k // 16), x,
+                            offs, ids, int(counts.max()), float(g))
 
 
 def config5_case(n: int, m: int = 4096, k: int = 3072) -> Int8Case:

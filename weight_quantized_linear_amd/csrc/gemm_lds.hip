@@ -1122,7 +1122,10 @@ hipError_t launch_grouped_cfg(typename WP<BN, 1, NW>::Args wa, const uint16_t* x
 
 constexpr int kGrpBM = 64, kGrpBN = 128, kGrpS = 4, kGrpWY = 2, kGrpNW = 4;
 using GrpLayout = WqLayout<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
-using GrpLayoutFp4 = WqLayout<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>;
+// NVFP4 experts: the four waves side by side along N (each 64 x 32), so no
+// two waves decode the same weight rows (measured 5-10 % faster than 2 x 2).
+constexpr int kGrp4WY = 1;
+using GrpLayoutFp4 = WqLayout<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrp4WY, kGrpNW>;
 
 }  // namespace
 
@@ -1151,7 +1154,7 @@ hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales
                                     const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
                                     int64_t G, int64_t E, int64_t T, int64_t N, int64_t K, int num_cus,
                                     hipStream_t s) {
-  return launch_grouped_cfg<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(
+  return launch_grouped_cfg<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrp4WY, kGrpNW>(
       Nvfp4Args{packed, scales}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
 }
 
