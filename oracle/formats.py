@@ -32,7 +32,9 @@ __all__ = [
     "bf16_bits_to_f64",
     "f64_to_bf16_bits",
     "round_to_precision",
+    "f64_to_e4m3_codes",
     "BF16_MAX",
+    "E4M3_MAX",
 ]
 
 
@@ -139,3 +141,31 @@ def f64_to_bf16_bits(x) -> np.ndarray:
         sign = (np.signbit(x) & nan).astype(np.uint16) << np.uint16(15)
         bits = np.where(nan, np.uint16(0x7FC0) | sign, bits)
     return bits.astype(np.uint16)
+
+
+# Largest finite float8_e4m3fn magnitude: 1.75 * 2^8.
+E4M3_MAX = 448.0
+
+
+def f64_to_e4m3_codes(x) -> np.ndarray:
+    """Round float64 values to float8_e4m3fn (round to nearest, ties to even)
+    in one rounding and return the codes as uint8, field by field.
+
+    4 significant bits, minimum normal exponent -6 (subnormals on the grid
+    2^-9), sign kept (-0.0 and negative values that round to zero give 0x80).
+    Magnitudes beyond 448 saturate to 448; the caller clamps in the precision
+    it works in.  NaN is not accepted.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)):
+        raise ValueError("NaN has no saturating E4M3 code here")
+    r = round_to_precision(np.clip(x, -E4M3_MAX, E4M3_MAX), 4, -6)
+    mag = np.abs(r)
+    sign = np.signbit(r).astype(np.int64) << 7
+    _, E = np.frexp(np.where(mag > 0, mag, 1.0))        # mag = f * 2^E, 0.5 <= f < 1
+    e = E - 1                                            # exponent of the leading bit
+    normal = mag >= 2.0 ** -6
+    field_e = np.where(normal, e + 7, 0)
+    mant = np.where(normal, np.ldexp(mag, -e) - 1.0, np.ldexp(mag, 9))   # 1.m -> m in [0,1); subnormal: m/8 * 2^-6
+    field_m = np.where(normal, np.rint(mant * 8.0), np.rint(mant)).astype(np.int64)
+    return (sign | (field_e.astype(np.int64) << 3) | field_m).astype(np.uint8)

@@ -19,9 +19,11 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (
+    E4M3_MAX,
     bf16_bits_to_f64,
     e2m1_to_f64,
     e4m3_to_f64,
+    f64_to_e4m3_codes,
     unpack_nibbles,
 )
 
@@ -34,6 +36,8 @@ __all__ = [
     "int8_quantize_act",
     "int8_accumulate",
     "int8_epilogue",
+    "fp8_quantize_act",
+    "fp8_w8a8_linear",
 ]
 
 _ROW_CHUNK = 8192  # weight rows decoded to float64 at a time (bounds memory on the widest layer)
@@ -244,3 +248,45 @@ def int8_epilogue(acc, a_scale, b_scale, bias_bits=None):
     ref = prod + bias[None, :]
     tau = 2.0 ** -22 * (np.abs(prod) + np.abs(bias)[None, :]) + 1e-6
     return ref, tau
+
+
+def fp8_quantize_act(x_bits, input_scale: float) -> np.ndarray:
+    """Static per-tensor FP8 quantisation of a bfloat16 activation (W8A8).
+
+    fp8_gemv page, "Scale contract": the per-tensor ``input_scale`` of a
+    modelopt FP8 checkpoint cancels only while the activation stays bf16; for
+    fp8 activations it is the quantisation step.  Readings (the page gives no
+    formula): q = E4M3(clamp(x / input_scale, -448, 448)), the division one IEEE
+    float32 division and the rounding to nearest, ties to even, in one step from
+    that float32 quotient; input_scale > 0.  Returns uint8 E4M3 codes [M, K].
+    """
+    x = bf16_bits_to_f64(x_bits).astype(np.float32)             # exact widening
+    s = np.float32(input_scale)
+    if not s > 0:
+        raise ValueError("input_scale must be positive")
+    v = np.divide(x, s, dtype=np.float32)
+    v = np.clip(v, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return f64_to_e4m3_codes(v.astype(np.float64))
+
+
+def fp8_w8a8_linear(xq_codes, w_codes, alpha: float = 1.0):
+    """FP8 W8A8 linear: out = alpha * dec(xq) @ dec(W)^T, both operands E4M3.
+
+    The fp8_gemv page's weight and layout with fp8 activations: alpha is
+    input_scale * weight_scale, applied once to the float64 sum.  Every product
+    of two E4M3 values is exact.  Returns (ref [M, N], bound [M, N]).
+    """
+    x = e4m3_to_f64(xq_codes)
+    if x.ndim != 2:
+        raise ValueError("activation must be [M, K]")
+    w = np.asarray(w_codes, dtype=np.uint8)
+    m, n_rows = x.shape[0], w.shape[0]
+    ref = np.empty((m, n_rows), dtype=np.float64)
+    bound = np.empty((m, n_rows), dtype=np.float64)
+    ax = np.abs(x)
+    for lo in range(0, n_rows, _ROW_CHUNK):
+        hi = min(n_rows, lo + _ROW_CHUNK)
+        wd = e4m3_to_f64(w[lo:hi])
+        ref[:, lo:hi] = x @ wd.T
+        bound[:, lo:hi] = ax @ np.abs(wd).T
+    return alpha * ref, abs(alpha) * bound

@@ -8,6 +8,7 @@ from fractions import Fraction
 
 import numpy as np
 import pytest
+import torch
 
 from conftest import GOLDEN
 from oracle import formats as F
@@ -284,3 +285,71 @@ def test_int8_gemm_golden():
     nob, _ = R.int8_epilogue(acc, np.array(g["a_scale"], np.float32), np.array(g["b_scale"], np.float32))
     assert np.array_equal(nob, out - np.array([1.0, -3.0])[None, :])
     assert np.all(tau > 0)
+
+
+# ------------------------------------------------------------------ FP8 W8A8 (fp8 activations)
+
+def test_fp8_quantize_golden():
+    g = _load("fp8_quant_example.json")
+    x = synth.bf16_bits_from_f32(np.array([float(v) for v in g["x_values"]], np.float32))[None, :]
+    got = R.fp8_quantize_act(x, float(g["input_scale"]))[0]
+    assert [f"0x{c:02X}" for c in got] == g["codes"]
+
+
+def test_e4m3_encoder_round_trips_and_matches_torch():
+    """Every finite code decodes and re-encodes to itself; on a dense grid and
+    at every midpoint between neighbouring codes (the ties) the encoder agrees
+    with torch's float8_e4m3fn cast, an independent round-to-nearest-even."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = F.e4m3_to_f64(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(F.f64_to_e4m3_codes(vals[fin]), codes[fin])
+    pos = np.unique(vals[fin & (vals >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    grid = np.concatenate([np.linspace(-448, 448, 20001), np.linspace(-0.02, 0.02, 20001), mids, -mids])
+    grid = grid.astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(grid.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(F.f64_to_e4m3_codes(grid), want)
+    assert F.f64_to_e4m3_codes(np.array([449.0, 1e30, -464.0]))[0] == 0x7E      # saturation
+    assert list(F.f64_to_e4m3_codes(np.array([1e30, -464.0]))) == [0x7E, 0xFE]
+
+
+def test_fp8_quantize_error_bound():
+    """|dec(q) * s - x| is at most half an E4M3 spacing of x / s (relative 2^-4
+    for normals, 2^-10 absolute below 2^-6), or the saturation excess."""
+    x = synth.bf16_activation((80,), 16, 512, outlier_p=0.02, outlier_mul=50.0)
+    s = 0.01
+    q = R.fp8_quantize_act(x, s)
+    xv = F.bf16_bits_to_f64(x)
+    v = np.clip(xv / s, -448, 448)
+    d = F.e4m3_to_f64(q)
+    spacing = np.where(np.abs(v) >= 2.0 ** -6, np.ldexp(1.0, np.frexp(np.abs(v))[1] - 1 - 3), 2.0 ** -9)
+    assert np.all(np.abs(d - v) <= spacing / 2 * (1 + 1e-6) + 1e-12)
+    assert np.any(np.abs(xv / s) > 448)                         # the outliers saturate
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 3, 5), (3, 4, 64), (2, 2, 130)])
+def test_fp8_w8a8_linear_fraction_brute_force(m, n, k):
+    r = np.random.default_rng(m * 31 + k)
+    xq = r.integers(0, 256, size=(m, k), dtype=np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x38
+    w = r.integers(0, 256, size=(n, k), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x38
+    got, bound = R.fp8_w8a8_linear(xq, w, 0.375)
+    xd, wd = F.e4m3_to_f64(xq), F.e4m3_to_f64(w)
+    exact = _fraction_linear(wd, xd)
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(float(got[i, j])) - Fraction(3, 8) * exact[i][j]) <= \
+                Fraction(2.0 ** -40) * Fraction(float(bound[i, j]) + 1)
+
+
+def test_fp8_w8a8_equals_w8a16_on_decoded_activation():
+    """Every E4M3 value is a bfloat16, so the W8A8 product equals the W8A16
+    product of the decoded activation."""
+    r = np.random.default_rng(81)
+    xq = r.integers(0, 0x7E, size=(5, 96), dtype=np.uint8)
+    w = r.integers(0, 0x7E, size=(7, 96), dtype=np.uint8)
+    a, _ = R.fp8_w8a8_linear(xq, w, 2.0)
+    b, _ = R.fp8_linear(w, F.f64_to_bf16_bits(F.e4m3_to_f64(xq)), 2.0)
+    assert np.array_equal(a, b)
