@@ -14,7 +14,8 @@ fp32 out), "nvfp4" (W4A16 at M in {1, 128, 2048}, N = K = 4096), "grouped"
 (MoE W8A16, 64 experts [64, 1536, 2048], 4096 Zipf-routed tokens),
 "grouped_nvfp4" (the same routing and shapes with NVFP4 experts), "int8"
 (W8A8: activation quantiser + int8 GEMM at N in {3072, 12288}, M = 4096,
-K = 3072).  Where a workload's weights would fit the last-level cache, the
+K = 3072), "fp8_w8a8" (the same shapes with a static per-tensor E4M3
+activation quantiser and the fp8 GEMM).  Where a workload's weights would fit the last-level cache, the
 timed graph cycles through enough copies of them (>= 1 GiB) that every read
 comes from HBM.
 
@@ -22,7 +23,7 @@ The step is captured once into a HIP graph (torch.cuda.CUDAGraph) and the
 graph is replayed: host-side launch overhead of the Python binding would
 otherwise exceed the 5-20 us kernels.  Prints ONE JSON line: value =
 algorithmic traffic (decode, gemv2048, grouped, grouped_nvfp4: weights +
-activations + outputs once, GB/s) or work (nvfp4: TFLOP/s, int8: TOPS) per step / step
+activations + outputs once, GB/s) or work (nvfp4, fp8_w8a8: TFLOP/s, int8: TOPS) per step / step
 time; ``roofline`` for the workload's dominant kernel, whose average launch
 duration is measured with HIP events around a graph of back-to-back launches
 of that kernel on its stream; ``cpu_baseline`` = the CPU oracle on a bounded
@@ -47,6 +48,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
+FP8_PEAK_TFLOPS = 5000.0
 POOL_BYTES = 1 << 30
 
 
@@ -406,8 +408,52 @@ def build_int8(dev, q, synth, np, torch):
                 baseline=baseline)
 
 
+def build_fp8_w8a8(dev, q, synth, np, torch):
+    m, k = 4096, 3072
+    cases = []
+    c0 = synth.fp8_w8a8_case(3072)
+    x = bf16_dev(c0.x, dev, np, torch)
+    qa = torch.empty((m, k), dtype=torch.uint8, device=dev)
+
+    def quant(copy):
+        q.fp8_quantize_act(x, c0.input_scale, q=qa)
+    cases.append(Case("fp8 quantize m=4096 k=3072", quant, m * k * 2 + m * k, 0))
+    for n in (3072, 12288):
+        c = synth.fp8_w8a8_case(n)
+        copies = copies_for(c.w.nbytes)
+        pw = [torch.from_numpy(c.w).to(dev) for _ in range(copies)]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        alpha = float(np.float32(c0.input_scale) * np.float32(c.weight_scale))
+
+        def run(copy, pw=pw, out=out, alpha=alpha):
+            q.fp8_w8a8_gemm(qa, pw[copy % len(pw)], out=out, alpha=alpha)
+        cases.append(Case(f"fp8 w8a8 gemm m={m} n={n} k={k}", run, m * k + n * k + m * n * 2, 2 * m * n * k, copies))
+
+    def baseline():
+        from oracle import ref
+        rows = 256
+        t0 = time.perf_counter()
+        qx = ref.fp8_quantize_act(c0.x, c0.input_scale)
+        flops = 0
+        for n in (3072, 12288):
+            c = synth.fp8_w8a8_case(n)
+            ref.fp8_w8a8_linear(qx[:rows], c.w, c0.input_scale * c.weight_scale)
+            flops += 2 * rows * n * k
+        el = time.perf_counter() - t0
+        return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"quantiser on all 4096 rows + GEMM on the first {rows} rows for both N ({el:.1f} s)"}
+
+    return dict(metric="FP8 W8A8 GEMM TFLOP/s (static per-tensor activation quantiser + fp8 GEMM)", unit="TFLOP/s",
+                per="work", cases=cases, dominant=cases[2], bound="mfma", peak=FP8_PEAK_TFLOPS,
+                kernel="fp8_w8a8_lds_kernel<256, 128> (M=4096, N=12288, K=3072)", dtype="f8",
+                config={"workload": "fp8_w8a8: quantise bf16 [4096,3072] to E4M3 + fp8 GEMM N in {3072,12288}, "
+                                    "bf16 out"},
+                baseline=baseline)
+
+
 WORKLOADS = {"decode": build_decode, "gemv2048": build_gemv2048, "nvfp4": build_nvfp4,
-             "grouped": build_grouped, "int8": build_int8, "grouped_nvfp4": build_grouped_nvfp4}
+             "grouped": build_grouped, "int8": build_int8, "grouped_nvfp4": build_grouped_nvfp4,
+             "fp8_w8a8": build_fp8_w8a8}
 
 
 # ---------------------------------------------------------------- timing
@@ -459,7 +505,7 @@ def main():
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
                    "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
-                   "grouped_nvfp4": "grouped_gemm_kernel"}
+                   "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds_kernel"}
         write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
         return
 

@@ -159,6 +159,32 @@ int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x,
                        void* stream);
 
 /*
+ * FP8 activation quantisation for W8A8, page "fp8_gemv" ("Scale contract":
+ * the checkpoint's per-tensor input_scale cancels only while the activation
+ * stays bf16; with fp8 activations it is the quantisation step):
+ *     q[m, k] = E4M3(clamp(x[m, k] / input_scale, -448, 448))
+ * one IEEE float32 division, round to nearest even, float8_e4m3fn codes.
+ * x: bfloat16 [M, K] (2-byte aligned); q: uint8 [M, K]; input_scale: finite
+ * and > 0, else QLINEAR_ERR_INVALID_ARG.  Non-finite activations are outside
+ * the contract.
+ */
+int qlinear_fp8_quantize_act(const void* x, void* q, float input_scale, int64_t M, int64_t K,
+                             void* stream);
+
+/*
+ * FP8 W8A8 matmul, page "fp8_gemv" with fp8 activations:
+ *     out[m, n] = alpha * sum_k dec_e4m3(xq[m, k]) * dec_e4m3(w[n, k])
+ * alpha = input_scale * weight_scale, applied in float32 before the single
+ * output rounding; every product is exact and accumulation is float32.
+ * xq: float8_e4m3fn [M, K] (as made by qlinear_fp8_quantize_act); w:
+ * float8_e4m3fn [N, K]; out: [M, N] of out_dtype (F32 or BF16).  K % 64 == 0
+ * with 16-byte aligned operands under 4 GiB runs on the gfx950 fp8 matrix
+ * cores; any other shape takes a slow element-wise kernel.
+ */
+int qlinear_fp8_w8a8_gemm(const void* xq, const void* w, void* out, int out_dtype,
+                          int64_t M, int64_t N, int64_t K, float alpha, void* stream);
+
+/*
  * Grouped (MoE) W4A16 NVFP4 matmul: the ragged addressing of page
  * "Matmul2dFp8" (run_grouped) with the weight format of page "fp4_matmul".
  * For every group z, rows r in [a_offsets[z], a_offsets[z+1]):

@@ -129,12 +129,14 @@ def check_bf16(gpu_bits, ref, tau) -> CheckResult:
     return CheckResult(True, 0, None, n_clause2=n_c2)
 
 
-def clause2_budget(ref) -> int:
+def clause2_budget(ref, share: float = 1e-3) -> int:
     """How many outputs may legitimately need clause 2 of ``check_bf16``.
 
     Clause 1 fails only where the float32 summation error exceeds one
     bfloat16 ulp of the result, i.e. |result| below about 2^8 sqrt(K) 2^-24
     times the typical magnitude of the partial sums; for Gaussian data and
-    K <= 14336 that is well under 1e-3 of the outputs.  Returns that share of
-    the outputs, plus 2."""
-    return int(1e-3 * np.asarray(ref).size) + 2
+    K <= 14336 that is well under 1e-3 of the outputs.  A kernel whose
+    accumulation is coarser than a float32 sum (still inside the tolerance
+    of ``fp_tolerance``) passes a larger ``share``.  Returns that share of the
+    outputs, plus 2."""
+    return int(share * np.asarray(ref).size) + 2

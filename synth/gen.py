@@ -62,6 +62,9 @@ __all__ = [
     "config4_case",
     "config5_case",
     "grouped_nvfp4_case",
+    "Fp8W8A8Case",
+    "fp8_w8a8_case",
+    "dyadic_e4m3_activation",
 ]
 
 
@@ -277,6 +280,15 @@ class GroupedNvfp4Case:
 
 
 @dataclass
+class Fp8W8A8Case:
+    name: str
+    x: np.ndarray            # uint16 [M, K] bfloat16 bits
+    input_scale: float       # static per-tensor activation scale (absmax / 448)
+    w: np.ndarray            # uint8 [N, K] E4M3 codes
+    weight_scale: float
+
+
+@dataclass
 class Int8Case:
     name: str
     x: np.ndarray            # uint16 [M, K] bfloat16 activation
@@ -333,6 +345,25 @@ def grouped_nvfp4_case(num_experts: int = 64, n: int = 1536, k: int = 2048, toke
     return GroupedNvfp4Case(f"grouped_nvfp4_e{num_experts}_n{n}_k{k}_t{tokens}",
                             packed.reshape(num_experts, n, k // 2), sc.reshape(num_experts, n, k // 16), x,
                             offs, ids, int(counts.max()), float(g))
+
+
+def fp8_w8a8_case(n: int, m: int = 4096, k: int = 3072) -> Fp8W8A8Case:
+    """FP8 W8A8 at the W8A8 shapes: bf16 activation N(0, 1) with 1% x20
+    outliers and a static per-tensor input_scale = absmax / 448 (a calibration
+    of this very tensor), E4M3 weight of N(0, 0.02^2) with its per-tensor scale."""
+    x = bf16_activation((7, n, 1), m, k, outlier_p=0.01)
+    xf = f32_from_bf16_bits_torch(x)
+    input_scale = float(np.float32(np.max(np.abs(xf)) / np.float32(448.0)))
+    w, s = fp8_weight((7, n, 0), n, k)
+    return Fp8W8A8Case(f"fp8_w8a8_m{m}_n{n}_k{k}", x, input_scale, w, float(s))
+
+
+def dyadic_e4m3_activation(key, m: int, k: int) -> np.ndarray:
+    """E4M3 codes of integers in [-4, 4]: with ``dyadic_fp8_weight`` every
+    partial sum of a W8A8 product is exact in float32 up to K = 2^18 / 64."""
+    r = rng_for(*key)
+    v = r.integers(-4, 5, size=(m, k)).astype(np.float32)
+    return e4m3_codes_from_f32(v)
 
 
 def config5_case(n: int, m: int = 4096, k: int = 3072) -> Int8Case:

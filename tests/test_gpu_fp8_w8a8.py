@@ -1,0 +1,119 @@
+"""GPU parity of the FP8 W8A8 calls (qlinear_fp8_quantize_act,
+qlinear_fp8_w8a8_gemm) against the CPU oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import compare as C
+from oracle import formats as F
+from oracle import ref as R
+from gpu_util import DEV, bf16_bits, show, to_dev_bf16, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import weight_quantized_linear_amd as q
+    return q
+
+
+def _finite_bf16_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    return bits[finite]
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.5, 0.0123, 3.7, 2.0 ** -20, 1e6])
+def test_quantizer_every_bf16_input_bit_exact(q, scale):
+    """Every finite bfloat16 value through the fast (16-byte) kernel: the codes
+    equal the CPU encoder's, ties, subnormals, signed zeros and saturation included."""
+    bits = _finite_bf16_patterns()
+    pad = (-bits.size) % 256
+    x = np.concatenate([bits, np.zeros(pad, np.uint16)]).reshape(-1, 256)
+    show("fp8 quant all bf16", scale)
+    got = q.fp8_quantize_act(to_dev_bf16(x), scale).cpu().numpy()
+    assert np.array_equal(got, R.fp8_quantize_act(x, scale))
+
+
+def test_quantizer_unaligned_and_odd_shapes(q):
+    """Odd K and a 2-byte offset base take the element-wise kernel."""
+    x = synth.bf16_activation((90,), 1, 3 * 1001 + 1, outlier_p=0.05, outlier_mul=200.0)
+    xd = to_dev_bf16(x)[0, 1:].reshape(3, 1001)
+    show("fp8 quant unaligned")
+    got = q.fp8_quantize_act(xd, 0.01).cpu().numpy()
+    assert np.array_equal(got, R.fp8_quantize_act(x[0, 1:].reshape(3, 1001), 0.01))
+
+
+def test_quantizer_rejects_bad_scale(q):
+    x = torch.zeros((2, 8), dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros((2, 8), dtype=torch.uint8, device=DEV)
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert q.lib.qlinear_fp8_quantize_act(x.data_ptr(), out.data_ptr(), s, 2, 8, None) == q.ERR_INVALID_ARG
+
+
+W8A8_DYADIC = [(256, 128, 64), (300, 200, 512), (1, 7, 4096), (513, 1000, 1024), (64, 2048, 128),
+               (5, 9, 100), (33, 17, 2050)]  # the last two: K % 64 != 0, element-wise kernel
+
+
+@pytest.mark.parametrize("m,n,k", W8A8_DYADIC)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_w8a8_dyadic_bit_exact(q, m, n, k, out_dtype):
+    xq = synth.dyadic_e4m3_activation((91, m, n, k), m, k)
+    w = synth.dyadic_fp8_weight((92, m, n, k), n, k)
+    ref, _ = R.fp8_w8a8_linear(xq, w, 0.5)
+    show("w8a8 dyadic", m, n, k, out_dtype)
+    out = q.fp8_w8a8_gemm(to_dev_u8(xq), to_dev_u8(w), out_dtype=out_dtype, alpha=0.5)
+    if out_dtype == torch.float32:
+        assert np.array_equal(out.cpu().numpy(), ref.astype(np.float32))
+    else:
+        assert np.array_equal(bf16_bits(out), F.f64_to_bf16_bits(ref))
+
+
+def test_w8a8_every_code_pair(q):
+    """One-hot activations pick single weight columns: out = dec(xq) * dec(w)
+    for every pair of finite codes (each product exact)."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]                     # 254 finite codes
+    k = 256
+    w = np.zeros((codes.size, k), np.uint8)
+    w[:, :codes.size] = np.diag(codes)                        # row n holds code n at k = n
+    xq = np.zeros((codes.size, k), np.uint8)
+    xq[:, :codes.size] = codes[:, None]                       # row m holds code m everywhere
+    show("w8a8 code pairs")
+    out = q.fp8_w8a8_gemm(to_dev_u8(xq), to_dev_u8(w), out_dtype=torch.float32).cpu().numpy()
+    ref, _ = R.fp8_w8a8_linear(xq, w)
+    assert np.array_equal(out, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("n", [3072, 12288])
+def test_w8a8_workload(q, n):
+    c = synth.fp8_w8a8_case(n)
+    show("w8a8 workload", c.name)
+    xd = to_dev_bf16(c.x)
+    qd = q.fp8_quantize_act(xd, c.input_scale)
+    alpha = float(np.float32(c.input_scale) * np.float32(c.weight_scale))
+    out = q.fp8_w8a8_gemm(qd, to_dev_u8(c.w), out_dtype=torch.bfloat16, alpha=alpha)
+    torch.cuda.synchronize()
+    want_q = R.fp8_quantize_act(c.x, c.input_scale)
+    assert np.array_equal(qd.cpu().numpy(), want_q)
+    rows = np.unique(np.concatenate([np.random.default_rng(n).choice(c.x.shape[0], 256, replace=False),
+                                     np.arange(c.x.shape[0] - 5, c.x.shape[0])]))
+    ref, bound = R.fp8_w8a8_linear(want_q[rows], c.w, alpha)
+    res = C.check_bf16(bf16_bits(out)[rows], ref, C.fp_tolerance(bound))
+    # The fp8 matrix-core instruction accumulates more coarsely than a float32
+    # sum (measured on this workload: error up to 3e-5 B against 7e-8 B for the
+    # bf16 instruction on the same decoded operands, both far inside the
+    # 2e-3 B tolerance), so about 0.3 % of outputs need the cancellation clause.
+    assert res and res.n_clause2 <= C.clause2_budget(ref, share=1e-2), res
+
+
+def test_w8a8_rejects_bad_arguments(q):
+    xq = torch.zeros((2, 64), dtype=torch.uint8, device=DEV)
+    w = torch.zeros((3, 32), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        q.fp8_w8a8_gemm(xq, w)                                 # K mismatch
+    st = q.lib.qlinear_fp8_w8a8_gemm(xq.data_ptr(), w.data_ptr(), xq.data_ptr(), 2, 2, 3, 64, 1.0, None)
+    assert st == q.ERR_INVALID_ARG                             # int32 output is not a W8A8 output type

@@ -28,6 +28,8 @@ __all__ = [
     "fp8_materialize",
     "fp8_grouped_gemm",
     "nvfp4_grouped_gemm",
+    "fp8_quantize_act",
+    "fp8_w8a8_gemm",
     "nvfp4_gemm",
     "nvfp4_dequant",
     "int8_quantize_act",
@@ -54,6 +56,8 @@ EXPORTED = {
     "qlinear_fp8_grouped_gemm": [_p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_nvfp4_gemm": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _p],
     "qlinear_nvfp4_grouped_gemm": [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
+    "qlinear_fp8_quantize_act": [_p, _p, _f, _i64, _i64, _p],
+    "qlinear_fp8_w8a8_gemm": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _p],
     "qlinear_nvfp4_gemm_path": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _i, _p],
     "qlinear_nvfp4_dequant": [_p, _p, _p, _i, _i64, _i64, _p],
     "qlinear_int8_quantize_act": [_p, _p, _p, _i64, _i64, _p],
@@ -201,6 +205,40 @@ def fp8_grouped_gemm(w: torch.Tensor, x: torch.Tensor, a_offsets: torch.Tensor, 
     st = lib.qlinear_fp8_grouped_gemm(_ptr(w), _ptr(x), _ptr(a_offsets), _ptr(expert_ids), _ptr(out),
                                       _OUT_CODES[out_dtype], g, int(max_tokens_per_group), e, t, n, k, _stream(x))
     _check(st, "qlinear_fp8_grouped_gemm")
+    return out
+
+
+def fp8_quantize_act(x: torch.Tensor, input_scale: float, q: torch.Tensor | None = None) -> torch.Tensor:
+    """Static per-tensor FP8 activation quantisation (``qlinear_fp8_quantize_act``):
+    q = E4M3(clamp(x / input_scale, -448, 448)) as uint8 codes [M, K]."""
+    x = _as_bf16(x, "x")
+    _require(x, "x")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    elif q.dtype != torch.uint8 or tuple(q.shape) != (m, k) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous uint8 [M, K] tensor")
+    st = lib.qlinear_fp8_quantize_act(_ptr(x), _ptr(q), float(input_scale), m, k, _stream(x))
+    _check(st, "qlinear_fp8_quantize_act")
+    return q
+
+
+def fp8_w8a8_gemm(xq: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,
+                  out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0) -> torch.Tensor:
+    """FP8 W8A8 (``qlinear_fp8_w8a8_gemm``): out = alpha * dec(xq) @ dec(w)^T,
+    xq and w float8_e4m3fn codes (uint8 or float8 tensors)."""
+    xq = _as_u8(xq, "xq")
+    w = _as_u8(w, "w")
+    for t, name in ((xq, "xq"), (w, "w")):
+        _require(t, name)
+    m, k = xq.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("xq must be [M, K] and w [N, K]")
+    out = _out(out, (m, n), out_dtype, xq.device)
+    st = lib.qlinear_fp8_w8a8_gemm(_ptr(xq), _ptr(w), _ptr(out), _OUT_CODES[out_dtype], m, n, k, float(alpha),
+                                   _stream(xq))
+    _check(st, "qlinear_fp8_w8a8_gemm")
     return out
 
 

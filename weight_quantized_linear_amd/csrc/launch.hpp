@@ -72,6 +72,15 @@ hipError_t launch_nvfp4_grouped(const uint8_t* packed, const uint8_t* scales, co
                                 int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
                                 int num_cus, hipStream_t s);
 
+// fp8_w8a8.hip (FP8 activations: static per-tensor quantiser, fp8 x fp8 GEMM)
+hipError_t launch_fp8_quantize_act(const uint16_t* x, uint8_t* q, float input_scale, int64_t M, int64_t K,
+                                   int num_cus, hipStream_t s);
+hipError_t launch_fp8_w8a8_gemm(const uint8_t* xq, const uint8_t* w, void* out, int out_bf16, int64_t M, int64_t N,
+                                int64_t K, float alpha, int num_cus, hipStream_t s);
+// gemm_lds.hip: the pipelined fp8 x fp8 kernel (K % 64 == 0, aligned, int8_lds_supported).
+hipError_t launch_fp8_w8a8_lds(const uint8_t* xq, const uint8_t* w, void* out, int out_bf16, int64_t M, int64_t N,
+                               int64_t K, float alpha, int num_cus, hipStream_t s);
+
 // nvfp4.hip
 hipError_t launch_nvfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,

@@ -238,6 +238,27 @@ int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_off
                                    static_cast<hipStream_t>(stream)));
 }
 
+int qlinear_fp8_quantize_act(const void* x, void* q, float input_scale, int64_t M, int64_t K, void* stream) {
+  if (!x || !q || M <= 0 || K <= 0 || !fits(M, K) || !aligned(x, 2)) return QLINEAR_ERR_INVALID_ARG;
+  if (!(input_scale > 0.f) || !(input_scale <= std::numeric_limits<float>::max())) return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_fp8_quantize_act(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), input_scale, M, K,
+                                        num_cus, static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_fp8_w8a8_gemm(const void* xq, const void* w, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                          float alpha, void* stream) {
+  if (!xq || !w || !out || M <= 0 || N <= 0 || K <= 0 || !fits(M, K) || !fits(N, K) || !fits(M, N))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!float_out_ok(out_dtype) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_fp8_w8a8_gemm(static_cast<const uint8_t*>(xq), static_cast<const uint8_t*>(w), out,
+                                     out_dtype == QLINEAR_BF16, M, N, K, alpha, num_cus,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 int qlinear_nvfp4_grouped_gemm(const void* w_packed, const void* w_scale, const void* x, const uint32_t* a_offsets,
                                const int32_t* expert_ids, void* out, int out_dtype, int64_t num_groups,
                                int64_t max_tokens_per_group, int64_t num_experts, int64_t T, int64_t N, int64_t K,
