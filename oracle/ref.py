@@ -38,6 +38,7 @@ __all__ = [
     "int8_epilogue",
     "fp8_quantize_act",
     "fp8_w8a8_linear",
+    "bf16_linear",
 ]
 
 _ROW_CHUNK = 8192  # weight rows decoded to float64 at a time (bounds memory on the widest layer)
@@ -290,3 +291,22 @@ def fp8_w8a8_linear(xq_codes, w_codes, alpha: float = 1.0):
         ref[:, lo:hi] = x @ wd.T
         bound[:, lo:hi] = ax @ np.abs(wd).T
     return alpha * ref, abs(alpha) * bound
+
+
+def bf16_linear(w_bits, x_bits, alpha: float = 1.0):
+    """Dense control: out = alpha * x @ W^T with a bfloat16 weight [N, K].
+
+    The comparison point the quantized paths are measured against: the bf16
+    weight path of the fp8_gemv page ("WHY it wins at decode": 2 bytes per
+    weight against W8A16's 1) and the dense bf16 GEMM the Matmul2dFp8 page's
+    tiled kernel mirrors with only the weight type changed (summary).
+    w_bits: uint16 [N, K]; x_bits: uint16 [M, K].  Returns (ref, bound),
+    both float64 [M, N].
+    """
+    w = np.asarray(w_bits, dtype=np.uint16)
+    if w.ndim != 2:
+        raise ValueError("weight must be [N, K]")
+    x = np.asarray(x_bits, dtype=np.uint16)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("K mismatch")
+    return _linear(lambda lo, hi: bf16_bits_to_f64(w[lo:hi]), w.shape[0], x, alpha)

@@ -353,3 +353,49 @@ def test_fp8_w8a8_equals_w8a16_on_decoded_activation():
     a, _ = R.fp8_w8a8_linear(xq, w, 2.0)
     b, _ = R.fp8_linear(w, F.f64_to_bf16_bits(F.e4m3_to_f64(xq)), 2.0)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ dense bf16 control
+
+def _torch_bf16_values(bits):
+    """bfloat16 bits -> float64 through torch's own bfloat16 type (not the
+    oracle's decoder)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.double().numpy()
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 3, 5), (2, 5, 7), (4, 3, 40), (3, 1, 2)])
+def test_bf16_linear_fraction_brute_force(m, n, k):
+    r = np.random.default_rng(m * 7 + n * 3 + k)
+    w = synth.bf16_bits_from_f32((r.standard_normal((n, k)) * 0.05).astype(np.float32))
+    x = synth.bf16_bits_from_f32(r.standard_normal((m, k)).astype(np.float32))
+    got, bound = R.bf16_linear(w, x, 0.75)
+    exact = _fraction_linear(_torch_bf16_values(w), _torch_bf16_values(x))
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(float(got[i, j])) - Fraction(3, 4) * exact[i][j]) <= \
+                Fraction(2.0 ** -40) * Fraction(float(bound[i, j]) + 1)
+            b = sum(abs(Fraction(float(a)) * Fraction(float(c)))
+                    for a, c in zip(_torch_bf16_values(x)[i], _torch_bf16_values(w)[j]))
+            assert abs(Fraction(float(bound[i, j])) - Fraction(3, 4) * b) <= Fraction(2.0 ** -40) * (b + 1)
+
+
+def test_bf16_linear_identity_weight():
+    """W = I returns the activation itself (x @ I^T = x), exactly."""
+    x = synth.bf16_activation((81,), 3, 24)
+    eye = np.where(np.eye(24, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    got, _ = R.bf16_linear(eye, x)
+    assert np.array_equal(got, _torch_bf16_values(x))
+
+
+def test_bf16_linear_equals_fp8_linear_on_widened_weight():
+    """Every E4M3 value is a bfloat16: the dense product of the weight widened
+    by torch's float8 -> bfloat16 cast equals the W8A16 product."""
+    r = np.random.default_rng(82)
+    w = r.integers(0, 256, size=(9, 80), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x38
+    wb = torch.from_numpy(w).view(torch.float8_e4m3fn).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    x = synth.bf16_activation((82,), 4, 80)
+    a, ba = R.bf16_linear(wb, x, 1.5)
+    b, bb = R.fp8_linear(w, x, 1.5)
+    assert np.array_equal(a, b) and np.array_equal(ba, bb)
