@@ -15,7 +15,9 @@ fp32 out), "nvfp4" (W4A16 at M in {1, 128, 2048}, N = K = 4096), "grouped"
 "grouped_nvfp4" (the same routing and shapes with NVFP4 experts), "int8"
 (W8A8: activation quantiser + int8 GEMM at N in {3072, 12288}, M = 4096,
 K = 3072), "fp8_w8a8" (the same shapes with a static per-tensor E4M3
-activation quantiser and the fp8 GEMM).  Where a workload's weights would fit the last-level cache, the
+activation quantiser and the fp8 GEMM), "bf16_decode" (the decode cases with
+a dense bf16 weight: the control that 1 vs 2 bytes per weight is measured
+against).  Where a workload's weights would fit the last-level cache, the
 timed graph cycles through enough copies of them (>= 1 GiB) that every read
 comes from HBM.
 
@@ -208,6 +210,54 @@ def build_decode(dev, q, synth, np, torch):
         dtype="f32",
         config={"workload": "fp8_w8a16_decode: M in {1,4,16} x (N,K) in {(4096,4096),(14336,4096),"
                             "(4096,14336),(128256,4096)}, E4M3 weight, bf16 activation, bf16 out"},
+        baseline=baseline)
+
+
+def build_bf16_decode(dev, q, synth, np, torch):
+    """The decode step's 12 cases with a dense bf16 weight (the control the
+    W8A16 kernels are measured against: 2 bytes per weight instead of 1)."""
+    shapes = ((4096, 4096), (14336, 4096), (4096, 14336), (128256, 4096))
+    ms = (1, 4, 16)
+    weights, heads = {}, {}
+    for si, (n, k) in enumerate(shapes):
+        wb = synth.bf16_weight((34, si), n, k)
+        weights[si] = bf16_dev(wb, dev, np, torch)
+        heads[si] = wb[:12288].copy()
+        del wb
+    cases = []
+    for m in ms:
+        for si, (n, k) in enumerate(shapes):
+            x = bf16_dev(synth.bf16_activation((2, si, 1, m), m, k), dev, np, torch)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            nbytes = n * k * 2 + m * k * 2 + m * n * 2
+
+            def run(copy, w=weights[si], x=x, out=out):
+                q.bf16_gemm(w, x, out=out, out_dtype=torch.bfloat16)
+            cases.append(Case(f"bf16 m={m} n={n} k={k}", run, nbytes, 2 * m * n * k))
+    dominant = cases[3]
+
+    def baseline():
+        from oracle import ref
+        total, elapsed = 0, 0.0
+        for m in ms:
+            for si, (n, k) in enumerate(shapes):
+                x = synth.bf16_activation((2, si, 1, m), m, k)
+                t0 = time.perf_counter()
+                ref.bf16_linear(heads[si], x)
+                elapsed += time.perf_counter() - t0
+                rows = heads[si].shape[0]
+                total += rows * k * 2 + m * k * 2 + m * rows * 2
+        return {"value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"first 12288 weight rows (all 4096 where N = 4096) of each of the 12 (M, N, K) cases, "
+                          f"full K ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
+
+    return dict(
+        metric="Dense bf16 control: GEMV M=1 achieved HBM GB/s (decode shapes, 2-byte weights)",
+        unit="GB/s", per="bytes", cases=cases, dominant=dominant, bound="hbm", peak=HBM_PEAK_GBS,
+        kernel="bf16_gemv_wide_kernel<1,2,4> (M=1, N=128256, K=4096)",
+        dtype="f32",
+        config={"workload": "bf16_decode: M in {1,4,16} x (N,K) in {(4096,4096),(14336,4096),"
+                            "(4096,14336),(128256,4096)}, bf16 weight, bf16 activation, bf16 out"},
         baseline=baseline)
 
 
@@ -453,7 +503,7 @@ def build_fp8_w8a8(dev, q, synth, np, torch):
 
 WORKLOADS = {"decode": build_decode, "gemv2048": build_gemv2048, "nvfp4": build_nvfp4,
              "grouped": build_grouped, "int8": build_int8, "grouped_nvfp4": build_grouped_nvfp4,
-             "fp8_w8a8": build_fp8_w8a8}
+             "fp8_w8a8": build_fp8_w8a8, "bf16_decode": build_bf16_decode}
 
 
 # ---------------------------------------------------------------- timing
@@ -505,7 +555,8 @@ def main():
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
                    "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
-                   "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds_kernel"}
+                   "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds_kernel",
+                   "bf16_decode": "bf16_gemv_wide_kernel"}
         write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
         return
 

@@ -248,6 +248,27 @@ int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const 
                       const void* bias, void* out, int out_dtype, int64_t M, int64_t N,
                       int64_t K, void* stream);
 
+/*
+ * Dense bf16 control matmul: the bf16 weight path that page "fp8_gemv"
+ * ("WHY it wins at decode") compares W8A16 against (2 bytes per weight
+ * against 1) and the dense GEMM that page "Matmul2dFp8" (summary) mirrors:
+ *     out[m, n] = alpha * sum_k x[m, k] * w[n, k]
+ * w: bfloat16 [N, K]; x: bfloat16 [M, K]; out: [M, N] of out_dtype (F32 or
+ * BF16); alpha applied in float32 before the single output rounding;
+ * float32 accumulation of exact products.  Any K >= 1 and alignment (both
+ * operands 2-byte aligned); K % 8 == 0 with 16-byte aligned operands takes
+ * the wide-load kernels.  The kernel families are those of
+ * qlinear_fp8_gemm: GEMV (M <= 4), skinny (M <= 16), tiled (any M; the
+ * tiled GEMM shares the split-K workspace and its stream-ordering rule).
+ */
+int qlinear_bf16_gemm(const void* w, const void* x, void* out, int out_dtype,
+                      int64_t M, int64_t N, int64_t K, float alpha, void* stream);
+
+/* As qlinear_bf16_gemm with the kernel family forced (see qlinear_fp8_gemm_path). */
+int qlinear_bf16_gemm_path(const void* w, const void* x, void* out, int out_dtype,
+                           int64_t M, int64_t N, int64_t K, float alpha, int path,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

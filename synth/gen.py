@@ -62,6 +62,8 @@ __all__ = [
     "config4_case",
     "config5_case",
     "grouped_nvfp4_case",
+    "bf16_weight",
+    "dyadic_bf16_weight",
     "Fp8W8A8Case",
     "fp8_w8a8_case",
     "dyadic_e4m3_activation",
@@ -212,6 +214,20 @@ def dyadic_fp8_weight(key, n: int, k: int) -> np.ndarray:
     ok = np.isfinite(vals) & (np.abs(vals) <= 16) & (np.mod(vals * 16, 1) == 0)
     pool = allc[ok]
     return rng_for(*key).choice(pool, size=(n, k)).astype(np.uint8)
+
+
+def bf16_weight(key, n: int, k: int) -> np.ndarray:
+    """bfloat16 bits [N, K] of N(0, 0.02^2): the dense control's weight."""
+    w = rng_for(*key).standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    return bf16_bits_from_f32(w)
+
+
+def dyadic_bf16_weight(key, n: int, k: int) -> np.ndarray:
+    """bfloat16 bits of multiples of 2^-4 with magnitude <= 16 (the values of
+    ``dyadic_fp8_weight``): with ``dyadic_activation`` every partial sum is
+    exact in float32."""
+    vals = e4m3_values_torch(dyadic_fp8_weight(key, n, k)).astype(np.float32)
+    return bf16_bits_from_f32(vals)
 
 
 def dyadic_activation(key, m: int, k: int, lo: int = -4, hi: int = 4) -> np.ndarray:

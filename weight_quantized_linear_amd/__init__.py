@@ -25,6 +25,7 @@ __all__ = [
     "EXPORTED",
     "fp8_gemv",
     "fp8_gemm",
+    "bf16_gemm",
     "fp8_materialize",
     "fp8_grouped_gemm",
     "nvfp4_grouped_gemm",
@@ -52,6 +53,8 @@ EXPORTED = {
     "qlinear_fp8_gemv": [_p, _p, _p, _i, _i64, _i64, _f, _p],
     "qlinear_fp8_gemm": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _p],
     "qlinear_fp8_gemm_path": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _i, _p],
+    "qlinear_bf16_gemm": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _p],
+    "qlinear_bf16_gemm_path": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _i, _p],
     "qlinear_fp8_materialize": [_p, _p, _i, _i64, _i64, _p],
     "qlinear_fp8_grouped_gemm": [_p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_nvfp4_gemm": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _p],
@@ -148,6 +151,24 @@ def fp8_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     st = lib.qlinear_fp8_gemm_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
                                    float(alpha), PATHS[path], _stream(x))
     _check(st, "qlinear_fp8_gemm")
+    return out
+
+
+def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+              out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto") -> torch.Tensor:
+    """Dense bf16 control: out[M, N] = alpha * x[M, K] @ w[N, K]^T (``qlinear_bf16_gemm``)."""
+    w = _as_bf16(w, "w")
+    x = _as_bf16(x, "x")
+    _require(w, "w")
+    _require(x, "x")
+    if w.dim() != 2 or x.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError(f"shapes: w {tuple(w.shape)} must be [N, K], x {tuple(x.shape)} must be [M, K]")
+    m, k = x.shape
+    n = w.shape[0]
+    out = _out(out, (m, n), out_dtype, x.device)
+    st = lib.qlinear_bf16_gemm_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
+                                    float(alpha), PATHS[path], _stream(x))
+    _check(st, "qlinear_bf16_gemm")
     return out
 
 

@@ -162,11 +162,29 @@ __device__ __forceinline__ void w_store(char* lds, const Nvfp4Tile&, const Nvfp4
   }
 }
 
+// ---------------------------------------------------------------- bf16 weight tile (dense control)
+
+// The weight tile has the activation tile's layout and loads.
+struct Bf16Tile {
+  const uint16_t* w;  // [N, K] bfloat16
+  int64_t N, K;
+  bool vec;           // K % 8 == 0 and 16-byte aligned base
+};
+
+struct Bf16Stage { ActStage a; };
+
+__device__ __forceinline__ void w_load(const Bf16Tile& B, int64_t n0, int64_t k0, Bf16Stage& st) {
+  act_load(ActTile{B.w, B.N, B.K, B.vec}, n0, k0, st.a);
+}
+
+__device__ __forceinline__ void w_store(char* lds, const Bf16Tile&, const Bf16Stage& st) { act_store(lds, st.a); }
+
 // ---------------------------------------------------------------- one output tile
 
 template <class T> struct StageOf;
 template <> struct StageOf<Fp8Tile> { using type = Fp8Stage; };
 template <> struct StageOf<Nvfp4Tile> { using type = Nvfp4Stage; };
+template <> struct StageOf<Bf16Tile> { using type = Bf16Stage; };
 
 // Expert e of a weight stack whose tile `b` addresses expert 0.
 __device__ __forceinline__ Fp8Tile expert_tile(const Fp8Tile& b, int64_t e) {
@@ -333,6 +351,17 @@ hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, cons
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   return launch(gemm_dense_kernel<Nvfp4Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16,
                 alpha);
+}
+
+hipError_t launch_bf16_tiled(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                             int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s) {
+  if (bf16_lds_supported(x, w, M, N, K))
+    return launch_bf16_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s);
+  const bool vec = bf16_wide(w, x, K);
+  const ActTile A{x, M, K, vec};
+  const Bf16Tile B{w, N, K, vec};
+  const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  return launch(gemm_dense_kernel<Bf16Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16, alpha);
 }
 
 hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,

@@ -243,6 +243,7 @@ struct ScaleDma {
 
 struct Fp8Args { const uint8_t* w; };
 struct Nvfp4Args { const uint8_t* packed; const uint8_t* scales; };
+struct Bf16Args { const uint16_t* w; };
 
 // fp8: 64 bytes per row per strip (4 chunks).  Step t, half h reads chunk
 // 2t + h (16 values) and feeds bytes 8e .. 8e + 7 to k-slice e.
@@ -349,6 +350,51 @@ struct Nvfp4Weight {
         b[e][j] = __builtin_bit_cast(v8bf, o);
       }
     }
+  }
+};
+
+// Dense bf16 weight (the control): 128 bytes per row per strip, the
+// activation strip's layout.  Step t, half h, k-slice e reads the chunk the
+// activation fragment of (t, h, e) reads, so both operands pair the same k;
+// the stored bits are the MFMA operand (no decode).
+template <int BN, int FN, int NW>
+struct Bf16Weight {
+  using Args = Bf16Args;
+  __device__ static Args expert(Args a, int64_t e, int64_t N, int64_t K) { return Args{a.w + e * N * K}; }
+  static constexpr int kBytes = BN * 128;
+  using Dma = StripDma<BN, 128, NW>;
+  static constexpr int kLoads = Dma::kInst;
+  static constexpr int kReads[2] = {2 * FN, 2 * FN};
+  static constexpr int kValu = 0;
+  __device__ static constexpr int a_chunk(int t, int h, int e) { return 2 * (2 * t + h) + e; }
+
+  Dma dma;
+  const char* w;
+  uint32_t foff[2][2];
+  u32x4 raw[2][FN];
+
+  __device__ __forceinline__ void init(Args a, int64_t n0, int64_t N, int64_t K, int col0, int r, int h) {
+    dma.init(n0, N, 2 * K);
+    w = reinterpret_cast<const char*>(a.w);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) foff[t][e] = uint32_t((col0 + r) * 128 + 16 * (a_chunk(t, h, e) ^ swz<8>(r)));
+  }
+  __device__ __forceinline__ void fetch(char* tile, int64_t strip) const { dma.fetch(tile, w + strip * 128); }
+  template <int T>
+  __device__ __forceinline__ void read(const char* tile) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) raw[e][j] = lds16(tile + foff[T][e] + j * 32 * 128);
+  }
+  template <int T>
+  __device__ __forceinline__ void decode(v8bf (&b)[2][FN]) const {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[e][j] = __builtin_bit_cast(v8bf, raw[e][j]);
   }
 };
 
@@ -1238,6 +1284,25 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   if (tiles(M, N, 128, 256) >= num_cus / 2)
     return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+}
+
+bool bf16_lds_supported(const void* x, const void* w, int64_t M, int64_t N, int64_t K) {
+  return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && M * K * 2 < (int64_t(1) << 32) &&
+         N * K * 2 < (int64_t(1) << 32);
+}
+
+hipError_t launch_bf16_gemm_lds(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s) {
+  const Bf16Args wa{w};
+  if (ws) {
+    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
+    if (sp > 1) return launch_wq_splitk<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, s);
+  }
+  // A 256 x 256 stage of both bf16 operands (64 KiB) leaves room for only two
+  // stages: the largest tile runs 256 x 128 with three.
+  if (tiles(M, N, 256, 128) >= num_cus)
+    return launch_wq<Bf16Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+  return launch_wq<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
 }
 
 namespace {

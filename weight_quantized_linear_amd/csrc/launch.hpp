@@ -82,6 +82,18 @@ hipError_t launch_fp8_w8a8_lds(const uint8_t* xq, const uint8_t* w, void* out, i
                                int64_t K, float alpha, int num_cus, hipStream_t s);
 
 // nvfp4.hip
+// Dense bf16 control (bf16_dense.hip, gemm_lds.hip, gemm_bf16.hip).
+bool bf16_wide(const void* w, const void* x, int64_t K);
+hipError_t launch_bf16_gemv(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                            int64_t K, float alpha, int num_cus, hipStream_t s);
+hipError_t launch_bf16_skinny(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                              int64_t K, float alpha, int num_cus, hipStream_t s);
+bool bf16_lds_supported(const void* x, const void* w, int64_t M, int64_t N, int64_t K);
+hipError_t launch_bf16_gemm_lds(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_bf16_tiled(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                             int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s);
+
 hipError_t launch_nvfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s);

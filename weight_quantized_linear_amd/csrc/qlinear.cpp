@@ -174,6 +174,43 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
       launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
 }
 
+int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                   float alpha, int path, void* stream) {
+  if (!w || !x || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!float_out_ok(out_dtype)) return QLINEAR_ERR_INVALID_ARG;
+  if (!aligned(w, 2) || !aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
+  const bool wide = bf16_wide(w, x, K);
+  if (path == QLINEAR_PATH_AUTO) {
+    if (M <= 4) path = QLINEAR_PATH_GEMV;
+    else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
+    else path = QLINEAR_PATH_TILED;
+  }
+  switch (path) {
+    case QLINEAR_PATH_GEMV:
+      if (M > 4) return QLINEAR_ERR_INVALID_ARG;
+      break;
+    case QLINEAR_PATH_SKINNY:
+      if (M > 16 || !wide) return QLINEAR_ERR_INVALID_ARG;
+      break;
+    case QLINEAR_PATH_TILED:
+      break;
+    default:
+      return QLINEAR_ERR_INVALID_ARG;
+  }
+  int num_cus = 0;
+  DeviceInfo* dev = nullptr;
+  if (int st = current_device(&num_cus, &dev)) return st;
+  auto s = static_cast<hipStream_t>(stream);
+  auto* wp = static_cast<const uint16_t*>(w);
+  auto* xp = static_cast<const uint16_t*>(x);
+  const int bf16 = out_dtype == QLINEAR_BF16;
+  if (path == QLINEAR_PATH_GEMV) return finish(launch_bf16_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  if (path == QLINEAR_PATH_SKINNY) return finish(launch_bf16_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
+  return finish(launch_bf16_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +366,16 @@ int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const 
   return finish(launch_int8_gemm(static_cast<const int8_t*>(a), static_cast<const int8_t*>(b), a_scale, b_scale,
                                  mode == 2 ? nullptr : static_cast<const uint16_t*>(bias), out, mode, M, N, K,
                                  num_cus, static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_bf16_gemm(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                      float alpha, void* stream) {
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
+}
+
+int qlinear_bf16_gemm_path(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                           float alpha, int path, void* stream) {
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream);
 }
 
 }  // extern "C"
