@@ -33,6 +33,8 @@ __all__ = [
     "bf16_ulp",
     "CheckResult",
     "clause2_budget",
+    "check_f32_tau",
+    "epilogue_tolerance",
 ]
 
 REL_TOL = 2e-3
@@ -68,11 +70,16 @@ def check_f32(gpu, ref, bound) -> CheckResult:
 
     NaN in the reference must be matched by NaN in the GPU output (weight NaN
     propagation); NaN anywhere else fails."""
+    return check_f32_tau(gpu, ref, fp_tolerance(bound), bound)
+
+
+def check_f32_tau(gpu, ref, tau, bound=None) -> CheckResult:
+    """``check_f32`` with the per-element tolerance given: |gpu - ref| <= tau."""
     g = np.asarray(gpu, dtype=np.float32).astype(np.float64)
     r = np.asarray(ref, dtype=np.float64)
-    b = np.asarray(bound, dtype=np.float64)
+    tol = np.broadcast_to(np.asarray(tau, dtype=np.float64), r.shape)
+    b = np.asarray(bound, dtype=np.float64) if bound is not None else tol
     err = np.abs(g - r)
-    tol = fp_tolerance(b)
     both_nan = np.isnan(g) & np.isnan(r)
     bad = ~((err <= tol) | both_nan)
     with np.errstate(invalid="ignore", divide="ignore"):
@@ -140,3 +147,24 @@ def clause2_budget(ref, share: float = 1e-3) -> int:
     of ``fp_tolerance``) passes a larger ``share``.  Returns that share of the
     outputs, plus 2."""
     return int(share * np.asarray(ref).size) + 2
+
+
+# Largest slope of each activation (its Lipschitz constant): SiLU's derivative
+# peaks at about 1.0998, the tanh-form GELU's at about 1.1289.
+ACT_LIPSCHITZ = {"none": 1.0, "relu": 1.0, "silu": 1.1, "gelu_tanh": 1.13}
+
+
+def epilogue_tolerance(bound, parts, act: str) -> np.ndarray:
+    """Tolerance of a fused-epilogue output (``oracle.ref.apply_epilogue``).
+
+    The matmul's own error, at most ``fp_tolerance(B)``, is multiplied by the
+    scales; the scale products and the bias addition each round once in
+    float32 (u = 2^-24 relative); the activation moves an input error by at
+    most its Lipschitz constant and, evaluated with float32 exp / tanh, adds a
+    few ulps of its input and output magnitude (8 u); the residual addition
+    and the final float32 value round once more."""
+    u = 2.0 ** -24
+    lip = ACT_LIPSCHITZ[act]
+    t = parts["scale"] * fp_tolerance(bound) + 4 * u * (np.abs(parts["scaled"]) + np.abs(parts["pre"]))
+    return lip * t + 8 * u * (np.abs(parts["post"]) + np.abs(parts["pre"])) + \
+        2 * u * (parts["residual"] + np.abs(parts["out"]))

@@ -39,6 +39,9 @@ __all__ = [
     "fp8_quantize_act",
     "fp8_w8a8_linear",
     "bf16_linear",
+    "ACTIVATIONS",
+    "activation",
+    "apply_epilogue",
 ]
 
 _ROW_CHUNK = 8192  # weight rows decoded to float64 at a time (bounds memory on the widest layer)
@@ -310,3 +313,65 @@ def bf16_linear(w_bits, x_bits, alpha: float = 1.0):
     if x.shape[1] != w.shape[1]:
         raise ValueError("K mismatch")
     return _linear(lambda lo, hi: bf16_bits_to_f64(w[lo:hi]), w.shape[0], x, alpha)
+
+
+ACTIVATIONS = ("none", "relu", "silu", "gelu_tanh")
+
+
+def activation(v, name: str) -> np.ndarray:
+    """The epilogue activations by their definitions, in float64: ReLU
+    max(v, 0); SiLU v / (1 + e^-v); GELU in its tanh form
+    0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))."""
+    v = np.asarray(v, dtype=np.float64)
+    if name == "none":
+        return v.copy()
+    if name == "relu":
+        return np.maximum(v, 0.0)
+    if name == "silu":
+        with np.errstate(over="ignore"):
+            return v / (1.0 + np.exp(-v))
+    if name == "gelu_tanh":
+        return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+    raise ValueError(f"unknown activation {name!r}")
+
+
+def apply_epilogue(value, row_scale=None, col_scale=None, bias_bits=None, act: str = "none", residual=None):
+    """Fused epilogue on an [M, N] float64 result whose alpha is applied.
+
+    Matmul2dFp8 page, "Parameters": elementwise_lambda_fn is an optional
+    element-wise function of each output element's (row, col) coordinates and
+    value, fused into the store.  Reading: a fixed menu of such steps, in this
+    order -- times row_scale[m], times col_scale[n], plus bias[n] (bfloat16
+    bits), the activation, plus residual[m, n] -- following the int8_matmul
+    page's epilogue, which scales first and adds the per-column bias after.
+    Missing steps (None, "none") are skipped.  ``residual`` holds values
+    (float64-convertible), already decoded.
+
+    Returns (out, parts): ``parts`` carries the intermediate magnitudes the
+    acceptance rule of ``oracle.compare.epilogue_tolerance`` needs: "scale"
+    |row_scale[m] col_scale[n]|, "scaled" the value after the scales, "pre" the
+    activation's input, "post" its output, "residual" |residual| and "out".
+    """
+    v = np.asarray(value, dtype=np.float64)
+    m, n = v.shape
+    scale = np.ones((m, n))
+    if row_scale is not None:
+        rs = np.asarray(row_scale, dtype=np.float64).reshape(m, 1)
+        v = v * rs
+        scale = scale * np.abs(rs)
+    if col_scale is not None:
+        cs = np.asarray(col_scale, dtype=np.float64).reshape(1, n)
+        v = v * cs
+        scale = scale * np.abs(cs)
+    scaled = v
+    if bias_bits is not None:
+        v = v + bf16_bits_to_f64(np.asarray(bias_bits, dtype=np.uint16)).reshape(1, n)
+    pre = v
+    post = activation(pre, act)
+    out = post
+    res = np.zeros((m, n))
+    if residual is not None:
+        res = np.asarray(residual, dtype=np.float64).reshape(m, n)
+        out = post + res
+    parts = {"scale": scale, "scaled": scaled, "pre": pre, "post": post, "residual": np.abs(res), "out": out}
+    return out, parts

@@ -399,3 +399,45 @@ def test_bf16_linear_equals_fp8_linear_on_widened_weight():
     a, ba = R.bf16_linear(wb, x, 1.5)
     b, bb = R.fp8_linear(w, x, 1.5)
     assert np.array_equal(a, b) and np.array_equal(ba, bb)
+
+
+# ------------------------------------------------------------------ fused epilogue
+
+def test_epilogue_golden():
+    g = _load("epilogue_example.json")
+    bias = np.array([int(b, 16) for b in g["bias_bits"]], dtype=np.uint16)
+    assert np.array_equal(F.bf16_bits_to_f64(bias), np.array(g["bias_values"]))
+    out, parts = R.apply_epilogue(np.array(g["value"]), g["row_scale"], g["col_scale"], bias, "relu",
+                                  np.array(g["residual"]))
+    assert np.array_equal(parts["scaled"], np.array(g["after_scales"]))
+    assert np.array_equal(parts["pre"], np.array(g["after_bias"]))
+    assert np.array_equal(parts["post"], np.array(g["after_relu"]))
+    assert np.array_equal(out, np.array(g["out"]))
+
+
+def test_epilogue_without_steps_is_identity():
+    v = np.random.default_rng(90).standard_normal((3, 5))
+    out, parts = R.apply_epilogue(v)
+    assert np.array_equal(out, v) and np.array_equal(parts["scale"], np.ones((3, 5)))
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("relu", lambda t: torch.relu(t)),
+    ("silu", lambda t: torch.nn.functional.silu(t)),
+    ("gelu_tanh", lambda t: torch.nn.functional.gelu(t, approximate="tanh")),
+])
+def test_activations_match_torch(name, fn):
+    v = np.concatenate([np.linspace(-12, 12, 2401), [-80.0, -30.0, 0.0, 30.0, 80.0]])
+    want = fn(torch.from_numpy(v)).numpy()
+    got = R.activation(v, name)
+    # absolute in |v|: where the factor 1 + tanh(.) cancels (large negative v)
+    # the two float64 evaluations agree only to a few ulps of v, not of the result
+    assert np.all(np.abs(got - want) <= 1e-14 * (1 + np.abs(v)))
+
+
+@pytest.mark.parametrize("name", ["silu", "gelu_tanh"])
+def test_activation_odd_part_is_identity(name):
+    """f(v) - f(-v) = v for SiLU and the tanh-form GELU (both are v times a
+    sigmoid-shaped factor g with g(v) + g(-v) = 1): fails on a wrong sign."""
+    v = np.linspace(-6, 6, 241)
+    assert np.allclose(R.activation(v, name) - R.activation(-v, name), v, rtol=0, atol=1e-12)
