@@ -121,7 +121,7 @@ def _grouped(linear_of_expert, e_count: int, n: int, x_bits, a_offsets, expert_i
     return ref, bound, written
 
 
-def fp8_grouped(w_codes, x_bits, a_offsets, expert_ids):
+def fp8_grouped(w_codes, x_bits, a_offsets, expert_ids, expert_scale=None):
     """Grouped (MoE) W8A16 linear.
 
     Matmul2dFp8 page, ``run_grouped``: group z covers the activation rows
@@ -136,27 +136,34 @@ def fp8_grouped(w_codes, x_bits, a_offsets, expert_ids):
     clipped to the T activation rows.
 
     w_codes: uint8 [E, N, K]; x_bits: uint16 [T, K]; a_offsets: [G+1];
-    expert_ids: [G].  Returns (ref [T, N], bound [T, N], written [T]).
+    expert_ids: [G].  ``expert_scale`` ([E] or None): the per-expert
+    weight_scale that the page leaves to the graph as a post-matmul multiply,
+    folded here as the alpha of the expert's rows (fp8_linear's scale fold).
+    Returns (ref [T, N], bound [T, N], written [T]).
     """
     w = np.asarray(w_codes, dtype=np.uint8)
     e_count, n, _ = w.shape
-    return _grouped(lambda e, xr: fp8_linear(w[e], xr), e_count, n, x_bits, a_offsets, expert_ids)
+    sc = (lambda e: 1.0) if expert_scale is None else (lambda e: float(np.float32(expert_scale[e])))
+    return _grouped(lambda e, xr: fp8_linear(w[e], xr, sc(e)), e_count, n, x_bits, a_offsets, expert_ids)
 
 
-def nvfp4_grouped(w_packed, w_scale_codes, x_bits, a_offsets, expert_ids):
+def nvfp4_grouped(w_packed, w_scale_codes, x_bits, a_offsets, expert_ids, expert_scale=None):
     """Grouped (MoE) W4A16 NVFP4 linear: the ``run_grouped`` addressing of the
     Matmul2dFp8 page applied to the fp4_matmul page's weight format.
 
     Same group readings as fp8_grouped; expert e's weight is the NVFP4 pair
     (w_packed[e] uint8 [N, K/2], w_scale_codes[e] E4M3 [N, K/16]).  The result
     is raw: each expert's per-tensor global scale (weight_scale_2) is left to
-    the caller, as the per-expert FP8 weight_scale is for fp8_grouped.
+    the caller, as the per-expert FP8 weight_scale is for fp8_grouped, unless
+    ``expert_scale`` ([E]) is given: then it is expert e's alpha.
     Returns (ref [T, N], bound [T, N], written [T]).
     """
     p = np.asarray(w_packed, dtype=np.uint8)
     sc = np.asarray(w_scale_codes, dtype=np.uint8)
     e_count, n, _ = p.shape
-    return _grouped(lambda e, xr: nvfp4_linear(p[e], sc[e], xr), e_count, n, x_bits, a_offsets, expert_ids)
+    es = (lambda e: 1.0) if expert_scale is None else (lambda e: float(np.float32(expert_scale[e])))
+    return _grouped(lambda e, xr: nvfp4_linear(p[e], sc[e], xr, es(e)), e_count, n, x_bits, a_offsets,
+                    expert_ids)
 
 
 def nvfp4_dequant(w_packed, w_scale_codes) -> np.ndarray:

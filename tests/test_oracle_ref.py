@@ -441,3 +441,23 @@ def test_activation_odd_part_is_identity(name):
     sigmoid-shaped factor g with g(v) + g(-v) = 1): fails on a wrong sign."""
     v = np.linspace(-6, 6, 241)
     assert np.allclose(R.activation(v, name) - R.activation(-v, name), v, rtol=0, atol=1e-12)
+
+
+def test_grouped_expert_scale_scales_each_experts_rows():
+    """The per-expert scale multiplies exactly the rows of that expert's
+    groups (inactive groups stay zero, uncovered rows untouched)."""
+    r = np.random.default_rng(91)
+    w = r.integers(0, 0x7E, size=(3, 6, 40), dtype=np.uint8)
+    x = synth.bf16_activation((91,), 12, 40)
+    offs = np.array([0, 3, 7, 7, 10])
+    ids = np.array([2, -1, 0, 1])
+    scale = np.array([0.5, 3.0, -2.0], np.float32)
+    raw, braw, wr = R.fp8_grouped(w, x, offs, ids)
+    got, bgot, wg = R.fp8_grouped(w, x, offs, ids, scale)
+    assert np.array_equal(wr, wg)
+    per_row = np.full(12, np.nan)
+    per_row[0:3], per_row[3:7], per_row[7:10] = -2.0, 1.0, 3.0   # experts 2, inactive, (empty), 1
+    rows = wr
+    assert np.array_equal(got[rows], raw[rows] * per_row[rows, None])
+    assert np.array_equal(bgot[rows], braw[rows] * np.abs(per_row[rows, None]))
+    assert np.all(got[3:7] == 0)
