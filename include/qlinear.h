@@ -71,6 +71,45 @@ typedef enum qlinear_path {
   QLINEAR_PATH_TILED = 3    /* LDS-tiled matrix-core GEMM, any M                     */
 } qlinear_path;
 
+/* Activation of a fused epilogue. */
+typedef enum qlinear_activation {
+  QLINEAR_ACT_NONE = 0,
+  QLINEAR_ACT_RELU = 1,       /* max(v, 0)                                           */
+  QLINEAR_ACT_SILU = 2,       /* v / (1 + exp(-v))                                   */
+  QLINEAR_ACT_GELU_TANH = 3   /* 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))     */
+} qlinear_activation;
+
+/*
+ * Fused epilogue of the *_epilogue calls: page "Matmul2dFp8" ("Parameters",
+ * elementwise_lambda_fn: an optional element-wise function of the output
+ * element's (row, col) coordinates and value, fused into the store).  A C
+ * ABI cannot take a lambda, so this is a fixed menu of element-wise steps,
+ * applied in float32 to output element (m, n) after alpha and before the
+ * single rounding to the output type:
+ *     v = alpha * acc
+ *     v = v * row_scale[m]            (row_scale: float32 [M], or NULL)
+ *     v = v * col_scale[n]            (col_scale: float32 [N], or NULL)
+ *     v = v + bias[n]                 (bias: bfloat16 [N], or NULL)
+ *     v = activation(v)
+ *     v = v + residual[m * residual_ld + n]   (residual: [M, residual_ld] of
+ *                                      residual_dtype F32 or BF16, or NULL)
+ * The residual may be the output buffer itself (same type, residual_ld = N):
+ * each element is read before it is written, by the same thread.  All
+ * pointers are device pointers, read only, owned by the caller.  An invalid
+ * activation, a residual_ld below N or a misaligned pointer gives
+ * QLINEAR_ERR_INVALID_ARG.  A NULL descriptor (or one with every pointer
+ * NULL and no activation) is the plain call.
+ */
+typedef struct qlinear_epilogue {
+  const float* row_scale;
+  const float* col_scale;
+  const void* bias;
+  const void* residual;
+  int64_t residual_ld;
+  int residual_dtype;
+  int activation;
+} qlinear_epilogue;
+
 /* Version of this ABI (QLINEAR_ABI_VERSION of the build). */
 int qlinear_abi_version(void);
 
@@ -268,6 +307,46 @@ int qlinear_bf16_gemm(const void* w, const void* x, void* out, int out_dtype,
 int qlinear_bf16_gemm_path(const void* w, const void* x, void* out, int out_dtype,
                            int64_t M, int64_t N, int64_t K, float alpha, int path,
                            void* stream);
+
+/*
+ * qlinear_fp8_gemm / qlinear_nvfp4_gemm / qlinear_bf16_gemm with a fused
+ * epilogue (qlinear_epilogue; NULL = the plain call).  Same operands, kernel
+ * choice, workspace rule and errors as the plain calls; the _path variant
+ * forces the kernel family as qlinear_fp8_gemm_path does.
+ */
+int qlinear_fp8_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype,
+                              int64_t M, int64_t N, int64_t K, float alpha,
+                              const qlinear_epilogue* epilogue, void* stream);
+int qlinear_fp8_gemm_epilogue_path(const void* w, const void* x, void* out, int out_dtype,
+                                   int64_t M, int64_t N, int64_t K, float alpha,
+                                   const qlinear_epilogue* epilogue, int path, void* stream);
+int qlinear_nvfp4_gemm_epilogue(const void* w_packed, const void* w_scale, const void* x,
+                                void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                float alpha, const qlinear_epilogue* epilogue, void* stream);
+int qlinear_bf16_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype,
+                               int64_t M, int64_t N, int64_t K, float alpha,
+                               const qlinear_epilogue* epilogue, void* stream);
+
+/*
+ * Grouped matmuls with the per-expert weight scale folded in: page
+ * "Matmul2dFp8" (run_grouped produces the raw product; the graph then
+ * multiplies each expert's rows by that expert's weight_scale).  Rows of
+ * group z are multiplied by expert_scale[expert_ids[z]] (float32
+ * [num_experts], device memory; NULL = raw) in float32 before the single
+ * output rounding; inactive groups still write zeros.  Everything else is
+ * exactly qlinear_fp8_grouped_gemm / qlinear_nvfp4_grouped_gemm.
+ */
+int qlinear_fp8_grouped_gemm_scaled(const void* w, const void* x, const uint32_t* a_offsets,
+                                    const int32_t* expert_ids, const float* expert_scale,
+                                    void* out, int out_dtype, int64_t num_groups,
+                                    int64_t max_tokens_per_group, int64_t num_experts,
+                                    int64_t T, int64_t N, int64_t K, void* stream);
+int qlinear_nvfp4_grouped_gemm_scaled(const void* w_packed, const void* w_scale, const void* x,
+                                      const uint32_t* a_offsets, const int32_t* expert_ids,
+                                      const float* expert_scale, void* out, int out_dtype,
+                                      int64_t num_groups, int64_t max_tokens_per_group,
+                                      int64_t num_experts, int64_t T, int64_t N, int64_t K,
+                                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -46,6 +46,16 @@ PATHS = {"auto": 0, "gemv": 1, "skinny": 2, "tiled": 3}
 
 _p, _i, _i64, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
 
+
+class EpilogueDesc(ctypes.Structure):
+    """``qlinear_epilogue``: the fused element-wise steps of the *_epilogue calls."""
+    _fields_ = [("row_scale", _p), ("col_scale", _p), ("bias", _p), ("residual", _p),
+                ("residual_ld", _i64), ("residual_dtype", _i), ("activation", _i)]
+
+
+ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2, "gelu_tanh": 3}
+_EP = ctypes.POINTER(EpilogueDesc)
+
 # name -> argument types (all return int status except where noted)
 EXPORTED = {
     "qlinear_abi_version": [],
@@ -65,6 +75,12 @@ EXPORTED = {
     "qlinear_nvfp4_dequant": [_p, _p, _p, _i, _i64, _i64, _p],
     "qlinear_int8_quantize_act": [_p, _p, _p, _i64, _i64, _p],
     "qlinear_int8_gemm": [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _p],
+    "qlinear_fp8_gemm_epilogue": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _p],
+    "qlinear_fp8_gemm_epilogue_path": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p],
+    "qlinear_nvfp4_gemm_epilogue": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _p],
+    "qlinear_bf16_gemm_epilogue": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _p],
+    "qlinear_fp8_grouped_gemm_scaled": [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
+    "qlinear_nvfp4_grouped_gemm_scaled": [_p, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
 }
 
 
@@ -136,9 +152,43 @@ def _out(out, shape, dtype, device):
     return out
 
 
+def _epilogue(m: int, n: int, row_scale, col_scale, bias, residual, activation: str):
+    """The ``qlinear_epilogue`` of the given tensors (None when nothing is fused)."""
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    if row_scale is None and col_scale is None and bias is None and residual is None and activation == "none":
+        return None
+    d = EpilogueDesc(None, None, None, None, 0, F32, ACTIVATIONS[activation])
+    for t, name, size, dt in ((row_scale, "row_scale", m, torch.float32), (col_scale, "col_scale", n, torch.float32),
+                              (bias, "bias", n, torch.bfloat16)):
+        if t is None:
+            continue
+        _require(t, name)
+        if t.dtype != dt or t.numel() != size:
+            raise ValueError(f"{name} must be {dt} with {size} elements")
+        setattr(d, name, t.data_ptr())
+    if residual is not None:
+        if not residual.is_cuda or residual.dim() != 2 or residual.shape[0] != m or residual.shape[1] < n \
+                or residual.stride(1) != 1 or residual.dtype not in _OUT_CODES:
+            raise ValueError("residual must be a float32/bfloat16 device tensor [M, >= N] with unit column stride")
+        d.residual = residual.data_ptr()
+        d.residual_ld = residual.stride(0) if m > 1 else residual.shape[1]
+        d.residual_dtype = _OUT_CODES[residual.dtype]
+    return d
+
+
+def _epi_ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
 def fp8_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
-             out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto") -> torch.Tensor:
-    """out[M, N] = alpha * x[M, K] @ dec_e4m3(w[N, K])^T (``qlinear_fp8_gemm``)."""
+             out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto",
+             row_scale: torch.Tensor | None = None, col_scale: torch.Tensor | None = None,
+             bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+             activation: str = "none") -> torch.Tensor:
+    """out[M, N] = alpha * x[M, K] @ dec_e4m3(w[N, K])^T (``qlinear_fp8_gemm``); with
+    any of row_scale / col_scale / bias / residual / activation, the fused epilogue
+    of ``qlinear_fp8_gemm_epilogue_path``."""
     w = _as_u8(w, "w")
     x = _as_bf16(x, "x")
     _require(w, "w")
@@ -148,6 +198,12 @@ def fp8_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     m, k = x.shape
     n = w.shape[0]
     out = _out(out, (m, n), out_dtype, x.device)
+    d = _epilogue(m, n, row_scale, col_scale, bias, residual, activation)
+    if d is not None:
+        st = lib.qlinear_fp8_gemm_epilogue_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
+                                                float(alpha), _epi_ref(d), PATHS[path], _stream(x))
+        _check(st, "qlinear_fp8_gemm_epilogue")
+        return out
     st = lib.qlinear_fp8_gemm_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
                                    float(alpha), PATHS[path], _stream(x))
     _check(st, "qlinear_fp8_gemm")
@@ -155,8 +211,12 @@ def fp8_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
 
 
 def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
-              out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto") -> torch.Tensor:
-    """Dense bf16 control: out[M, N] = alpha * x[M, K] @ w[N, K]^T (``qlinear_bf16_gemm``)."""
+              out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto",
+              row_scale: torch.Tensor | None = None, col_scale: torch.Tensor | None = None,
+              bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+              activation: str = "none") -> torch.Tensor:
+    """Dense bf16 control: out[M, N] = alpha * x[M, K] @ w[N, K]^T (``qlinear_bf16_gemm``);
+    with an epilogue argument, ``qlinear_bf16_gemm_epilogue`` (automatic kernel choice)."""
     w = _as_bf16(w, "w")
     x = _as_bf16(x, "x")
     _require(w, "w")
@@ -166,6 +226,14 @@ def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     m, k = x.shape
     n = w.shape[0]
     out = _out(out, (m, n), out_dtype, x.device)
+    d = _epilogue(m, n, row_scale, col_scale, bias, residual, activation)
+    if d is not None:
+        if path != "auto":
+            raise ValueError("the bf16 epilogue call chooses its kernel itself (path='auto')")
+        st = lib.qlinear_bf16_gemm_epilogue(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
+                                            float(alpha), _epi_ref(d), _stream(x))
+        _check(st, "qlinear_bf16_gemm_epilogue")
+        return out
     st = lib.qlinear_bf16_gemm_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
                                     float(alpha), PATHS[path], _stream(x))
     _check(st, "qlinear_bf16_gemm")
@@ -201,12 +269,23 @@ def fp8_materialize(w: torch.Tensor, out_dtype: torch.dtype = torch.float32,
     return out
 
 
+def _expert_scale(expert_scale, e: int):
+    if expert_scale is None:
+        return None
+    _require(expert_scale, "expert_scale")
+    if expert_scale.dtype != torch.float32 or expert_scale.numel() != e:
+        raise ValueError(f"expert_scale must be float32 with {e} elements")
+    return _ptr(expert_scale)
+
+
 def fp8_grouped_gemm(w: torch.Tensor, x: torch.Tensor, a_offsets: torch.Tensor, expert_ids: torch.Tensor,
                      out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
-                     max_tokens_per_group: int | None = None) -> torch.Tensor:
-    """Grouped MoE W8A16 (``qlinear_fp8_grouped_gemm``): rows a_offsets[z] ..
-    a_offsets[z+1]-1 of x times dec(w[expert_ids[z]])^T.  Rows outside every
-    group keep whatever ``out`` held (a new ``out`` starts uninitialised)."""
+                     max_tokens_per_group: int | None = None,
+                     expert_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped MoE W8A16 (``qlinear_fp8_grouped_gemm_scaled``): rows a_offsets[z] ..
+    a_offsets[z+1]-1 of x times dec(w[expert_ids[z]])^T, times expert_scale[expert_ids[z]]
+    when given (raw otherwise).  Rows outside every group keep whatever ``out`` held
+    (a new ``out`` starts uninitialised)."""
     w = _as_u8(w, "w")
     x = _as_bf16(x, "x")
     for t, name in ((w, "w"), (x, "x"), (a_offsets, "a_offsets"), (expert_ids, "expert_ids")):
@@ -223,9 +302,10 @@ def fp8_grouped_gemm(w: torch.Tensor, x: torch.Tensor, a_offsets: torch.Tensor, 
     if max_tokens_per_group is None:
         max_tokens_per_group = t
     out = _out(out, (t, n), out_dtype, x.device)
-    st = lib.qlinear_fp8_grouped_gemm(_ptr(w), _ptr(x), _ptr(a_offsets), _ptr(expert_ids), _ptr(out),
-                                      _OUT_CODES[out_dtype], g, int(max_tokens_per_group), e, t, n, k, _stream(x))
-    _check(st, "qlinear_fp8_grouped_gemm")
+    st = lib.qlinear_fp8_grouped_gemm_scaled(_ptr(w), _ptr(x), _ptr(a_offsets), _ptr(expert_ids),
+                                             _expert_scale(expert_scale, e), _ptr(out), _OUT_CODES[out_dtype], g,
+                                             int(max_tokens_per_group), e, t, n, k, _stream(x))
+    _check(st, "qlinear_fp8_grouped_gemm_scaled")
     return out
 
 
@@ -265,11 +345,13 @@ def fp8_w8a8_gemm(xq: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = 
 
 def nvfp4_grouped_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, a_offsets: torch.Tensor,
                        expert_ids: torch.Tensor, out: torch.Tensor | None = None,
-                       out_dtype: torch.dtype = torch.bfloat16, max_tokens_per_group: int | None = None) -> torch.Tensor:
-    """Grouped MoE W4A16 NVFP4 (``qlinear_nvfp4_grouped_gemm``): rows a_offsets[z] ..
+                       out_dtype: torch.dtype = torch.bfloat16, max_tokens_per_group: int | None = None,
+                       expert_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped MoE W4A16 NVFP4 (``qlinear_nvfp4_grouped_gemm_scaled``): rows a_offsets[z] ..
     a_offsets[z+1]-1 of x times D_e^T, e = expert_ids[z], D_e the expert's NVFP4
-    weight (w_packed [E, N, K/2], w_scale [E, N, K/16]); raw output.  Rows outside
-    every group keep whatever ``out`` held (a new ``out`` starts uninitialised)."""
+    weight (w_packed [E, N, K/2], w_scale [E, N, K/16]), times expert_scale[e] when
+    given (raw otherwise).  Rows outside every group keep whatever ``out`` held (a
+    new ``out`` starts uninitialised)."""
     p = _as_u8(w_packed, "w_packed")
     sc = _as_u8(w_scale, "w_scale")
     x = _as_bf16(x, "x")
@@ -289,15 +371,20 @@ def nvfp4_grouped_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.T
     if max_tokens_per_group is None:
         max_tokens_per_group = t
     out = _out(out, (t, n), out_dtype, x.device)
-    st = lib.qlinear_nvfp4_grouped_gemm(_ptr(p), _ptr(sc), _ptr(x), _ptr(a_offsets), _ptr(expert_ids), _ptr(out),
-                                        _OUT_CODES[out_dtype], g, int(max_tokens_per_group), e, t, n, k, _stream(x))
-    _check(st, "qlinear_nvfp4_grouped_gemm")
+    st = lib.qlinear_nvfp4_grouped_gemm_scaled(_ptr(p), _ptr(sc), _ptr(x), _ptr(a_offsets), _ptr(expert_ids),
+                                               _expert_scale(expert_scale, e), _ptr(out), _OUT_CODES[out_dtype], g,
+                                               int(max_tokens_per_group), e, t, n, k, _stream(x))
+    _check(st, "qlinear_nvfp4_grouped_gemm_scaled")
     return out
 
 
 def nvfp4_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
-               out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto") -> torch.Tensor:
-    """out[M, N] = alpha * x[M, K] @ D^T, D the NVFP4 weight (``qlinear_nvfp4_gemm``)."""
+               out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto",
+               row_scale: torch.Tensor | None = None, col_scale: torch.Tensor | None = None,
+               bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+               activation: str = "none") -> torch.Tensor:
+    """out[M, N] = alpha * x[M, K] @ D^T, D the NVFP4 weight (``qlinear_nvfp4_gemm``); with
+    an epilogue argument, ``qlinear_nvfp4_gemm_epilogue`` (automatic kernel choice)."""
     p = _as_u8(w_packed, "w_packed")
     sc = _as_u8(w_scale, "w_scale")
     x = _as_bf16(x, "x")
@@ -308,6 +395,14 @@ def nvfp4_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, o
     if tuple(p.shape) != (n, k // 2) or tuple(sc.shape) != (n, k // 16):
         raise ValueError("w_packed must be [N, K/2] and w_scale [N, K/16]")
     out = _out(out, (m, n), out_dtype, x.device)
+    d = _epilogue(m, n, row_scale, col_scale, bias, residual, activation)
+    if d is not None:
+        if path != "auto":
+            raise ValueError("the NVFP4 epilogue call chooses its kernel itself (path='auto')")
+        st = lib.qlinear_nvfp4_gemm_epilogue(_ptr(p), _ptr(sc), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
+                                             float(alpha), _epi_ref(d), _stream(x))
+        _check(st, "qlinear_nvfp4_gemm_epilogue")
+        return out
     st = lib.qlinear_nvfp4_gemm_path(_ptr(p), _ptr(sc), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
                                      float(alpha), PATHS[path], _stream(x))
     _check(st, "qlinear_nvfp4_gemm")

@@ -31,7 +31,7 @@ namespace {
 template <int M, int ROWS, int U>
 __global__ __launch_bounds__(256) void bf16_gemv_wide_kernel(const uint16_t* __restrict__ w,
                                                              const uint16_t* __restrict__ x, void* __restrict__ out,
-                                                             int out_bf16, int64_t N, int64_t K, float alpha) {
+                                                             int out_bf16, int64_t N, int64_t K, float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t row0 = wave * ROWS;
@@ -80,14 +80,14 @@ __global__ __launch_bounds__(256) void bf16_gemv_wide_kernel(const uint16_t* __r
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float s = wave_sum(acc[m][r]);
-      if (lane == 0 && row0 + r < N) store_out(out, m * N + row0 + r, s, alpha, out_bf16);
+      if (lane == 0 && row0 + r < N) store_epi(out, m, row0 + r, N, s, alpha, out_bf16, epi);
     }
 }
 
 template <int M, int ROWS>
 __global__ __launch_bounds__(256) void bf16_gemv_any_kernel(const uint16_t* __restrict__ w,
                                                             const uint16_t* __restrict__ x, void* __restrict__ out,
-                                                            int out_bf16, int64_t N, int64_t K, float alpha) {
+                                                            int out_bf16, int64_t N, int64_t K, float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t row0 = wave * ROWS;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void bf16_gemv_any_kernel(const uint16_t* __re
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float s = wave_sum(acc[m][r]);
-      if (lane == 0 && row0 + r < N) store_out(out, m * N + row0 + r, s, alpha, out_bf16);
+      if (lane == 0 && row0 + r < N) store_epi(out, m, row0 + r, N, s, alpha, out_bf16, epi);
     }
 }
 
@@ -140,7 +140,7 @@ template <int G, int U, int NWV>
 __global__ __launch_bounds__(NWV * 64) void bf16_skinny_kernel(const uint16_t* __restrict__ w,
                                                                const uint16_t* __restrict__ x,
                                                                void* __restrict__ out, int out_bf16, int M, int64_t N,
-                                                               int64_t K, float alpha) {
+                                                               int64_t K, float alpha, Epilogue epi) {
   static_assert(NWV >= 4, "the final sum uses four waves");
   __shared__ v4f red[NWV][G][kWave];
 
@@ -199,41 +199,41 @@ __global__ __launch_bounds__(NWV * 64) void bf16_skinny_kernel(const uint16_t* _
 #pragma unroll
     for (int q = 0; q < NWV; ++q) s += red[q][g][lane][wid];
     const int64_t n = n0 + 16 * g + r16;
-    if (m < M && n < N) store_out(out, int64_t(m) * N + n, s, alpha, out_bf16);
+    if (m < M && n < N) store_epi(out, m, n, N, s, alpha, out_bf16, epi);
   }
 }
 
 template <int M, int ROWS>
 hipError_t launch_gemv_rows(bool wide, const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t N,
-                            int64_t K, float alpha, hipStream_t s) {
+                            int64_t K, float alpha, const Epilogue& epi, hipStream_t s) {
   constexpr int kThreads = 256;
   constexpr int kRowsPerBlock = ROWS * (kThreads / kWave);
   const int64_t blocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
   if (!wide)
     return launch(bf16_gemv_any_kernel<M, ROWS>, dim3(blocks), dim3(kThreads), 0, s, w, x, out, out_bf16, N, K,
-                  alpha);
+                  alpha, epi);
   // Rows of 512 or more chunks keep four chunks per lane in flight at M = 1.
   const int64_t per_lane = ((K >> 3) + kWave - 1) / kWave;
   if (M > 1 || per_lane <= 2)
     return launch(bf16_gemv_wide_kernel<M, ROWS, 2>, dim3(blocks), dim3(kThreads), 0, s, w, x, out, out_bf16, N, K,
-                  alpha);
+                  alpha, epi);
   return launch(bf16_gemv_wide_kernel<M, ROWS, 4>, dim3(blocks), dim3(kThreads), 0, s, w, x, out, out_bf16, N, K,
-                alpha);
+                alpha, epi);
 }
 
 template <int M>
 hipError_t launch_gemv_m(bool wide, const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t N,
-                         int64_t K, float alpha, int num_cus, hipStream_t s) {
-  if (N >= int64_t(num_cus) * 16) return launch_gemv_rows<M, 2>(wide, w, x, out, out_bf16, N, K, alpha, s);
-  return launch_gemv_rows<M, 1>(wide, w, x, out, out_bf16, N, K, alpha, s);
+                         int64_t K, float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
+  if (N >= int64_t(num_cus) * 16) return launch_gemv_rows<M, 2>(wide, w, x, out, out_bf16, N, K, alpha, epi, s);
+  return launch_gemv_rows<M, 1>(wide, w, x, out, out_bf16, N, K, alpha, epi, s);
 }
 
 template <int G, int U, int NWV>
 hipError_t launch_skinny(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                         int64_t K, float alpha, hipStream_t s) {
+                         int64_t K, float alpha, const Epilogue& epi, hipStream_t s) {
   const int64_t blocks = (N + 16 * G - 1) / (16 * G);
   return launch(bf16_skinny_kernel<G, U, NWV>, dim3(blocks), dim3(NWV * kWave), 0, s, w, x, out, out_bf16, int(M),
-                N, K, alpha);
+                N, K, alpha, epi);
 }
 
 }  // namespace
@@ -243,25 +243,25 @@ bool bf16_wide(const void* w, const void* x, int64_t K) {
 }
 
 hipError_t launch_bf16_gemv(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                            int64_t K, float alpha, int num_cus, hipStream_t s) {
+                            int64_t K, float alpha, int num_cus, hipStream_t s, const Epilogue& epi) {
   const bool wide = bf16_wide(w, x, K);
   switch (M) {
-    case 1: return launch_gemv_m<1>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 2: return launch_gemv_m<2>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 3: return launch_gemv_m<3>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 4: return launch_gemv_m<4>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
+    case 1: return launch_gemv_m<1>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 2: return launch_gemv_m<2>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 3: return launch_gemv_m<3>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 4: return launch_gemv_m<4>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_bf16_skinny(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                              int64_t K, float alpha, int num_cus, hipStream_t s) {
+                              int64_t K, float alpha, int num_cus, hipStream_t s, const Epilogue& epi) {
   if (M < 1 || M > 16 || !bf16_wide(w, x, K)) return hipErrorInvalidValue;
   // The FP8 skinny kernel's choice: four 16-column groups per block from
   // 8192 output features, else one group with more K steps in flight.
   (void)num_cus;
-  if (N >= 8192) return launch_skinny<4, 2, 16>(w, x, out, out_bf16, M, N, K, alpha, s);
-  return launch_skinny<1, 4, 16>(w, x, out, out_bf16, M, N, K, alpha, s);
+  if (N >= 8192) return launch_skinny<4, 2, 16>(w, x, out, out_bf16, M, N, K, alpha, epi, s);
+  return launch_skinny<1, 4, 16>(w, x, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
 }  // namespace qlinear

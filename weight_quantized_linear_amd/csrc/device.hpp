@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "epilogue.hpp"
+
 namespace qlinear {
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -138,6 +140,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // out[i] = round(alpha * acc) in the output type (0 = float32, 1 = bfloat16).
 __device__ __forceinline__ void store_out(void* out, int64_t i, float acc, float alpha, int out_bf16) {
   const float v = acc * alpha;
+  if (out_bf16) reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
+  else reinterpret_cast<float*>(out)[i] = v;
+}
+
+// ---------------------------------------------------------------- fused epilogue
+
+// Fused epilogue (the steps are listed at Epilogue) of output element (m, n).
+__device__ __forceinline__ float epi_apply(const Epilogue& e, float v, int64_t m, int64_t n) {
+  if (e.row_scale) v *= e.row_scale[m];
+  if (e.col_scale) v *= e.col_scale[n];
+  if (e.bias) v += bf16_to_f32(e.bias[n]);
+  if (e.act == 1) {
+    v = v > 0.f ? v : 0.f;
+  } else if (e.act == 2) {
+    v = v / (1.f + expf(-v));
+  } else if (e.act == 3) {
+    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+    v = 0.5f * v * (1.f + tanhf(u));
+  }
+  if (e.residual) {
+    const int64_t i = m * e.ld + n;
+    v += e.res_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(e.residual)[i])
+                    : reinterpret_cast<const float*>(e.residual)[i];
+  }
+  return v;
+}
+
+// out[m * N + n] = round(epilogue(alpha * acc)) in the output type.
+__device__ __forceinline__ void store_epi(void* out, int64_t m, int64_t n, int64_t N, float acc, float alpha,
+                                          int out_bf16, const Epilogue& epi) {
+  float v = acc * alpha;
+  if (epi.on) v = epi_apply(epi, v, m, n);
+  const int64_t i = m * N + n;
   if (out_bf16) reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
   else reinterpret_cast<float*>(out)[i] = v;
 }

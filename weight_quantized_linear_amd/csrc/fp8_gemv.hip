@@ -29,7 +29,7 @@ namespace qlinear {
 template <int M, int ROWS, int U>
 __global__ __launch_bounds__(256) void fp8_gemv_wide_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int64_t N, int64_t K, float alpha) {
+    int out_bf16, int64_t N, int64_t K, float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t row0 = wave * ROWS;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void fp8_gemv_wide_kernel(
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float s = wave_sum(acc[m][r]);
-      if (lane == 0 && row0 + r < N) store_out(out, m * N + row0 + r, s, alpha, out_bf16);
+      if (lane == 0 && row0 + r < N) store_epi(out, m, row0 + r, N, s, alpha, out_bf16, epi);
     }
 }
 
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void fp8_gemv_wide_kernel(
 template <int M, int ROWS>
 __global__ __launch_bounds__(256) void fp8_gemv_any_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int64_t N, int64_t K, float alpha) {
+    int out_bf16, int64_t N, int64_t K, float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t row0 = wave * ROWS;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void fp8_gemv_any_kernel(
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float s = wave_sum(acc[m][r]);
-      if (lane == 0 && row0 + r < N) store_out(out, m * N + row0 + r, s, alpha, out_bf16);
+      if (lane == 0 && row0 + r < N) store_epi(out, m, row0 + r, N, s, alpha, out_bf16, epi);
     }
 }
 
@@ -153,7 +153,7 @@ namespace {
 
 template <int M, int ROWS>
 hipError_t launch_rows(bool wide, const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
-                       int64_t N, int64_t K, float alpha, hipStream_t s) {
+                       int64_t N, int64_t K, float alpha, const Epilogue& epi, hipStream_t s) {
   constexpr int kThreads = 256;
   constexpr int kRowsPerBlock = ROWS * (kThreads / kWave);
   const int64_t blocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -163,33 +163,33 @@ hipError_t launch_rows(bool wide, const uint8_t* w, const uint16_t* x, void* out
     const int64_t per_lane = ((K >> 4) + kWave - 1) / kWave;
     if (M > 1 || per_lane <= 2)
       return launch(fp8_gemv_wide_kernel<M, ROWS, 2>, dim3(blocks), dim3(kThreads), 0, s, w, x, out,
-                    out_bf16, N, K, alpha);
+                    out_bf16, N, K, alpha, epi);
     return launch(fp8_gemv_wide_kernel<M, ROWS, 4>, dim3(blocks), dim3(kThreads), 0, s, w, x, out,
-                  out_bf16, N, K, alpha);
+                  out_bf16, N, K, alpha, epi);
   }
   return launch(fp8_gemv_any_kernel<M, ROWS>, dim3(blocks), dim3(kThreads), 0, s, w, x, out,
-                out_bf16, N, K, alpha);
+                out_bf16, N, K, alpha, epi);
 }
 
 template <int M>
 hipError_t launch_m(bool wide, const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
-                    int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s) {
+                    int64_t N, int64_t K, float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
   // Two rows per wave once that still gives every SIMD several waves.
-  if (N >= int64_t(num_cus) * 16) return launch_rows<M, 2>(wide, w, x, out, out_bf16, N, K, alpha, s);
-  return launch_rows<M, 1>(wide, w, x, out, out_bf16, N, K, alpha, s);
+  if (N >= int64_t(num_cus) * 16) return launch_rows<M, 2>(wide, w, x, out, out_bf16, N, K, alpha, epi, s);
+  return launch_rows<M, 1>(wide, w, x, out, out_bf16, N, K, alpha, epi, s);
 }
 
 }  // namespace
 
 hipError_t launch_fp8_gemv(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
-                           int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s) {
+                           int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s, const Epilogue& epi) {
   const bool wide = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   switch (M) {
-    case 1: return launch_m<1>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 2: return launch_m<2>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 3: return launch_m<3>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 4: return launch_m<4>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, s);
+    case 1: return launch_m<1>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 2: return launch_m<2>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 3: return launch_m<3>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 4: return launch_m<4>(wide, w, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
     default: return hipErrorInvalidValue;
   }
 }

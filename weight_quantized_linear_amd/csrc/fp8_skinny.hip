@@ -48,7 +48,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 template <int G, int U, int NWV>
 __global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int M, int64_t N, int64_t K, float alpha) {
+    int out_bf16, int M, int64_t N, int64_t K, float alpha, Epilogue epi) {
   constexpr int kWaves = NWV;
   static_assert(NWV >= 4, "the final sum uses four waves");
   __shared__ v4f red[kWaves][G][kWave];
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) s += red[q][g][lane][wid];
     const int64_t n = n0 + 16 * g + r16;
-    if (m < M && n < N) store_out(out, int64_t(m) * N + n, s, alpha, out_bf16);
+    if (m < M && n < N) store_epi(out, m, n, N, s, alpha, out_bf16, epi);
   }
 }
 
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
 template <int G, int KT>
 __global__ __launch_bounds__(256) void fp8_skinny_lds_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int M, int64_t N, int64_t K, float alpha) {
+    int out_bf16, int M, int64_t N, int64_t K, float alpha, Epilogue epi) {
   constexpr int kRow = KT + 16;                        // padded LDS row (bytes)
   constexpr int kChunksPerRow = KT / 16;
   constexpr int kLoads = 16 * G * kChunksPerRow / 256;  // 16-byte loads per thread per tile
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void fp8_skinny_lds_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) s += red[q][g][lane][wid];
     const int64_t n = n0 + 16 * g + r16;
-    if (m < M && n < N) store_out(out, int64_t(m) * N + n, s, alpha, out_bf16);
+    if (m < M && n < N) store_epi(out, m, n, N, s, alpha, out_bf16, epi);
   }
 }
 
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void fp8_skinny_lds_kernel(
 template <int G, int U>
 __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int M, int64_t N, int64_t K, float alpha) {
+    int out_bf16, int M, int64_t N, int64_t K, float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t n0 = wave * 4 * G;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
       if (n >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (i < M) store_out(out, int64_t(i) * N + n, acc[g][i], alpha, out_bf16);
+        if (i < M) store_epi(out, i, n, N, acc[g][i], alpha, out_bf16, epi);
     }
   }
 }
@@ -317,7 +317,7 @@ __device__ __forceinline__ void rs_halve(float* v, int lane, int mask) {
 template <int MG, int NWB, int KS>
 __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int M, int N, int K, float alpha) {
+    int out_bf16, int M, int N, int K, float alpha, Epilogue epi) {
   extern __shared__ __attribute__((aligned(16))) char xs[];
   constexpr int kU = 16;          // 16-byte loads per lane per stage (4 KiB per row)
   constexpr int kV = 4 * MG;      // accumulator values per lane
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
   auto store = [&](int grp, float val) {
     const int m = b >> (4 - kLogV);
     const int n = 4 * grp + j;
-    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N) store_out(out, int64_t(m) * N + n, val, alpha, out_bf16);
+    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N) store_epi(out, m, n, N, val, alpha, out_bf16, epi);
   };
 
   int g = blockIdx.x * kGpb + gi;
@@ -474,9 +474,9 @@ constexpr int kMaxLds = 160 * 1024;
 // fp8_skinny_kernel: a block of NWV waves per 16 G output columns.
 template <int G, int U, int NWV>
 hipError_t launch_skinny16(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                           int64_t K, float alpha, hipStream_t s) {
+                           int64_t K, float alpha, const Epilogue& epi, hipStream_t s) {
   return launch(fp8_skinny_kernel<G, U, NWV>, dim3((N + 16 * G - 1) / (16 * G)), dim3(NWV * kWave), 0, s, w, x, out,
-                out_bf16, int(M), N, K, alpha);
+                out_bf16, int(M), N, K, alpha, epi);
 }
 
 // Largest activation copy (bytes) the LDS holds: 4 MG padded rows x K bf16.
@@ -484,7 +484,7 @@ int xlds_groups(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
 
 template <int MG, int NWB, int KS>
 hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
-                           float alpha, int num_cus, hipStream_t s) {
+                           float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
   auto kern = fp8_skinny_xlds_kernel<MG, NWB, KS>;
   static bool attr_set = false;  // one flag per instantiation
   if (!attr_set) {
@@ -499,12 +499,12 @@ hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int o
   const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kMaxLds / lds, 16 / NWB));
   const int64_t blocks = std::min<int64_t>((groups + kGpb - 1) / kGpb, int64_t(num_cus) * per_cu);
   return launch(kern, dim3(unsigned(blocks)), dim3(NWB * kWave), size_t(lds), s, w, x, out, out_bf16, M, N, K,
-                alpha);
+                alpha, epi);
 }
 
 template <int MG>
 hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
-                       float alpha, int num_cus, hipStream_t s) {
+                       float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
   // About a dozen waves per CU in total: one large block per CU when there
   // are enough 4-row groups, otherwise smaller blocks over more CUs, and
   // with few groups the K chunks of each group split over four waves.  With
@@ -513,12 +513,12 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
   constexpr int kBig = MG == 1 ? 16 : (MG == 2 ? 12 : 8);
   const int64_t groups = (int64_t(N) + 3) / 4;
   if (groups >= int64_t(num_cus) * kBig)
-    return launch_xlds_nwb<MG, kBig, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+    return launch_xlds_nwb<MG, kBig, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
   if (groups >= int64_t(num_cus) * 8)
-    return launch_xlds_nwb<MG, 8, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+    return launch_xlds_nwb<MG, 8, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
   if (K >= 4096)
-    return launch_xlds_nwb<MG, 8, 4>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
-  return launch_xlds_nwb<MG, 4, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, s);
+    return launch_xlds_nwb<MG, 8, 4>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+  return launch_xlds_nwb<MG, 4, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
 }
 
 }  // namespace
@@ -530,14 +530,14 @@ bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                             hipStream_t s) {
+                             hipStream_t s, const Epilogue& epi) {
   // Measured: for 5 <= M <= 8 the activation-in-LDS kernel wins only at
   // very many output features, where its whole-row weight bursts matter most.
   if (fp8_skinny_xlds_supported(M, N, K) && (M <= 4 || N >= 65536)) {
     switch (xlds_groups(M)) {
-      case 1: return launch_xlds<1>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
-      case 2: return launch_xlds<2>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
-      default: return launch_xlds<4>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, s);
+      case 1: return launch_xlds<1>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, epi, s);
+      case 2: return launch_xlds<2>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, epi, s);
+      default: return launch_xlds<4>(w, x, out, out_bf16, int(M), int(N), int(K), alpha, num_cus, epi, s);
     }
   }
   const bool wide_n = N >= 65536;
@@ -545,17 +545,17 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
     if (wide_n) {
       const int64_t blocks = (N + 63) / 64;  // 4 waves x 16 rows
       return launch(fp8_skinny4_kernel<4, 2>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16, int(M), N,
-                    K, alpha);
+                    K, alpha, epi);
     }
     const int64_t blocks = (N + 15) / 16;  // 4 waves x 4 rows
     return launch(fp8_skinny4_kernel<1, 4>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16, int(M), N, K,
-                  alpha);
+                  alpha, epi);
   }
   if (wide_n)
     return launch(fp8_skinny_lds_kernel<4, 512>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out, out_bf16,
-                  int(M), N, K, alpha);
-  if (N >= 8192) return launch_skinny16<4, 2, 16>(w, x, out, out_bf16, M, N, K, alpha, s);
-  return launch_skinny16<1, 4, 16>(w, x, out, out_bf16, M, N, K, alpha, s);
+                  int(M), N, K, alpha, epi);
+  if (N >= 8192) return launch_skinny16<4, 2, 16>(w, x, out, out_bf16, M, N, K, alpha, epi, s);
+  return launch_skinny16<1, 4, 16>(w, x, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
 }  // namespace qlinear

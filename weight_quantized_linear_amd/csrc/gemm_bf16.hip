@@ -198,7 +198,7 @@ __device__ __forceinline__ Nvfp4Tile expert_tile(const Nvfp4Tile& b, int64_t e) 
 // stores alpha * acc.  Every thread of the block must call it.
 template <class WTile>
 __device__ void gemm_tile(char* lds, const ActTile& A, const WTile& B, void* out, int out_bf16,
-                          int64_t m0, int64_t n0, float alpha) {
+                          int64_t m0, int64_t n0, float alpha, const Epilogue& epi) {
   using WStage = typename StageOf<WTile>::type;
   char* lds_a = lds;
   char* lds_b = lds + kLdsTile;
@@ -255,7 +255,7 @@ __device__ void gemm_tile(char* lds, const ActTile& A, const WTile& B, void* out
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wx * 64 + 16 * j + r16;
-        if (n < B.N) store_out(out, m * B.N + n, acc[i][j][v], alpha, out_bf16);
+        if (n < B.N) store_epi(out, m, n, B.N, acc[i][j][v], alpha, out_bf16, epi);
       }
     }
 }
@@ -281,12 +281,12 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_m, int64_
 
 template <class WTile>
 __global__ __launch_bounds__(kThreads) void gemm_dense_kernel(ActTile A, WTile B, void* __restrict__ out,
-                                                              int out_bf16, float alpha) {
+                                                              int out_bf16, float alpha, Epilogue epi) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int64_t tiles_m = (A.M + BM - 1) / BM, tiles_n = (B.N + BN - 1) / BN;
   int64_t tm, tn;
   tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  gemm_tile(lds, A, B, out, out_bf16, tm * BM, tn * BN, alpha);
+  gemm_tile(lds, A, B, out, out_bf16, tm * BM, tn * BN, alpha, epi);
 }
 
 // Ragged groups: group z = blockIdx.z covers activation rows
@@ -294,12 +294,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dense_kernel(ActTile A, WTile B
 // the column tile and row tiles of the group are taken blockIdx.y, +gridDim.y, ...
 // An id outside 0..E-1 (-1 marks an inactive group) writes zeros; offsets are
 // clipped to T and a group whose end does not exceed its start does nothing.
-// `B` addresses expert 0 of the weight stack (FP8 or NVFP4).
+// `B` addresses expert 0 of the weight stack (FP8 or NVFP4); expert_scale
+// (null: raw output) gives the factor of each expert's rows.
 template <class WTile>
 __global__ __launch_bounds__(kThreads) void gemm_grouped_kernel(
     const uint16_t* __restrict__ x, WTile B, const uint32_t* __restrict__ a_offsets,
-    const int32_t* __restrict__ expert_ids, void* __restrict__ out, int out_bf16, int64_t T,
-    int64_t N, int64_t K, int64_t E, bool vec) {
+    const int32_t* __restrict__ expert_ids, const float* __restrict__ expert_scale, void* __restrict__ out,
+    int out_bf16, int64_t T, int64_t N, int64_t K, int64_t E, bool vec) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int64_t z = blockIdx.z;
   int64_t start = a_offsets[z], end = a_offsets[z + 1];
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void gemm_grouped_kernel(
     }
     const ActTile A{x + start * K, rows, K, vec};
     gemm_tile(lds, A, expert_tile(B, e), static_cast<char*>(out) + start * N * (out_bf16 ? 2 : 4), out_bf16, m0, n0,
-              1.f);
+              expert_scale ? expert_scale[e] : 1.f, Epilogue{});
   }
 }
 
@@ -328,48 +329,50 @@ __global__ __launch_bounds__(kThreads) void gemm_grouped_kernel(
 
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
                             int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
-                            hipStream_t s) {
+                            hipStream_t s, const Epilogue& epi) {
   if (gemm_lds_supported(x, w, w, M, N, K))
-    return launch_fp8_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s);
+    return launch_fp8_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s, epi);
   const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const ActTile A{x, M, K, vec};
   const Fp8Tile B{w, N, K, vec};
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return launch(gemm_dense_kernel<Fp8Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16, alpha);
+  return launch(gemm_dense_kernel<Fp8Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16, alpha, epi);
 }
 
 hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                               int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
-                              size_t ws_bytes, hipStream_t s) {
+                              size_t ws_bytes, hipStream_t s, const Epilogue& epi) {
   if (gemm_lds_supported(x, packed, scales, M, N, K))
-    return launch_nvfp4_gemm_lds(packed, scales, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s);
+    return launch_nvfp4_gemm_lds(packed, scales, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s, epi);
   const bool vec = (K % 32 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const ActTile A{x, M, K, vec};
   const Nvfp4Tile B{packed, scales, N, K, vec};
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   return launch(gemm_dense_kernel<Nvfp4Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16,
-                alpha);
+                alpha, epi);
 }
 
 hipError_t launch_bf16_tiled(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                             int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s) {
+                             int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s,
+                             const Epilogue& epi) {
   if (bf16_lds_supported(x, w, M, N, K))
-    return launch_bf16_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s);
+    return launch_bf16_gemm_lds(w, x, out, out_bf16, M, N, K, alpha, num_cus, ws, ws_bytes, s, epi);
   const bool vec = bf16_wide(w, x, K);
   const ActTile A{x, M, K, vec};
   const Bf16Tile B{w, N, K, vec};
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return launch(gemm_dense_kernel<Bf16Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16, alpha);
+  return launch(gemm_dense_kernel<Bf16Tile>, dim3(blocks), dim3(kThreads), 0, s, A, B, out, out_bf16, alpha, epi);
 }
 
 hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G,
                               int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
-                              int num_cus, hipStream_t s) {
+                              int num_cus, hipStream_t s, const float* expert_scale) {
   if (grouped_lds_supported(x, w, G, T, N, K))
-    return launch_fp8_grouped_lds(w, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
+    return launch_fp8_grouped_lds(w, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s,
+                                  expert_scale);
   const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   int64_t tiles_m = (max_tokens + BM - 1) / BM;
@@ -377,16 +380,16 @@ hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_
   if (tiles_m > 65535) tiles_m = 65535;
   (void)num_cus;
   return launch(gemm_grouped_kernel<Fp8Tile>, dim3((N + BN - 1) / BN, tiles_m, G), dim3(kThreads), 0, s, x,
-                Fp8Tile{w, N, K, vec}, a_offsets, expert_ids, out, out_bf16, T, N, K, E, vec);
+                Fp8Tile{w, N, K, vec}, a_offsets, expert_ids, expert_scale, out, out_bf16, T, N, K, E, vec);
 }
 
 hipError_t launch_nvfp4_grouped(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
                                 const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
                                 int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
-                                int num_cus, hipStream_t s) {
+                                int num_cus, hipStream_t s, const float* expert_scale) {
   if (nvfp4_grouped_lds_supported(x, packed, scales, G, T, N, K))
     return launch_nvfp4_grouped_lds(packed, scales, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus,
-                                    s);
+                                    s, expert_scale);
   // The element-wise fallback: vec needs every expert's packed rows 16-byte
   // aligned (K % 32 == 0 and an aligned base).
   const bool vec = (K % 32 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0) &&
@@ -395,7 +398,8 @@ hipError_t launch_nvfp4_grouped(const uint8_t* packed, const uint8_t* scales, co
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_m > 65535) tiles_m = 65535;
   return launch(gemm_grouped_kernel<Nvfp4Tile>, dim3((N + BN - 1) / BN, tiles_m, G), dim3(kThreads), 0, s, x,
-                Nvfp4Tile{packed, scales, N, K, vec}, a_offsets, expert_ids, out, out_bf16, T, N, K, E, vec);
+                Nvfp4Tile{packed, scales, N, K, vec}, a_offsets, expert_ids, expert_scale, out, out_bf16, T, N, K, E,
+                vec);
 }
 
 }  // namespace qlinear

@@ -539,7 +539,7 @@ struct WqLayout {
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
 __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ x, typename WP<BN, 1, NW>::Args wa,
                                         void* __restrict__ out, int64_t M, int64_t N, int64_t K, float alpha,
-                                        int vec, int64_t m0, int64_t n0, int64_t s0, int64_t ns) {
+                                        int vec, int64_t m0, int64_t n0, int64_t s0, int64_t ns, const Epilogue& epi) {
   using L = WqLayout<WP, BM, BN, S, WY, NW>;
   using W = typename L::W;
   constexpr int FM = L::FM, FN = L::FN;
@@ -651,45 +651,59 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
   else main_loop(std::false_type{});
 
   // acc[i][j][v] = C[m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + col0 + 32 j + r]
-  // Full tiles leave through the per-wave LDS slabs when they fit.
-  constexpr bool kSlabFits = kSlabBase + NW * Slab<OUT, FN, 32>::kBytes <= L::kLds;
-  if (kSlabFits && vec && m0 + BM <= M && n0 + BN <= N) {
-    block_barrier();  // every wave is done reading the last strip
-    const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
+  // Full tiles leave through the per-wave LDS slabs when they fit.  The
+  // fused epilogue, when present, is applied to each element on its way.
+  auto store = [&](auto fused) {
+    constexpr bool FUSED = decltype(fused)::value;
+    auto value = [&](float a, int64_t m, int64_t n) {
+      if constexpr (FUSED) return epi_apply(epi, a * alpha, m, n);
+      else return a * alpha;
+    };
+    constexpr bool kSlabFits = kSlabBase + NW * Slab<OUT, FN, 32>::kBytes <= L::kLds;
+    if (kSlabFits && vec && m0 + BM <= M && n0 + BN <= N) {
+      block_barrier();  // every wave is done reading the last strip
+      const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) slab.put_f(8 * (v / 4) + 4 * h + (v % 4), 32 * j + r, acc[i][j][v] * alpha);
-      slab.flush(out, N, m0 + row0 + 32 * i, n0 + col0);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab reads done before it is rewritten
-    }
-  } else {
-    const int64_t mw = m0 + row0 + 4 * h, nw = n0 + col0 + r;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = mw + 32 * i + 8 * (v / 4) + (v % 4);
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t n = nw + 32 * j;
-          if (n < N) put_out<OUT>(out, m * N + n, acc[i][j][v] * alpha);
-        }
+          for (int v = 0; v < 16; ++v) {
+            const int row = 8 * (v / 4) + 4 * h + (v % 4), col = 32 * j + r;
+            slab.put_f(row, col, value(acc[i][j][v], m0 + row0 + 32 * i + row, n0 + col0 + col));
+          }
+        slab.flush(out, N, m0 + row0 + 32 * i, n0 + col0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab reads done before it is rewritten
       }
-  }
+    } else {
+      const int64_t mw = m0 + row0 + 4 * h, nw = n0 + col0 + r;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = mw + 32 * i + 8 * (v / 4) + (v % 4);
+          if (m >= M) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = nw + 32 * j;
+            if (n < N) put_out<OUT>(out, m * N + n, value(acc[i][j][v], m, n));
+          }
+        }
+    }
+  };
+  if (epi.on) store(std::true_type{});
+  else store(std::false_type{});
 }
 
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
 __global__ __launch_bounds__(64 * NW) void wq_gemm_kernel(const uint16_t* __restrict__ x,
                                                           typename WP<BN, 1, NW>::Args wa, void* __restrict__ out,
-                                                          int64_t M, int64_t N, int64_t K, float alpha, int vec) {
+                                                          int64_t M, int64_t N, int64_t K, float alpha, int vec,
+                                                          Epilogue epi) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0, K / 64);
+  wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0, K / 64, epi);
 }
 
 // Split-K: block b computes slice b % splits of tile b / splits into the
@@ -705,15 +719,26 @@ __global__ __launch_bounds__(64 * NW) void wq_splitk_kernel(const uint16_t* __re
   tile_of_block(tile, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int64_t nk = K / 64, per = (nk + splits - 1) / splits;
   const int64_t s0 = slice * per, ns = nk - s0 < per ? nk - s0 : per;
-  wq_tile<WP, BM, BN, S, WY, NW, 0>(lds, x, wa, part + slice * M * N, M, N, K, 1.f, vec, tm * BM, tn * BN, s0, ns);
+  wq_tile<WP, BM, BN, S, WY, NW, 0>(lds, x, wa, part + slice * M * N, M, N, K, 1.f, vec, tm * BM, tn * BN, s0, ns,
+                                    Epilogue{});
 }
 
-// out[i] = alpha * sum over the planes of part[plane][i], four elements per thread.
+// out[i] = epilogue(alpha * sum over the planes of part[plane][i]), four
+// elements per thread; element i is (i / N, i % N) of out[M, N].
 template <int OUT>
 __global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict__ part, void* __restrict__ out,
-                                                        int64_t count, int splits, float alpha) {
+                                                        int64_t count, int splits, float alpha, int64_t N,
+                                                        Epilogue epi) {
   const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= count) return;
+  if (epi.on) {
+    for (int64_t j = i; j < i + 4 && j < count; ++j) {
+      float acc = part[j];
+      for (int p = 1; p < splits; ++p) acc += part[p * count + j];
+      put_out<OUT>(out, j, epi_apply(epi, acc * alpha, j / N, j % N));
+    }
+    return;
+  }
   if (i + 4 <= count && count % 4 == 0) {
     v4f acc = *reinterpret_cast<const v4f*>(part + i);
     for (int p = 1; p < splits; ++p) acc += *reinterpret_cast<const v4f*>(part + p * count + i);
@@ -741,12 +766,14 @@ __global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict_
 // expert then meet its weight tiles in the same L2, which each weight tile
 // is fetched into once.
 // WP: the weight format (Fp8Weight, or Nvfp4Weight for W4A16 experts); `wa`
-// addresses expert 0 of the stack.
+// addresses expert 0 of the stack.  expert_scale (null: raw output) gives the
+// factor of each expert's rows, applied before the single rounding.
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
 __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* __restrict__ x,
                                                                 typename WP<BN, 1, NW>::Args wa,
                                                                 const uint32_t* __restrict__ a_offsets,
                                                                 const int32_t* __restrict__ expert_ids,
+                                                                const float* __restrict__ expert_scale,
                                                                 void* __restrict__ out, int64_t G, int64_t T,
                                                                 int64_t N, int64_t K, int64_t E, int vec) {
   using L = WqLayout<WP, BM, BN, S, WY, NW>;
@@ -817,28 +844,29 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* _
     if (!first) __syncthreads();
     first = false;
     wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x + start * K, WP<BN, 1, NW>::expert(wa, e, N, K), gout, rows, N, K,
-                                         1.f, vec, m0, n0, 0, K / 64);
+                                         expert_scale ? expert_scale[e] : 1.f, vec, m0, n0, 0, K / 64, Epilogue{});
   }
 }
 
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
 hipError_t launch_wq(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, void* out, int out_bf16, int64_t M,
-                     int64_t N, int64_t K, float alpha, hipStream_t s) {
+                     int64_t N, int64_t K, float alpha, const Epilogue& epi, hipStream_t s) {
   using L = WqLayout<WP, BM, BN, S, WY, NW>;
   const int64_t blocks = tiles(M, N, BM, BN);
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   if (out_bf16)
     return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N, K,
-                                                                     alpha, vec);
+                                                                     alpha, vec, epi);
   return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N, K,
-                                                                   alpha, vec);
+                                                                   alpha, vec, epi);
 }
 
 // Split-K launch: partial planes in the caller's float32 workspace.
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
 hipError_t launch_wq_splitk(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, void* out, int out_bf16, int64_t M,
-                            int64_t N, int64_t K, float alpha, int splits, float* ws, hipStream_t s) {
+                            int64_t N, int64_t K, float alpha, int splits, float* ws, const Epilogue& epi,
+                            hipStream_t s) {
   using L = WqLayout<WP, BM, BN, S, WY, NW>;
   const int64_t blocks = tiles(M, N, BM, BN) * splits;
   const int vec = aligned16(ws) && (N * 4) % 16 == 0;
@@ -846,8 +874,9 @@ hipError_t launch_wq_splitk(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, 
                                                                           K, splits, vec);
   if (e != hipSuccess) return e;
   const int64_t count = M * N, rblocks = (count + 1023) / 1024;
-  if (out_bf16) return launch(wq_reduce_kernel<1>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha);
-  return launch(wq_reduce_kernel<0>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha);
+  if (out_bf16)
+    return launch(wq_reduce_kernel<1>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha, N, epi);
+  return launch(wq_reduce_kernel<0>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha, N, epi);
 }
 
 // Number of K slices for a grid of `nt` tiles: enough blocks to cover the
@@ -1255,35 +1284,36 @@ bool int8_lds_supported(const void* a, const void* b, int64_t M, int64_t N, int6
 }
 
 hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                               int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s) {
+                               int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s,
+                               const Epilogue& epi) {
   const Fp8Args wa{w};
   if (ws) {
     const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
-    if (sp > 1) return launch_wq_splitk<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, s);
+    if (sp > 1) return launch_wq_splitk<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
   }
   // Largest tile that still gives every CU a block.
   if (tiles(M, N, 256, 256) >= num_cus)
-    return launch_wq<Fp8Weight, 256, 256, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+    return launch_wq<Fp8Weight, 256, 256, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   if (tiles(M, N, 256, 128) >= num_cus)
-    return launch_wq<Fp8Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  return launch_wq<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+    return launch_wq<Fp8Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+  return launch_wq<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
 hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                                  int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
-                                 size_t ws_bytes, hipStream_t s) {
+                                 size_t ws_bytes, hipStream_t s, const Epilogue& epi) {
   const Nvfp4Args wa{packed, scales};
   if (ws) {
     const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
     if (sp > 1)
-      return launch_wq_splitk<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, s);
+      return launch_wq_splitk<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
   }
   // The FP4 decode is the expensive part: waves side by side along N (WY = 1)
   // where the tile is wide enough, so that no two waves decode the same
   // weight rows.
   if (tiles(M, N, 128, 256) >= num_cus / 2)
-    return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+    return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+  return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
 bool bf16_lds_supported(const void* x, const void* w, int64_t M, int64_t N, int64_t K) {
@@ -1292,17 +1322,18 @@ bool bf16_lds_supported(const void* x, const void* w, int64_t M, int64_t N, int6
 }
 
 hipError_t launch_bf16_gemm_lds(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s) {
+                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s,
+                                const Epilogue& epi) {
   const Bf16Args wa{w};
   if (ws) {
     const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
-    if (sp > 1) return launch_wq_splitk<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, s);
+    if (sp > 1) return launch_wq_splitk<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
   }
   // A 256 x 256 stage of both bf16 operands (64 KiB) leaves room for only two
   // stages: the largest tile runs 256 x 128 with three.
   if (tiles(M, N, 256, 128) >= num_cus)
-    return launch_wq<Bf16Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
-  return launch_wq<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, s);
+    return launch_wq<Bf16Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+  return launch_wq<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
 namespace {
@@ -1313,7 +1344,7 @@ namespace {
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW>
 hipError_t launch_grouped_cfg(typename WP<BN, 1, NW>::Args wa, const uint16_t* x, const uint32_t* a_offsets,
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
-                              int64_t N, int64_t K, int num_cus, hipStream_t s) {
+                              int64_t N, int64_t K, int num_cus, hipStream_t s, const float* expert_scale) {
   using L = WqLayout<WP, BM, BN, S, WY, NW>;
   const int lds_bytes = int(L::kLds + 4 * (G + 1));
   if (lds_bytes > kMaxLds) return hipErrorInvalidValue;
@@ -1334,8 +1365,8 @@ hipError_t launch_grouped_cfg(typename WP<BN, 1, NW>::Args wa, const uint16_t* x
       if (e != hipSuccess) return e;
       attr = true;
     }
-    return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, x, wa, a_offsets, expert_ids, out, G, T, N, K,
-                  E, vec);
+    return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, x, wa, a_offsets, expert_ids, expert_scale, out, G,
+                  T, N, K, E, vec);
   };
   if (out_bf16) return go(grouped_gemm_kernel<WP, BM, BN, S, WY, NW, 1>);
   return go(grouped_gemm_kernel<WP, BM, BN, S, WY, NW, 0>);
@@ -1366,17 +1397,17 @@ bool nvfp4_grouped_lds_supported(const void* x, const void* packed, const void* 
 
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                                   const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
-                                  int64_t N, int64_t K, int num_cus, hipStream_t s) {
+                                  int64_t N, int64_t K, int num_cus, hipStream_t s, const float* expert_scale) {
   return launch_grouped_cfg<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(
-      Fp8Args{w}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
+      Fp8Args{w}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s, expert_scale);
 }
 
 hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
                                     const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
                                     int64_t G, int64_t E, int64_t T, int64_t N, int64_t K, int num_cus,
-                                    hipStream_t s) {
+                                    hipStream_t s, const float* expert_scale) {
   return launch_grouped_cfg<Nvfp4Weight, kGrpBM, kGrpBN, kGrpS, kGrp4WY, kGrpNW>(
-      Nvfp4Args{packed, scales}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s);
+      Nvfp4Args{packed, scales}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s, expert_scale);
 }
 
 hipError_t launch_fp8_w8a8_lds(const uint8_t* xq, const uint8_t* w, void* out, int out_bf16, int64_t M, int64_t N,

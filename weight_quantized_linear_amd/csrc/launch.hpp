@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "epilogue.hpp"
+
 namespace qlinear {
 
 template <typename T> struct same_type { using type = T; };
@@ -22,7 +24,7 @@ hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t shmem
 
 // fp8_gemv.hip
 hipError_t launch_fp8_gemv(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
-                           int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s);
+                           int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // fp8_skinny.hip
 // True when the activation-resident matrix-core kernel serves (M, N, K)
@@ -30,47 +32,47 @@ hipError_t launch_fp8_gemv(const uint8_t* w, const uint16_t* x, void* out, int o
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                             hipStream_t s);
+                             hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // gemm_bf16.hip (dispatches to gemm_lds.hip when K % 64 == 0 and operands are aligned)
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
                             int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
-                            hipStream_t s);
+                            hipStream_t s, const Epilogue& epi = Epilogue{});
 hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                               int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
-                              size_t ws_bytes, hipStream_t s);
+                              size_t ws_bytes, hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // gemm_lds.hip
 bool gemm_lds_supported(const void* x, const void* w, const void* scales, int64_t M, int64_t N, int64_t K);
 // ws / ws_bytes: float32 workspace for split-K partial sums (null: whole-K tiles only).
 hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                               int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s);
+                               int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s, const Epilogue& epi = Epilogue{});
 bool int8_lds_supported(const void* a, const void* b, int64_t M, int64_t N, int64_t K);
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
                                 const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
                                 int num_cus, hipStream_t s);
 hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                                  int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus, float* ws,
-                                 size_t ws_bytes, hipStream_t s);
+                                 size_t ws_bytes, hipStream_t s, const Epilogue& epi = Epilogue{});
 bool grouped_lds_supported(const void* x, const void* w, int64_t G, int64_t T, int64_t N, int64_t K);
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                                   const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
-                                  int64_t N, int64_t K, int num_cus, hipStream_t s);
+                                  int64_t N, int64_t K, int num_cus, hipStream_t s, const float* expert_scale = nullptr);
 hipError_t launch_fp8_grouped(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                               const int32_t* expert_ids, void* out, int out_bf16, int64_t G,
                               int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
-                              int num_cus, hipStream_t s);
+                              int num_cus, hipStream_t s, const float* expert_scale = nullptr);
 bool nvfp4_grouped_lds_supported(const void* x, const void* packed, const void* scales, int64_t G, int64_t T,
                                  int64_t N, int64_t K);
 hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
                                     const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
                                     int64_t G, int64_t E, int64_t T, int64_t N, int64_t K, int num_cus,
-                                    hipStream_t s);
+                                    hipStream_t s, const float* expert_scale = nullptr);
 // Grouped NVFP4 (expert stacks [E, N, K/2] and [E, N, K/16], K % 16 == 0).
 hipError_t launch_nvfp4_grouped(const uint8_t* packed, const uint8_t* scales, const uint16_t* x,
                                 const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
                                 int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
-                                int num_cus, hipStream_t s);
+                                int num_cus, hipStream_t s, const float* expert_scale = nullptr);
 
 // fp8_w8a8.hip (FP8 activations: static per-tensor quantiser, fp8 x fp8 GEMM)
 hipError_t launch_fp8_quantize_act(const uint16_t* x, uint8_t* q, float input_scale, int64_t M, int64_t K,
@@ -85,18 +87,18 @@ hipError_t launch_fp8_w8a8_lds(const uint8_t* xq, const uint8_t* w, void* out, i
 // Dense bf16 control (bf16_dense.hip, gemm_lds.hip, gemm_bf16.hip).
 bool bf16_wide(const void* w, const void* x, int64_t K);
 hipError_t launch_bf16_gemv(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                            int64_t K, float alpha, int num_cus, hipStream_t s);
+                            int64_t K, float alpha, int num_cus, hipStream_t s, const Epilogue& epi = Epilogue{});
 hipError_t launch_bf16_skinny(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                              int64_t K, float alpha, int num_cus, hipStream_t s);
+                              int64_t K, float alpha, int num_cus, hipStream_t s, const Epilogue& epi = Epilogue{});
 bool bf16_lds_supported(const void* x, const void* w, int64_t M, int64_t N, int64_t K);
 hipError_t launch_bf16_gemm_lds(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s);
+                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s, const Epilogue& epi = Epilogue{});
 hipError_t launch_bf16_tiled(const uint16_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
-                             int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s);
+                             int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s, const Epilogue& epi = Epilogue{});
 
 hipError_t launch_nvfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                             hipStream_t s);
+                             hipStream_t s, const Epilogue& epi = Epilogue{});
 hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, void* out, int out_bf16,
                                 int64_t N, int64_t K, hipStream_t s);
 

@@ -28,7 +28,7 @@ template <int M, int ROWS>
 __global__ __launch_bounds__(256) void nvfp4_gemv_wide_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const uint16_t* __restrict__ x, void* __restrict__ out, int out_bf16, int64_t N, int64_t K,
-    float alpha) {
+    float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t row0 = wave * ROWS;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemv_wide_kernel(
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const float t = wave_sum(acc[m][r]);
-      if (lane == 0 && row0 + r < N) store_out(out, m * N + row0 + r, t, alpha, out_bf16);
+      if (lane == 0 && row0 + r < N) store_epi(out, m, row0 + r, N, t, alpha, out_bf16, epi);
     }
 }
 
@@ -125,7 +125,7 @@ template <int M>
 __global__ __launch_bounds__(256) void nvfp4_gemv_any_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     const uint16_t* __restrict__ x, void* __restrict__ out, int out_bf16, int64_t N, int64_t K,
-    float alpha) {
+    float alpha, Epilogue epi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (row >= N) return;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemv_any_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const float t = wave_sum(acc[m]);
-    if (lane == 0) store_out(out, m * N + row, t, alpha, out_bf16);
+    if (lane == 0) store_epi(out, m, row, N, t, alpha, out_bf16, epi);
   }
 }
 
@@ -174,35 +174,35 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t* __res
 
 template <int M>
 hipError_t gemv_m(bool wide, const uint8_t* p, const uint8_t* sc, const uint16_t* x, void* out, int bf16,
-                  int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s) {
+                  int64_t N, int64_t K, float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
   if (!wide) {
     const int64_t blocks = (N + 3) / 4;
-    return launch(nvfp4_gemv_any_kernel<M>, dim3(blocks), dim3(256), 0, s, p, sc, x, out, bf16, N, K, alpha);
+    return launch(nvfp4_gemv_any_kernel<M>, dim3(blocks), dim3(256), 0, s, p, sc, x, out, bf16, N, K, alpha, epi);
   }
   const int64_t target_waves = int64_t(num_cus) * 8;
   if (N >= target_waves * 4)
     return launch(nvfp4_gemv_wide_kernel<M, 4>, dim3((N + 15) / 16), dim3(256), 0, s, p, sc, x, out, bf16, N,
-                  K, alpha);
+                  K, alpha, epi);
   if (N >= target_waves * 2)
     return launch(nvfp4_gemv_wide_kernel<M, 2>, dim3((N + 7) / 8), dim3(256), 0, s, p, sc, x, out, bf16, N, K,
-                  alpha);
+                  alpha, epi);
   return launch(nvfp4_gemv_wide_kernel<M, 1>, dim3((N + 3) / 4), dim3(256), 0, s, p, sc, x, out, bf16, N, K,
-                alpha);
+                alpha, epi);
 }
 
 }  // namespace
 
 hipError_t launch_nvfp4_gemv(const uint8_t* packed, const uint8_t* scales, const uint16_t* x, void* out,
                              int out_bf16, int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
-                             hipStream_t s) {
+                             hipStream_t s, const Epilogue& epi) {
   const bool wide = (K % 32 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(scales) % 2 == 0) &&
                     (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   switch (M) {
-    case 1: return gemv_m<1>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 2: return gemv_m<2>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 3: return gemv_m<3>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, s);
-    case 4: return gemv_m<4>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, s);
+    case 1: return gemv_m<1>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 2: return gemv_m<2>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 3: return gemv_m<3>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
+    case 4: return gemv_m<4>(wide, packed, scales, x, out, out_bf16, N, K, alpha, num_cus, epi, s);
     default: return hipErrorInvalidValue;
   }
 }

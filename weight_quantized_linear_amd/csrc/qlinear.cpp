@@ -100,8 +100,33 @@ size_t out_size(int out_dtype) { return out_dtype == QLINEAR_BF16 ? 2 : 4; }
 
 int finish(hipError_t e) { return e == hipSuccess ? QLINEAR_OK : QLINEAR_ERR_LAUNCH; }
 
+// Validates a caller's epilogue for an [M, N] output and converts it (null:
+// no epilogue).  The residual may be the output itself (same type, ld = N).
+int to_epilogue(const qlinear_epilogue* e, int64_t M, int64_t N, Epilogue* out) {
+  *out = Epilogue{};
+  if (!e) return QLINEAR_OK;
+  if (e->activation < QLINEAR_ACT_NONE || e->activation > QLINEAR_ACT_GELU_TANH) return QLINEAR_ERR_INVALID_ARG;
+  if ((e->row_scale && !aligned(e->row_scale, 4)) || (e->col_scale && !aligned(e->col_scale, 4)) ||
+      (e->bias && !aligned(e->bias, 2)))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (e->residual) {
+    if (e->residual_dtype != QLINEAR_F32 && e->residual_dtype != QLINEAR_BF16) return QLINEAR_ERR_INVALID_ARG;
+    if (e->residual_ld < N || !aligned(e->residual, out_size(e->residual_dtype)) || !fits(M, e->residual_ld))
+      return QLINEAR_ERR_INVALID_ARG;
+  }
+  out->row_scale = e->row_scale;
+  out->col_scale = e->col_scale;
+  out->bias = static_cast<const uint16_t*>(e->bias);
+  out->residual = e->residual;
+  out->ld = e->residual ? e->residual_ld : 0;
+  out->act = e->activation;
+  out->res_bf16 = e->residual_dtype == QLINEAR_BF16;
+  out->on = e->row_scale || e->col_scale || e->bias || e->residual || e->activation != QLINEAR_ACT_NONE;
+  return QLINEAR_OK;
+}
+
 int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
-                  int64_t K, float alpha, int path, void* stream) {
+                  int64_t K, float alpha, int path, void* stream, const qlinear_epilogue* epilogue = nullptr) {
   if (!w || !x || !out) return QLINEAR_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return QLINEAR_ERR_INVALID_ARG;
@@ -133,6 +158,8 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
     default:
       return QLINEAR_ERR_INVALID_ARG;
   }
+  Epilogue epi;
+  if (int st = to_epilogue(epilogue, M, N, &epi)) return st;
   int num_cus = 0;
   DeviceInfo* dev = nullptr;
   if (int st = current_device(&num_cus, &dev)) return st;
@@ -141,14 +168,16 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   auto* xp = static_cast<const uint16_t*>(x);
   const int bf16 = out_dtype == QLINEAR_BF16;
   if (path == QLINEAR_PATH_GEMV)
-    return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
+    return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
   if (path == QLINEAR_PATH_SKINNY)
-    return finish(launch_fp8_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
+    return finish(launch_fp8_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
+  return finish(
+      launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s, epi));
 }
 
 int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, int out_dtype, int64_t M,
-                    int64_t N, int64_t K, float alpha, int path, void* stream) {
+                    int64_t N, int64_t K, float alpha, int path, void* stream,
+                    const qlinear_epilogue* epilogue = nullptr) {
   if (!wp || !ws || !x || !out) return QLINEAR_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return QLINEAR_ERR_INVALID_ARG;
@@ -160,6 +189,8 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
   } else if (path != QLINEAR_PATH_TILED) {
     return QLINEAR_ERR_INVALID_ARG;
   }
+  Epilogue epi;
+  if (int st = to_epilogue(epilogue, M, N, &epi)) return st;
   int num_cus = 0;
   DeviceInfo* dev = nullptr;
   if (int st = current_device(&num_cus, &dev)) return st;
@@ -169,13 +200,13 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
   auto* xp = static_cast<const uint16_t*>(x);
   const int bf16 = out_dtype == QLINEAR_BF16;
   if (path == QLINEAR_PATH_GEMV)
-    return finish(launch_nvfp4_gemv(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s));
+    return finish(launch_nvfp4_gemv(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
   return finish(
-      launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
+      launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s, epi));
 }
 
 int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
-                   float alpha, int path, void* stream) {
+                   float alpha, int path, void* stream, const qlinear_epilogue* epilogue = nullptr) {
   if (!w || !x || !out) return QLINEAR_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return QLINEAR_ERR_INVALID_ARG;
@@ -199,6 +230,8 @@ int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64
     default:
       return QLINEAR_ERR_INVALID_ARG;
   }
+  Epilogue epi;
+  if (int st = to_epilogue(epilogue, M, N, &epi)) return st;
   int num_cus = 0;
   DeviceInfo* dev = nullptr;
   if (int st = current_device(&num_cus, &dev)) return st;
@@ -206,9 +239,12 @@ int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64
   auto* wp = static_cast<const uint16_t*>(w);
   auto* xp = static_cast<const uint16_t*>(x);
   const int bf16 = out_dtype == QLINEAR_BF16;
-  if (path == QLINEAR_PATH_GEMV) return finish(launch_bf16_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  if (path == QLINEAR_PATH_SKINNY) return finish(launch_bf16_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s));
-  return finish(launch_bf16_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s));
+  if (path == QLINEAR_PATH_GEMV)
+    return finish(launch_bf16_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
+  if (path == QLINEAR_PATH_SKINNY)
+    return finish(launch_bf16_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
+  return finish(
+      launch_bf16_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s, epi));
 }
 
 }  // namespace
@@ -259,7 +295,16 @@ int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_off
                              const int32_t* expert_ids, void* out, int out_dtype, int64_t num_groups,
                              int64_t max_tokens_per_group, int64_t num_experts, int64_t T, int64_t N,
                              int64_t K, void* stream) {
+  return qlinear_fp8_grouped_gemm_scaled(w, x, a_offsets, expert_ids, nullptr, out, out_dtype, num_groups,
+                                         max_tokens_per_group, num_experts, T, N, K, stream);
+}
+
+int qlinear_fp8_grouped_gemm_scaled(const void* w, const void* x, const uint32_t* a_offsets,
+                                    const int32_t* expert_ids, const float* expert_scale, void* out, int out_dtype,
+                                    int64_t num_groups, int64_t max_tokens_per_group, int64_t num_experts, int64_t T,
+                                    int64_t N, int64_t K, void* stream) {
   if (!w || !x || !a_offsets || !expert_ids || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (expert_scale && !aligned(expert_scale, 4)) return QLINEAR_ERR_INVALID_ARG;
   if (num_groups <= 0 || num_groups > 65535 || max_tokens_per_group < 0 || num_experts <= 0 || T <= 0 ||
       N <= 0 || K <= 0)
     return QLINEAR_ERR_INVALID_ARG;
@@ -272,7 +317,7 @@ int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_off
   return finish(launch_fp8_grouped(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x),
                                    a_offsets, expert_ids, out, out_dtype == QLINEAR_BF16, num_groups,
                                    max_tokens_per_group, num_experts, T, N, K, num_cus,
-                                   static_cast<hipStream_t>(stream)));
+                                   static_cast<hipStream_t>(stream), expert_scale));
 }
 
 int qlinear_fp8_quantize_act(const void* x, void* q, float input_scale, int64_t M, int64_t K, void* stream) {
@@ -300,7 +345,16 @@ int qlinear_nvfp4_grouped_gemm(const void* w_packed, const void* w_scale, const 
                                const int32_t* expert_ids, void* out, int out_dtype, int64_t num_groups,
                                int64_t max_tokens_per_group, int64_t num_experts, int64_t T, int64_t N, int64_t K,
                                void* stream) {
+  return qlinear_nvfp4_grouped_gemm_scaled(w_packed, w_scale, x, a_offsets, expert_ids, nullptr, out, out_dtype,
+                                           num_groups, max_tokens_per_group, num_experts, T, N, K, stream);
+}
+
+int qlinear_nvfp4_grouped_gemm_scaled(const void* w_packed, const void* w_scale, const void* x,
+                                      const uint32_t* a_offsets, const int32_t* expert_ids, const float* expert_scale,
+                                      void* out, int out_dtype, int64_t num_groups, int64_t max_tokens_per_group,
+                                      int64_t num_experts, int64_t T, int64_t N, int64_t K, void* stream) {
   if (!w_packed || !w_scale || !x || !a_offsets || !expert_ids || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (expert_scale && !aligned(expert_scale, 4)) return QLINEAR_ERR_INVALID_ARG;
   if (num_groups <= 0 || num_groups > 65535 || max_tokens_per_group < 0 || num_experts <= 0 || T <= 0 ||
       N <= 0 || K <= 0 || K % 16 != 0)
     return QLINEAR_ERR_INVALID_ARG;
@@ -313,7 +367,7 @@ int qlinear_nvfp4_grouped_gemm(const void* w_packed, const void* w_scale, const 
   return finish(launch_nvfp4_grouped(static_cast<const uint8_t*>(w_packed), static_cast<const uint8_t*>(w_scale),
                                      static_cast<const uint16_t*>(x), a_offsets, expert_ids, out,
                                      out_dtype == QLINEAR_BF16, num_groups, max_tokens_per_group, num_experts, T,
-                                     N, K, num_cus, static_cast<hipStream_t>(stream)));
+                                     N, K, num_cus, static_cast<hipStream_t>(stream), expert_scale));
 }
 
 int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
@@ -376,6 +430,27 @@ int qlinear_bf16_gemm(const void* w, const void* x, void* out, int out_dtype, in
 int qlinear_bf16_gemm_path(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
                            float alpha, int path, void* stream) {
   return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream);
+}
+
+int qlinear_fp8_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
+                              int64_t K, float alpha, const qlinear_epilogue* epilogue, void* stream) {
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
+}
+
+int qlinear_fp8_gemm_epilogue_path(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
+                                   int64_t K, float alpha, const qlinear_epilogue* epilogue, int path, void* stream) {
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream, epilogue);
+}
+
+int qlinear_nvfp4_gemm_epilogue(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
+                                int64_t M, int64_t N, int64_t K, float alpha, const qlinear_epilogue* epilogue,
+                                void* stream) {
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
+}
+
+int qlinear_bf16_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
+                               int64_t K, float alpha, const qlinear_epilogue* epilogue, void* stream) {
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
 }
 
 }  // extern "C"
