@@ -36,6 +36,7 @@ __all__ = [
     "int8_quantize_act",
     "int8_accumulate",
     "int8_epilogue",
+    "int8_grouped",
     "fp8_quantize_act",
     "fp8_w8a8_linear",
     "bf16_linear",
@@ -94,8 +95,9 @@ def _grouped(linear_of_expert, e_count: int, n: int, x_bits, a_offsets, expert_i
     covers rows a_offsets[z] .. a_offsets[z+1]-1 (clipped to T; empty when the
     end does not exceed the start) and uses expert expert_ids[z]; an id outside
     0..E-1 writes zeros; rows no group covers stay NaN with written[r] = False.
-    linear_of_expert(e, x_rows) returns (ref, bound) for one expert."""
-    x = np.asarray(x_bits, dtype=np.uint16)
+    linear_of_expert(e, x_rows) returns (ref, bound) for one expert; x_rows
+    are rows start .. end-1 of x_bits, passed as stored."""
+    x = np.asarray(x_bits)
     offs = np.asarray(a_offsets).astype(np.int64)
     ids = np.asarray(expert_ids).astype(np.int64)
     t = x.shape[0]
@@ -259,6 +261,35 @@ def int8_epilogue(acc, a_scale, b_scale, bias_bits=None):
     ref = prod + bias[None, :]
     tau = 2.0 ** -22 * (np.abs(prod) + np.abs(bias)[None, :]) + 1e-6
     return ref, tau
+
+
+def int8_grouped(a_codes, b_codes, a_scale, b_scale, bias_bits, a_offsets, expert_ids, raw: bool = False):
+    """Grouped (MoE) W8A8 int8: the ``run_grouped`` addressing of the
+    Matmul2dFp8 page applied to the int8_matmul page's body.
+
+    Group z covers activation rows a_offsets[z] .. a_offsets[z+1]-1 (already
+    quantised per row: a_codes int8 [T, K], a_scale float32 [T]) and expert
+    e = expert_ids[z] (b_codes int8 [E, N, K], b_scale float32 [E, N], bias
+    bfloat16 bits [E, N] or None): acc = int8_accumulate, out = int8_epilogue
+    with that expert's b_scale and bias.  Group readings as fp8_grouped.
+    raw=True returns the exact accumulators instead (inactive rows 0).
+    Returns (ref [T, N], tau [T, N], written [T]); tau as int8_epilogue's
+    (0 for raw and for inactive rows).
+    """
+    a = np.asarray(a_codes, dtype=np.int8)
+    b = np.asarray(b_codes, dtype=np.int8)
+    a_s = np.asarray(a_scale, dtype=np.float32)
+    b_s = np.asarray(b_scale, dtype=np.float32)
+    e_count, n, _ = b.shape
+    bias = None if bias_bits is None else np.asarray(bias_bits, dtype=np.uint16)
+
+    def expert(e, rows):
+        acc = int8_accumulate(a[rows], b[e])
+        if raw:
+            return acc.astype(np.float64), np.zeros(acc.shape)
+        return int8_epilogue(acc, a_s[rows], b_s[e], None if bias is None else bias[e])
+
+    return _grouped(expert, e_count, n, np.arange(a.shape[0]), a_offsets, expert_ids)
 
 
 def fp8_quantize_act(x_bits, input_scale: float) -> np.ndarray:

@@ -461,3 +461,34 @@ def test_grouped_expert_scale_scales_each_experts_rows():
     assert np.array_equal(got[rows], raw[rows] * per_row[rows, None])
     assert np.array_equal(bgot[rows], braw[rows] * np.abs(per_row[rows, None]))
     assert np.all(got[3:7] == 0)
+
+
+def test_int8_grouped_python_integer_brute_force():
+    """Exact Python-integer accumulators per group and expert, the epilogue of
+    each row with its own a_scale and its expert's b_scale / bias, zeros for
+    an inactive group, untouched rows for uncovered ones."""
+    r = np.random.default_rng(92)
+    e, n, k, t = 3, 5, 33, 11
+    a = r.integers(-127, 128, size=(t, k), dtype=np.int8)
+    b = r.integers(-127, 128, size=(e, n, k), dtype=np.int8)
+    a_s = r.uniform(0.001, 0.1, t).astype(np.float32)
+    b_s = r.uniform(0.001, 0.1, (e, n)).astype(np.float32)
+    bias = synth.bf16_bits_from_f32(r.standard_normal((e, n)).astype(np.float32))
+    offs = np.array([1, 4, 4, 6, 10])          # row 0 and row 10 uncovered; group 1 empty
+    ids = np.array([2, 0, -1, 1])
+    acc, _, w_raw = R.int8_grouped(a, b, a_s, b_s, bias, offs, ids, raw=True)
+    ref, tau, written = R.int8_grouped(a, b, a_s, b_s, bias, offs, ids)
+    assert np.array_equal(w_raw, written)
+    assert list(np.flatnonzero(~written)) == [0, 10]
+    expert_of_row = {1: 2, 2: 2, 3: 2, 4: -1, 5: -1, 6: 1, 7: 1, 8: 1, 9: 1}
+    bias_v = F.bf16_bits_to_f64(bias)
+    for row, ex in expert_of_row.items():
+        for col in range(n):
+            if ex < 0:
+                assert acc[row, col] == 0 and ref[row, col] == 0 and tau[row, col] == 0
+                continue
+            want = sum(int(a[row, i]) * int(b[ex, col, i]) for i in range(k))
+            assert acc[row, col] == want
+            exact = Fraction(want) * Fraction(float(a_s[row])) * Fraction(float(b_s[ex, col])) + \
+                Fraction(float(bias_v[ex, col]))
+            assert abs(Fraction(float(ref[row, col])) - exact) <= Fraction(2.0 ** -40) * (abs(exact) + 1)
