@@ -17,7 +17,8 @@ fp32 out), "nvfp4" (W4A16 at M in {1, 128, 2048}, N = K = 4096), "grouped"
 K = 3072), "fp8_w8a8" (the same shapes with a static per-tensor E4M3
 activation quantiser and the fp8 GEMM), "bf16_decode" (the decode cases with
 a dense bf16 weight: the control that 1 vs 2 bytes per weight is measured
-against).  Where a workload's weights would fit the last-level cache, the
+against), "grouped_int8" (the grouped routing and shapes with int8 experts:
+per-token quantiser + grouped W8A8 GEMM).  Where a workload's weights would fit the last-level cache, the
 timed graph cycles through enough copies of them (>= 1 GiB) that every read
 comes from HBM.
 
@@ -412,6 +413,55 @@ def build_grouped_nvfp4(dev, q, synth, np, torch):
                 baseline=baseline)
 
 
+def build_grouped_int8(dev, q, synth, np, torch):
+    c = synth.grouped_int8_case()
+    e, n, k = c.b.shape
+    t = c.x.shape[0]
+    copies = 2  # two copies of the 201 MB expert stack alternate (no last-level-cache hits)
+    pb = [torch.from_numpy(c.b).to(dev) for _ in range(copies)]
+    sb = torch.from_numpy(c.b_scale).to(dev)
+    bias = bf16_dev(c.bias, dev, np, torch)
+    x = bf16_dev(c.x, dev, np, torch)
+    qa = torch.empty((t, k), dtype=torch.int8, device=dev)
+    sa = torch.empty((t,), dtype=torch.float32, device=dev)
+    offs = torch.from_numpy(c.a_offsets.astype(np.int32)).to(dev)
+    ids = torch.from_numpy(c.expert_ids.astype(np.int32)).to(dev)
+    out = torch.empty((t, n), dtype=torch.bfloat16, device=dev)
+    active = [z for z in range(e) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
+    rows_active = int(sum(int(c.a_offsets[z + 1]) - int(c.a_offsets[z]) for z in active))
+
+    def quant(copy):
+        q.int8_quantize_act(x, q=qa, a_scale=sa)
+
+    def run(copy):
+        q.int8_grouped_gemm(qa, pb[copy % copies], sa, sb, offs, ids, bias=bias, out=out,
+                            max_tokens_per_group=c.max_tokens)
+    cases = [Case("int8 quantize t=4096 k=2048", quant, t * k * 2 + t * k + t * 4, 0),
+             Case(c.name, run, len(active) * n * (k + 4 + 2) + t * (k + 4) + t * n * 2, 2 * rows_active * n * k,
+                  copies)]
+
+    def baseline():
+        from oracle import ref
+        gz = 8  # the first 8 groups, whole
+        rows = int(c.a_offsets[gz])
+        t0 = time.perf_counter()
+        a, a_s = ref.int8_quantize_act(c.x[:rows])
+        ref.int8_grouped(a, c.b, a_s, c.b_scale, c.bias, c.a_offsets[: gz + 1], c.expert_ids[:gz])
+        el = time.perf_counter() - t0
+        act = [z for z in range(gz) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
+        byts = len(act) * n * (k + 6) + rows * (k * 3 + 4 + n * 2)
+        return {"value": round(byts / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"groups 0-7 ({rows} tokens, {len(act)} active experts, quantiser + GEMM, {el:.1f} s)"}
+
+    return dict(metric="Grouped MoE W8A8 int8 achieved HBM GB/s (per-token quantiser + grouped GEMM)", unit="GB/s",
+                per="bytes", cases=cases, dominant=cases[1], bound="hbm", peak=HBM_PEAK_GBS,
+                kernel="int8_grouped_kernel<64, 128> (64 experts, N=1536, K=2048, 4096 tokens)", dtype="i32",
+                config={"workload": f"grouped_moe_w8a8_int8: E=64 [64,1536,2048] int8 + bf16 bias, T=4096 tokens "
+                                    f"quantised per row, Zipf(1.2) groups, {len(active)} active experts, "
+                                    f"{rows_active} active tokens"},
+                baseline=baseline)
+
+
 def build_int8(dev, q, synth, np, torch):
     m, k = 4096, 3072
     cases = []
@@ -503,7 +553,7 @@ def build_fp8_w8a8(dev, q, synth, np, torch):
 
 WORKLOADS = {"decode": build_decode, "gemv2048": build_gemv2048, "nvfp4": build_nvfp4,
              "grouped": build_grouped, "int8": build_int8, "grouped_nvfp4": build_grouped_nvfp4,
-             "fp8_w8a8": build_fp8_w8a8, "bf16_decode": build_bf16_decode}
+             "fp8_w8a8": build_fp8_w8a8, "bf16_decode": build_bf16_decode, "grouped_int8": build_grouped_int8}
 
 
 # ---------------------------------------------------------------- timing
@@ -556,7 +606,7 @@ def main():
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
                    "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
                    "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds_kernel",
-                   "bf16_decode": "bf16_gemv_wide_kernel"}
+                   "bf16_decode": "bf16_gemv_wide_kernel", "grouped_int8": "int8_grouped_kernel"}
         write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
         return
 

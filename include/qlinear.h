@@ -348,6 +348,31 @@ int qlinear_nvfp4_grouped_gemm_scaled(const void* w_packed, const void* w_scale,
                                       int64_t num_experts, int64_t T, int64_t N, int64_t K,
                                       void* stream);
 
+/*
+ * Grouped (MoE) W8A8 int8 matmul: the ragged addressing of page
+ * "Matmul2dFp8" (run_grouped) over the body of page "int8_matmul"
+ * ("Quantization (W8A8)"; Int8DequantWriter).  For every group z, rows r in
+ * [a_offsets[z], a_offsets[z+1]) and e = expert_ids[z]:
+ *     acc[r, n] = sum_k a[r, k] * b[e, n, k]                     (exact int32)
+ *     out[r, n] = acc[r, n] * a_scale[r] * b_scale[e, n] + bias[e, n]
+ * a: int8 [T, K] and a_scale: float32 [T] (qlinear_int8_quantize_act over the
+ * T rows); b: int8 [num_experts, N, K]; b_scale: float32 [num_experts, N];
+ * bias: bfloat16 [num_experts, N] or NULL; out: [T, N] of out_dtype (BF16,
+ * F32, or I32 for the raw accumulators, which ignores the scales and bias).
+ * a_offsets, expert_ids, num_groups, max_tokens_per_group, inactive / empty
+ * groups (zeros / nothing), untouched rows, preconditions and bounds
+ * behaviour: exactly as qlinear_fp8_grouped_gemm.  K <= 133144 (no int32
+ * overflow).  K % 64 == 0 with 16-byte aligned a and b runs the LDS-tiled
+ * matrix-core kernel; anything else a register-staged one.  Returns
+ * QLINEAR_ERR_INVALID_ARG for a null pointer, a non-positive size, a bad
+ * out_dtype or a misaligned pointer; nothing is written then.
+ */
+int qlinear_int8_grouped_gemm(const void* a, const void* b, const float* a_scale,
+                              const float* b_scale, const void* bias, const uint32_t* a_offsets,
+                              const int32_t* expert_ids, void* out, int out_dtype,
+                              int64_t num_groups, int64_t max_tokens_per_group,
+                              int64_t num_experts, int64_t T, int64_t N, int64_t K, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,8 @@ __all__ = [
     "grouped_nvfp4_case",
     "bf16_weight",
     "dyadic_bf16_weight",
+    "GroupedInt8Case",
+    "grouped_int8_case",
     "Fp8W8A8Case",
     "fp8_w8a8_case",
     "dyadic_e4m3_activation",
@@ -296,6 +298,18 @@ class GroupedNvfp4Case:
 
 
 @dataclass
+class GroupedInt8Case:
+    name: str
+    x: np.ndarray            # uint16 [T, K] bfloat16 bits (quantised per row by the kernel under test)
+    b: np.ndarray            # int8 [E, N, K]
+    b_scale: np.ndarray      # float32 [E, N]
+    bias: np.ndarray         # uint16 [E, N] bfloat16 bits
+    a_offsets: np.ndarray    # uint32 [G+1]
+    expert_ids: np.ndarray   # int32 [G]
+    max_tokens: int
+
+
+@dataclass
 class Fp8W8A8Case:
     name: str
     x: np.ndarray            # uint16 [M, K] bfloat16 bits
@@ -361,6 +375,18 @@ def grouped_nvfp4_case(num_experts: int = 64, n: int = 1536, k: int = 2048, toke
     return GroupedNvfp4Case(f"grouped_nvfp4_e{num_experts}_n{n}_k{k}_t{tokens}",
                             packed.reshape(num_experts, n, k // 2), sc.reshape(num_experts, n, k // 16), x,
                             offs, ids, int(counts.max()), float(g))
+
+
+def grouped_int8_case(num_experts: int = 64, n: int = 1536, k: int = 2048, tokens: int = 4096) -> GroupedInt8Case:
+    """Grouped MoE W8A8: the grouped workload's routing and shapes with int8
+    experts (per-output-channel absmax / 127 scales of N(0, 0.02^2)), a bf16
+    bias per expert and the W8A8 activation recipe (1% x20 outliers)."""
+    b, b_scale = int8_weight((8, 0, 0), num_experts * n, k)
+    bias = bf16_bias((8, 0, 2), num_experts * n)
+    x = bf16_activation((8, 0, 1), tokens, k, outlier_p=0.01)
+    offs, ids, counts = grouped_routing((4, 0), num_experts, tokens)
+    return GroupedInt8Case(f"grouped_int8_e{num_experts}_n{n}_k{k}_t{tokens}", x, b.reshape(num_experts, n, k),
+                           b_scale.reshape(num_experts, n), bias.reshape(num_experts, n), offs, ids, int(counts.max()))
 
 
 def fp8_w8a8_case(n: int, m: int = 4096, k: int = 3072) -> Fp8W8A8Case:

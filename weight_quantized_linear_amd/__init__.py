@@ -29,6 +29,7 @@ __all__ = [
     "fp8_materialize",
     "fp8_grouped_gemm",
     "nvfp4_grouped_gemm",
+    "int8_grouped_gemm",
     "fp8_quantize_act",
     "fp8_w8a8_gemm",
     "nvfp4_gemm",
@@ -81,6 +82,7 @@ EXPORTED = {
     "qlinear_bf16_gemm_epilogue": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _p],
     "qlinear_fp8_grouped_gemm_scaled": [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_nvfp4_grouped_gemm_scaled": [_p, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
+    "qlinear_int8_grouped_gemm": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
 }
 
 
@@ -475,3 +477,51 @@ def int8_gemm(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tensor | None, b_
                                m, n, k, _stream(a))
     _check(st, "qlinear_int8_gemm")
     return out
+
+
+def int8_grouped_gemm(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tensor | None, b_scale: torch.Tensor | None,
+                      a_offsets: torch.Tensor, expert_ids: torch.Tensor, bias: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                      max_tokens_per_group: int | None = None) -> torch.Tensor:
+    """Grouped MoE W8A8 (``qlinear_int8_grouped_gemm``): rows a_offsets[z] ..
+    a_offsets[z+1]-1 of the int8 activation a [T, K] times b[expert_ids[z]] [N, K]^T,
+    dequantised by a_scale[r] * b_scale[e, n] + bias[e, n] (out_dtype bf16 / f32) or
+    raw int32 accumulators (out_dtype int32).  Rows outside every group keep whatever
+    ``out`` held (a new ``out`` starts uninitialised)."""
+    codes = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}
+    if out_dtype not in codes:
+        raise ValueError("out_dtype must be bfloat16, float32 or int32")
+    for t, name in ((a, "a"), (b, "b"), (a_offsets, "a_offsets"), (expert_ids, "expert_ids")):
+        _require(t, name)
+    if a.dtype != torch.int8 or b.dtype != torch.int8:
+        raise TypeError("a and b must be int8")
+    if a_offsets.dtype not in (torch.int32, torch.uint32) or expert_ids.dtype != torch.int32:
+        raise TypeError("a_offsets must be uint32/int32 and expert_ids int32")
+    if b.dim() != 3 or a.dim() != 2 or a.shape[1] != b.shape[2]:
+        raise ValueError("b must be [E, N, K] and a [T, K]")
+    e, n, k = b.shape
+    t = a.shape[0]
+    g = expert_ids.numel()
+    if a_offsets.numel() != g + 1:
+        raise ValueError("a_offsets needs num_groups + 1 entries")
+    if out_dtype != torch.int32:
+        if a_scale is None or b_scale is None:
+            raise ValueError("a_scale and b_scale are needed for a dequantised output")
+        for s_, name, size in ((a_scale, "a_scale", t), (b_scale, "b_scale", e * n)):
+            _require(s_, name)
+            if s_.dtype != torch.float32 or s_.numel() != size:
+                raise ValueError(f"{name} must be float32 with {size} elements")
+        if bias is not None:
+            _require(bias, "bias")
+            if bias.dtype != torch.bfloat16 or bias.numel() != e * n:
+                raise ValueError(f"bias must be bfloat16 with {e * n} elements")
+    if max_tokens_per_group is None:
+        max_tokens_per_group = t
+    out = _out(out, (t, n), out_dtype, a.device)
+    opt = lambda x: None if x is None else _ptr(x)  # noqa: E731
+    st = lib.qlinear_int8_grouped_gemm(_ptr(a), _ptr(b), opt(a_scale), opt(b_scale), opt(bias), _ptr(a_offsets),
+                                       _ptr(expert_ids), _ptr(out), codes[out_dtype], g, int(max_tokens_per_group),
+                                       e, t, n, k, _stream(a))
+    _check(st, "qlinear_int8_grouped_gemm")
+    return out
+

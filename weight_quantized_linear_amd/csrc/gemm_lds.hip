@@ -917,21 +917,17 @@ struct I8Layout {
 };
 
 // OUT: 0 = float32, 1 = bfloat16 (dequantised), 2 = raw int32 accumulators.
+// One BM x BN output tile at (m0, n0) of out[M, N]: a [M, K], b [N, K],
+// a_scale [M], b_scale [N], bias [N] or null.  Every thread of the block
+// calls it; the LDS ring starts at `lds`.
 template <int BM, int BN, int S, int WY, int NW, int OUT>
-__global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __restrict__ a,
-                                                                 const int8_t* __restrict__ b,
-                                                                 const float* __restrict__ a_scale,
-                                                                 const float* __restrict__ b_scale,
-                                                                 const uint16_t* __restrict__ bias,
-                                                                 void* __restrict__ out, int64_t M, int64_t N,
-                                                                 int64_t K, int vec) {
+__device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ a, const int8_t* __restrict__ b,
+                                          const float* __restrict__ a_scale, const float* __restrict__ b_scale,
+                                          const uint16_t* __restrict__ bias, void* __restrict__ out, int64_t M,
+                                          int64_t N, int64_t K, int vec, int64_t m0, int64_t n0) {
   using L = I8Layout<BM, BN, S, WY, NW>;
   constexpr int FM = L::FM, FN = L::FN;
   constexpr int NM = FM * FN;  // MFMAs per step
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  int64_t tm, tn;
-  tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wy = wid / L::WX, wx = wid % L::WX;
   const int r = lane & 31, h = lane >> 5;
@@ -1091,6 +1087,104 @@ __global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __
           }
         }
       }
+  }
+}
+
+template <int BM, int BN, int S, int WY, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __restrict__ a,
+                                                                 const int8_t* __restrict__ b,
+                                                                 const float* __restrict__ a_scale,
+                                                                 const float* __restrict__ b_scale,
+                                                                 const uint16_t* __restrict__ bias,
+                                                                 void* __restrict__ out, int64_t M, int64_t N,
+                                                                 int64_t K, int vec) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t tm, tn;
+  tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  int8_tile<BM, BN, S, WY, NW, OUT>(lds, a, b, a_scale, b_scale, bias, out, M, N, K, vec, tm * BM, tn * BN);
+}
+
+// Grouped MoE W8A8: the ragged walk of grouped_gemm_kernel (prefix sum of
+// the groups' row tiles in LDS after the strip ring, one contiguous range
+// of (row tile, column tile) pairs per XCD) over int8 tiles.  Group z uses
+// rows a_offsets[z] .. (clipped to T) of a / a_scale and expert
+// e = expert_ids[z] of b [E, N, K], b_scale [E, N] and bias [E, N]; an id
+// outside 0 .. E - 1 writes zeros.
+template <int BM, int BN, int S, int WY, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void int8_grouped_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, const float* __restrict__ a_scale,
+    const float* __restrict__ b_scale, const uint16_t* __restrict__ bias, const uint32_t* __restrict__ a_offsets,
+    const int32_t* __restrict__ expert_ids, void* __restrict__ out, int64_t G, int64_t T, int64_t N, int64_t K,
+    int64_t E, int vec) {
+  using L = I8Layout<BM, BN, S, WY, NW>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int kEs = OUT == 1 ? 2 : 4;
+  int* cum = reinterpret_cast<int*>(lds + L::kLds);  // cum[z] = row tiles of groups 0 .. z-1; cum[G] = total
+  auto group_span = [&](int64_t z, int64_t& start, int64_t& rows) {
+    int64_t lo = a_offsets[z], hi = a_offsets[z + 1];
+    lo = lo < T ? lo : T;
+    hi = hi < T ? hi : T;
+    start = lo;
+    rows = hi > lo ? hi - lo : 0;
+  };
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int64_t z0 = 0; z0 <= G; z0 += 64) {
+      const int64_t z = z0 + lane;
+      int t = 0;
+      if (z < G) {
+        int64_t st, rows;
+        group_span(z, st, rows);
+        t = int((rows + BM - 1) / BM);
+      }
+      int incl = t;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      if (z <= G) cum[z] = carry + incl - t;
+      carry += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  const int64_t n_tiles = (N + BN - 1) / BN;
+  const int64_t work = int64_t(cum[G]) * n_tiles;
+  constexpr int kXcd = 8;  // gridDim.x is a multiple of 8
+  const int64_t xcd = blockIdx.x % kXcd, per_xcd = gridDim.x / kXcd;
+  const int64_t w_lo = xcd * work / kXcd, w_hi = (xcd + 1) * work / kXcd;
+  bool first = true;
+  for (int64_t wi = w_lo + blockIdx.x / kXcd; wi < w_hi; wi += per_xcd) {
+    const int mt = int(wi / n_tiles);
+    const int64_t n0 = (wi % n_tiles) * BN;
+    int64_t lo = 0, hi = G;  // cum[lo] <= mt < cum[hi]
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (cum[mid] <= mt) lo = mid;
+      else hi = mid;
+    }
+    const int64_t z = lo;
+    int64_t start, rows;
+    group_span(z, start, rows);
+    const int64_t m0 = int64_t(mt - cum[z]) * BM;
+    const int64_t e = expert_ids[z];
+    char* gout = static_cast<char*>(out) + start * N * kEs;
+    if (e < 0 || e >= E) {
+      for (int idx = threadIdx.x; idx < BM * BN; idx += 64 * NW) {
+        const int64_t m = m0 + idx / BN, n = n0 + idx % BN;
+        if (m < rows && n < N) {
+          if constexpr (OUT == 2) reinterpret_cast<int32_t*>(gout)[m * N + n] = 0;
+          else put_out<OUT>(gout, m * N + n, 0.f);
+        }
+      }
+      continue;
+    }
+    if (!first) __syncthreads();  // the previous tile's LDS use is over for every wave
+    first = false;
+    int8_tile<BM, BN, S, WY, NW, OUT>(lds, a + start * K, b + e * N * K, a_scale ? a_scale + start : nullptr,
+                                      b_scale ? b_scale + e * N : nullptr,
+                                      bias ? bias + e * N : nullptr, gout, rows, N, K, vec, m0, n0);
   }
 }
 
@@ -1429,6 +1523,55 @@ hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* s
   if (tiles(M, N, 256, 128) >= num_cus / 2)
     return launch_int8_cfg<256, 128, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
   return launch_int8_cfg<128, 128, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+}
+
+namespace {
+
+template <int BM, int BN, int S, int WY, int NW>
+hipError_t launch_int8_grouped_cfg(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
+                                   const uint16_t* bias, const uint32_t* a_offsets, const int32_t* expert_ids,
+                                   void* out, int out_mode, int64_t G, int64_t E, int64_t T, int64_t N, int64_t K,
+                                   int num_cus, hipStream_t s) {
+  using L = I8Layout<BM, BN, S, WY, NW>;
+  const int lds_bytes = int(L::kLds + 4 * (G + 1));
+  if (lds_bytes > kMaxLds) return hipErrorInvalidValue;
+  const int64_t upper = ((T + BM - 1) / BM + G) * ((N + BN - 1) / BN);
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kMaxLds / lds_bytes, 16 / NW));
+  const int64_t want = upper < per_cu * num_cus ? upper : per_cu * num_cus;
+  const int64_t blocks = (want + 7) / 8 * 8;
+  const int es = out_mode == 1 ? 2 : 4;
+  const int vec = aligned16(out) && (N * es) % 16 == 0;
+  auto go = [&](auto kernel) -> hipError_t {
+    static bool attr = false;
+    if (!attr) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, a, b, sa, sb, bias, a_offsets, expert_ids, out,
+                  G, T, N, K, E, vec);
+  };
+  if (out_mode == 1) return go(int8_grouped_kernel<BM, BN, S, WY, NW, 1>);
+  if (out_mode == 2) return go(int8_grouped_kernel<BM, BN, S, WY, NW, 2>);
+  return go(int8_grouped_kernel<BM, BN, S, WY, NW, 0>);
+}
+
+}  // namespace
+
+bool int8_grouped_lds_supported(const void* a, const void* b, int64_t G, int64_t T, int64_t N, int64_t K) {
+  return K >= 64 && K % 64 == 0 && aligned16(a) && aligned16(b) && T * K < (int64_t(1) << 32) &&
+         N * K < (int64_t(1) << 32) && G <= 8192;
+}
+
+hipError_t launch_int8_grouped_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
+                                   const uint16_t* bias, const uint32_t* a_offsets, const int32_t* expert_ids,
+                                   void* out, int out_mode, int64_t G, int64_t E, int64_t T, int64_t N, int64_t K,
+                                   int num_cus, hipStream_t s) {
+  // The grouped W8A16 tile shape: 64 rows (groups average ~64 tokens), 128
+  // columns, four waves side by side.
+  return launch_int8_grouped_cfg<64, 128, 4, 1, 4>(a, b, sa, sb, bias, a_offsets, expert_ids, out, out_mode, G, E, T,
+                                                   N, K, num_cus, s);
 }
 
 }  // namespace qlinear

@@ -184,19 +184,15 @@ __device__ __forceinline__ void i8_tile_of_block(int64_t b, int64_t tiles_m, int
   tn = in_group / gm;
 }
 
-// out_mode: 0 = float32, 1 = bfloat16 (both dequantised), 2 = raw int32 accumulators.
-__global__ __launch_bounds__(kThreads) void int8_gemm_kernel(I8Operand A, I8Operand B,
-                                                             const float* __restrict__ a_scale,
-                                                             const float* __restrict__ b_scale,
-                                                             const uint16_t* __restrict__ bias,
-                                                             void* __restrict__ out, int out_mode) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsTile];
+// The 128 x 128 tile at (m0, n0) of out[M, N] (M = A.rows, N = B.rows).
+// out_mode: 0 = float32, 1 = bfloat16 (both dequantised), 2 = raw int32
+// accumulators.  Every thread of the block calls it.
+__device__ void int8_dense_tile(char* lds, const I8Operand& A, const I8Operand& B, const float* __restrict__ a_scale,
+                                const float* __restrict__ b_scale, const uint16_t* __restrict__ bias,
+                                void* __restrict__ out, int out_mode, int64_t m0, int64_t n0) {
   char* lds_a = lds;
   char* lds_b = lds + kLdsTile;
   const int64_t M = A.rows, N = B.rows;
-  int64_t tm, tn;
-  i8_tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
@@ -271,6 +267,55 @@ __global__ __launch_bounds__(kThreads) void int8_gemm_kernel(I8Operand A, I8Oper
     }
 }
 
+__global__ __launch_bounds__(kThreads) void int8_gemm_kernel(I8Operand A, I8Operand B,
+                                                             const float* __restrict__ a_scale,
+                                                             const float* __restrict__ b_scale,
+                                                             const uint16_t* __restrict__ bias,
+                                                             void* __restrict__ out, int out_mode) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsTile];
+  int64_t tm, tn;
+  i8_tile_of_block(blockIdx.x, (A.rows + BM - 1) / BM, (B.rows + BN - 1) / BN, tm, tn);
+  int8_dense_tile(lds, A, B, a_scale, b_scale, bias, out, out_mode, tm * BM, tn * BN);
+}
+
+// Grouped W8A8 for any K and alignment: group z = blockIdx.z covers rows
+// a_offsets[z] .. a_offsets[z+1]-1 (clipped to T) with expert expert_ids[z];
+// blockIdx.x is the column tile and the group's row tiles are taken
+// blockIdx.y, + gridDim.y, ...  An id outside 0 .. E-1 writes zeros.
+__global__ __launch_bounds__(kThreads) void int8_grouped_any_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, const float* __restrict__ a_scale,
+    const float* __restrict__ b_scale, const uint16_t* __restrict__ bias, const uint32_t* __restrict__ a_offsets,
+    const int32_t* __restrict__ expert_ids, void* __restrict__ out, int out_mode, int64_t T, int64_t N, int64_t K,
+    int64_t E, bool vec) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsTile];
+  const int64_t z = blockIdx.z;
+  int64_t start = a_offsets[z], end = a_offsets[z + 1];
+  start = start < T ? start : T;
+  end = end < T ? end : T;
+  if (end <= start) return;
+  const int64_t rows = end - start;
+  const int64_t e = expert_ids[z];
+  const int64_t n0 = int64_t(blockIdx.x) * BN;
+  const int es = out_mode == 1 ? 2 : 4;
+  char* gout = static_cast<char*>(out) + start * N * es;
+  for (int64_t mt = blockIdx.y; mt * BM < rows; mt += gridDim.y) {
+    const int64_t m0 = mt * BM;
+    if (e < 0 || e >= E) {
+      for (int idx = threadIdx.x; idx < BM * BN; idx += kThreads) {
+        const int64_t m = m0 + idx / BN, n = n0 + idx % BN;
+        if (m >= rows || n >= N) continue;
+        if (out_mode == 2) reinterpret_cast<int32_t*>(gout)[m * N + n] = 0;
+        else if (out_mode == 1) reinterpret_cast<uint16_t*>(gout)[m * N + n] = 0;
+        else reinterpret_cast<float*>(gout)[m * N + n] = 0.f;
+      }
+      continue;
+    }
+    const I8Operand A{a + start * K, rows, K, vec}, B{b + e * N * K, N, K, vec};
+    int8_dense_tile(lds, A, B, a_scale ? a_scale + start : nullptr, b_scale ? b_scale + e * N : nullptr, bias ? bias + e * N : nullptr,
+                    gout, out_mode, m0, n0);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_int8_quantize(const uint16_t* x, int8_t* q, float* a_scale, int64_t M, int64_t K,
@@ -293,6 +338,23 @@ hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, const float* a_sca
   const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   return launch(int8_gemm_kernel, dim3(blocks), dim3(kThreads), 0, s, A, B, a_scale, b_scale, bias, out,
                 out_mode);
+}
+
+hipError_t launch_int8_grouped(const int8_t* a, const int8_t* b, const float* a_scale, const float* b_scale,
+                               const uint16_t* bias, const uint32_t* a_offsets, const int32_t* expert_ids, void* out,
+                               int out_mode, int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
+                               int num_cus, hipStream_t s) {
+  if (int8_grouped_lds_supported(a, b, G, T, N, K))
+    return launch_int8_grouped_lds(a, b, a_scale, b_scale, bias, a_offsets, expert_ids, out, out_mode, G, E, T, N, K,
+                                   num_cus, s);
+  // vec needs every expert's rows 16-byte aligned: K % 16 == 0 and aligned bases.
+  const bool vec = (K % 16 == 0) && (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(b) % 16 == 0);
+  int64_t tiles_m = (max_tokens + BM - 1) / BM;
+  if (tiles_m < 1) tiles_m = 1;
+  if (tiles_m > 65535) tiles_m = 65535;
+  return launch(int8_grouped_any_kernel, dim3((N + BN - 1) / BN, tiles_m, G), dim3(kThreads), 0, s, a, b, a_scale,
+                b_scale, bias, a_offsets, expert_ids, out, out_mode, T, N, K, E, vec);
 }
 
 }  // namespace qlinear

@@ -105,6 +105,15 @@ hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, vo
 // int8.hip
 hipError_t launch_int8_quantize(const uint16_t* x, int8_t* q, float* a_scale, int64_t M, int64_t K,
                                 hipStream_t s);
+bool int8_grouped_lds_supported(const void* a, const void* b, int64_t G, int64_t T, int64_t N, int64_t K);
+hipError_t launch_int8_grouped_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
+                                   const uint16_t* bias, const uint32_t* a_offsets, const int32_t* expert_ids,
+                                   void* out, int out_mode, int64_t G, int64_t E, int64_t T, int64_t N, int64_t K,
+                                   int num_cus, hipStream_t s);
+hipError_t launch_int8_grouped(const int8_t* a, const int8_t* b, const float* a_scale, const float* b_scale,
+                               const uint16_t* bias, const uint32_t* a_offsets, const int32_t* expert_ids, void* out,
+                               int out_mode, int64_t G, int64_t max_tokens, int64_t E, int64_t T, int64_t N, int64_t K,
+                               int num_cus, hipStream_t s);
 hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, const float* a_scale, const float* b_scale,
                             const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
                             int num_cus, hipStream_t s);

@@ -453,4 +453,32 @@ int qlinear_bf16_gemm_epilogue(const void* w, const void* x, void* out, int out_
   return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
 }
 
+int qlinear_int8_grouped_gemm(const void* a, const void* b, const float* a_scale, const float* b_scale,
+                              const void* bias, const uint32_t* a_offsets, const int32_t* expert_ids, void* out,
+                              int out_dtype, int64_t num_groups, int64_t max_tokens_per_group, int64_t num_experts,
+                              int64_t T, int64_t N, int64_t K, void* stream) {
+  if (!a || !b || !a_offsets || !expert_ids || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (num_groups <= 0 || num_groups > 65535 || max_tokens_per_group < 0 || num_experts <= 0 || T <= 0 ||
+      N <= 0 || K <= 0 || K > 133144)
+    return QLINEAR_ERR_INVALID_ARG;
+  if (!fits(num_experts, N, K) || !fits(T, K) || !fits(T, N)) return QLINEAR_ERR_INVALID_ARG;
+  int mode;
+  if (out_dtype == QLINEAR_F32) mode = 0;
+  else if (out_dtype == QLINEAR_BF16) mode = 1;
+  else if (out_dtype == QLINEAR_I32) mode = 2;
+  else return QLINEAR_ERR_INVALID_ARG;
+  if (mode != 2 && (!a_scale || !b_scale || !aligned(a_scale, 4) || !aligned(b_scale, 4)))
+    return QLINEAR_ERR_INVALID_ARG;
+  if (mode != 2 && bias && !aligned(bias, 2)) return QLINEAR_ERR_INVALID_ARG;
+  if (!aligned(out, mode == 1 ? 2 : 4) || !aligned(a_offsets, 4) || !aligned(expert_ids, 4))
+    return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  return finish(launch_int8_grouped(static_cast<const int8_t*>(a), static_cast<const int8_t*>(b),
+                                    mode == 2 ? nullptr : a_scale, mode == 2 ? nullptr : b_scale,
+                                    mode == 2 ? nullptr : static_cast<const uint16_t*>(bias), a_offsets, expert_ids,
+                                    out, mode, num_groups, max_tokens_per_group, num_experts, T, N, K, num_cus,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
