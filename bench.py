@@ -167,6 +167,21 @@ def bf16_dev(bits, dev, np, torch):
 
 # ---------------------------------------------------------------- workloads
 
+BASELINE_SECONDS = 10.0
+
+
+def repeat_until(seconds, fn):
+    """Call fn() until `seconds` have elapsed (at least once): (passes, elapsed s)."""
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        fn()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return passes, el
+
+
 def build_decode(dev, q, synth, np, torch):
     shapes = ((4096, 4096), (14336, 4096), (4096, 14336), (128256, 4096))
     ms = (1, 4, 16)
@@ -191,18 +206,19 @@ def build_decode(dev, q, synth, np, torch):
 
     def baseline():
         from oracle import ref
-        total, elapsed = 0, 0.0
-        for m in ms:
-            for si, (n, k) in enumerate(shapes):
-                x = synth.bf16_activation((2, si, 1, m), m, k)
-                t0 = time.perf_counter()
-                ref.fp8_linear(heads[si], x, scales[si])
-                elapsed += time.perf_counter() - t0
-                rows = heads[si].shape[0]
-                total += rows * k + m * k * 2 + m * rows * 2
+        xs = {(m, si): synth.bf16_activation((2, si, 1, m), m, k) for m in ms for si, (n, k) in enumerate(shapes)}
+        per_pass = sum(heads[si].shape[0] * k + m * k * 2 + m * heads[si].shape[0] * 2
+                       for m in ms for si, (n, k) in enumerate(shapes))
+
+        def one_pass():
+            for m in ms:
+                for si in range(len(shapes)):
+                    ref.fp8_linear(heads[si], xs[(m, si)], scales[si])
+        passes, elapsed = repeat_until(BASELINE_SECONDS, one_pass)
+        total = passes * per_pass
         return {"value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
                 "sample": f"first 12288 weight rows (all 4096 where N = 4096) of each of the 12 (M, N, K) cases, "
-                          f"full K ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
+                          f"full K, {passes} pass(es) ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
 
     return dict(
         metric="FP8 W8A16 GEMV M=1 achieved HBM GB/s; dequant-GEMM TFLOP/s; % of roofline",
@@ -239,18 +255,19 @@ def build_bf16_decode(dev, q, synth, np, torch):
 
     def baseline():
         from oracle import ref
-        total, elapsed = 0, 0.0
-        for m in ms:
-            for si, (n, k) in enumerate(shapes):
-                x = synth.bf16_activation((2, si, 1, m), m, k)
-                t0 = time.perf_counter()
-                ref.bf16_linear(heads[si], x)
-                elapsed += time.perf_counter() - t0
-                rows = heads[si].shape[0]
-                total += rows * k * 2 + m * k * 2 + m * rows * 2
+        xs = {(m, si): synth.bf16_activation((2, si, 1, m), m, k) for m in ms for si, (n, k) in enumerate(shapes)}
+        per_pass = sum(heads[si].shape[0] * k * 2 + m * k * 2 + m * heads[si].shape[0] * 2
+                       for m in ms for si, (n, k) in enumerate(shapes))
+
+        def one_pass():
+            for m in ms:
+                for si in range(len(shapes)):
+                    ref.bf16_linear(heads[si], xs[(m, si)])
+        passes, elapsed = repeat_until(BASELINE_SECONDS, one_pass)
+        total = passes * per_pass
         return {"value": round(total / elapsed / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
                 "sample": f"first 12288 weight rows (all 4096 where N = 4096) of each of the 12 (M, N, K) cases, "
-                          f"full K ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
+                          f"full K, {passes} pass(es) ({total / 1e6:.1f} MB of algorithmic traffic, {elapsed:.1f} s)"}
 
     return dict(
         metric="Dense bf16 control: GEMV M=1 achieved HBM GB/s (decode shapes, 2-byte weights)",
@@ -279,13 +296,10 @@ def build_gemv2048(dev, q, synth, np, torch):
 
     def baseline():
         from oracle import ref
-        t0 = time.perf_counter()
-        reps = 0
-        while time.perf_counter() - t0 < 10:
+        def one_pass():
             for c in raw:
                 ref.fp8_linear(c.w, c.x)
-            reps += 1
-        el = time.perf_counter() - t0
+        reps, el = repeat_until(BASELINE_SECONDS, one_pass)
         b = reps * sum(cc.bytes for cc in cases)
         return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
                 "sample": f"{reps} passes over both cases ({el:.1f} s)"}
@@ -315,14 +329,15 @@ def build_nvfp4(dev, q, synth, np, torch):
     def baseline():
         from oracle import ref
         rows = 512
-        t0 = time.perf_counter()
-        for m in (1, 128, 2048):
-            x = synth.bf16_activation((3, 0, 1, m), m, k)
-            ref.nvfp4_linear(packed[:rows], sc[:rows], x, float(g))
-        el = time.perf_counter() - t0
-        fl = sum(2 * m * rows * k for m in (1, 128, 2048))
+        xs = [synth.bf16_activation((3, 0, 1, m), m, k) for m in (1, 128, 2048)]
+
+        def one_pass():
+            for x in xs:
+                ref.nvfp4_linear(packed[:rows], sc[:rows], x, float(g))
+        passes, el = repeat_until(BASELINE_SECONDS, one_pass)
+        fl = passes * sum(2 * m * rows * k for m in (1, 128, 2048))
         return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"first {rows} weight rows for M in (1, 128, 2048), full K ({el:.1f} s)"}
+                "sample": f"first {rows} weight rows for M in (1, 128, 2048), full K, {passes} passes ({el:.1f} s)"}
 
     return dict(metric="W4A16 NVFP4 dequant-GEMM TFLOP/s", unit="TFLOP/s", per="work", cases=cases,
                 dominant=cases[2], bound="mfma", peak=BF16_PEAK_TFLOPS,
@@ -354,13 +369,13 @@ def build_grouped(dev, q, synth, np, torch):
     def baseline():
         from oracle import ref
         gz = 8  # the first 8 groups, whole
-        t0 = time.perf_counter()
-        ref.fp8_grouped(c.w, c.x[: int(c.a_offsets[gz])], c.a_offsets[: gz + 1], c.expert_ids[:gz])
-        el = time.perf_counter() - t0
+        passes, el = repeat_until(BASELINE_SECONDS, lambda: ref.fp8_grouped(
+            c.w, c.x[: int(c.a_offsets[gz])], c.a_offsets[: gz + 1], c.expert_ids[:gz]))
         act = [z for z in range(gz) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
-        b = len(act) * n * k + int(c.a_offsets[gz]) * (k + n) * 2
+        b = passes * (len(act) * n * k + int(c.a_offsets[gz]) * (k + n) * 2)
         return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"groups 0-7 ({int(c.a_offsets[gz])} tokens, {len(act)} active experts, {el:.1f} s)"}
+                "sample": f"groups 0-7 ({int(c.a_offsets[gz])} tokens, {len(act)} active experts), {passes} passes "
+                          f"({el:.1f} s)"}
 
     return dict(metric="Grouped MoE W8A16 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
                 dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS,
@@ -396,13 +411,13 @@ def build_grouped_nvfp4(dev, q, synth, np, torch):
     def baseline():
         from oracle import ref
         gz = 8  # the first 8 groups, whole
-        t0 = time.perf_counter()
-        ref.nvfp4_grouped(c.packed, c.scales, c.x[: int(c.a_offsets[gz])], c.a_offsets[: gz + 1], c.expert_ids[:gz])
-        el = time.perf_counter() - t0
+        passes, el = repeat_until(BASELINE_SECONDS, lambda: ref.nvfp4_grouped(
+            c.packed, c.scales, c.x[: int(c.a_offsets[gz])], c.a_offsets[: gz + 1], c.expert_ids[:gz]))
         act = [z for z in range(gz) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
-        b = len(act) * n * (k // 2 + k // 16) + int(c.a_offsets[gz]) * (k + n) * 2
+        b = passes * (len(act) * n * (k // 2 + k // 16) + int(c.a_offsets[gz]) * (k + n) * 2)
         return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"groups 0-7 ({int(c.a_offsets[gz])} tokens, {len(act)} active experts, {el:.1f} s)"}
+                "sample": f"groups 0-7 ({int(c.a_offsets[gz])} tokens, {len(act)} active experts), {passes} passes "
+                          f"({el:.1f} s)"}
 
     return dict(metric="Grouped MoE W4A16 NVFP4 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
                 dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS,
@@ -444,14 +459,16 @@ def build_grouped_int8(dev, q, synth, np, torch):
         from oracle import ref
         gz = 8  # the first 8 groups, whole
         rows = int(c.a_offsets[gz])
-        t0 = time.perf_counter()
-        a, a_s = ref.int8_quantize_act(c.x[:rows])
-        ref.int8_grouped(a, c.b, a_s, c.b_scale, c.bias, c.a_offsets[: gz + 1], c.expert_ids[:gz])
-        el = time.perf_counter() - t0
+
+        def one_pass():
+            a, a_s = ref.int8_quantize_act(c.x[:rows])
+            ref.int8_grouped(a, c.b, a_s, c.b_scale, c.bias, c.a_offsets[: gz + 1], c.expert_ids[:gz])
+        passes, el = repeat_until(BASELINE_SECONDS, one_pass)
         act = [z for z in range(gz) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
-        byts = len(act) * n * (k + 6) + rows * (k * 3 + 4 + n * 2)
+        byts = passes * (len(act) * n * (k + 6) + rows * (k * 3 + 4 + n * 2))
         return {"value": round(byts / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"groups 0-7 ({rows} tokens, {len(act)} active experts, quantiser + GEMM, {el:.1f} s)"}
+                "sample": f"groups 0-7 ({rows} tokens, {len(act)} active experts, quantiser + GEMM), {passes} passes "
+                          f"({el:.1f} s)"}
 
     return dict(metric="Grouped MoE W8A8 int8 achieved HBM GB/s (per-token quantiser + grouped GEMM)", unit="GB/s",
                 per="bytes", cases=cases, dominant=cases[1], bound="hbm", peak=HBM_PEAK_GBS,
@@ -489,17 +506,18 @@ def build_int8(dev, q, synth, np, torch):
     def baseline():
         from oracle import ref
         rows = 256
-        t0 = time.perf_counter()
-        qx, sx = ref.int8_quantize_act(c0.x)
-        ops = 0
-        for n in (3072, 12288):
-            c = synth.config5_case(n)
-            acc = ref.int8_accumulate(qx[:rows], c.b)
-            ref.int8_epilogue(acc, sx[:rows], c.b_scale, c.bias)
-            ops += 2 * rows * n * k
-        el = time.perf_counter() - t0
+        cs = [synth.config5_case(n) for n in (3072, 12288)]
+
+        def one_pass():
+            qx, sx = ref.int8_quantize_act(c0.x)
+            for c in cs:
+                acc = ref.int8_accumulate(qx[:rows], c.b)
+                ref.int8_epilogue(acc, sx[:rows], c.b_scale, c.bias)
+        passes, el = repeat_until(BASELINE_SECONDS, one_pass)
+        ops = passes * sum(2 * rows * c.b.shape[0] * k for c in cs)
         return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"quantiser on all 4096 rows + GEMM on the first {rows} rows for both N ({el:.1f} s)"}
+                "sample": f"quantiser on all 4096 rows + GEMM on the first {rows} rows for both N, {passes} passes "
+                          f"({el:.1f} s)"}
 
     return dict(metric="W8A8 int8 GEMM TOPS (quantiser + GEMM + dequant epilogue)", unit="TOPS", per="work",
                 cases=cases, dominant=cases[2], bound="mfma", peak=INT8_PEAK_TOPS,
@@ -532,20 +550,21 @@ def build_fp8_w8a8(dev, q, synth, np, torch):
     def baseline():
         from oracle import ref
         rows = 256
-        t0 = time.perf_counter()
-        qx = ref.fp8_quantize_act(c0.x, c0.input_scale)
-        flops = 0
-        for n in (3072, 12288):
-            c = synth.fp8_w8a8_case(n)
-            ref.fp8_w8a8_linear(qx[:rows], c.w, c0.input_scale * c.weight_scale)
-            flops += 2 * rows * n * k
-        el = time.perf_counter() - t0
+        cs = [synth.fp8_w8a8_case(n) for n in (3072, 12288)]
+
+        def one_pass():
+            qx = ref.fp8_quantize_act(c0.x, c0.input_scale)
+            for c in cs:
+                ref.fp8_w8a8_linear(qx[:rows], c.w, c0.input_scale * c.weight_scale)
+        passes, el = repeat_until(BASELINE_SECONDS, one_pass)
+        flops = passes * sum(2 * rows * c.w.shape[0] * k for c in cs)
         return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"quantiser on all 4096 rows + GEMM on the first {rows} rows for both N ({el:.1f} s)"}
+                "sample": f"quantiser on all 4096 rows + GEMM on the first {rows} rows for both N, {passes} passes "
+                          f"({el:.1f} s)"}
 
     return dict(metric="FP8 W8A8 GEMM TFLOP/s (static per-tensor activation quantiser + fp8 GEMM)", unit="TFLOP/s",
                 per="work", cases=cases, dominant=cases[2], bound="mfma", peak=FP8_PEAK_TFLOPS,
-                kernel="fp8_w8a8_lds_kernel<256, 128> (M=4096, N=12288, K=3072)", dtype="f8",
+                kernel="fp8_w8a8_lds2_kernel<256, 256> (M=4096, N=12288, K=3072)", dtype="f8",
                 config={"workload": "fp8_w8a8: quantise bf16 [4096,3072] to E4M3 + fp8 GEMM N in {3072,12288}, "
                                     "bf16 out"},
                 baseline=baseline)
@@ -605,7 +624,7 @@ def main():
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
                    "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
-                   "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds_kernel",
+                   "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds2_kernel",
                    "bf16_decode": "bf16_gemv_wide_kernel", "grouped_int8": "int8_grouped_kernel"}
         write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
         return

@@ -1331,6 +1331,171 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds_kernel(const uint8_t* __
   }
 }
 
+// The same GEMM with the A fragments refreshed in place: the fragments of
+// A row block i for strip s + 1 are read right after the MFMAs of block i
+// for strip s, so only one set of A fragments (and two of B) is live.  This
+// fits a 256 x 256 tile (128 x 64 per wave) in the 256 registers a wave has
+// at two waves per SIMD.
+template <int BM, int BN, int S, int WY, int NW, int OUT>
+__global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* __restrict__ a,
+                                                                 const uint8_t* __restrict__ b,
+                                                                 void* __restrict__ out, int64_t M, int64_t N,
+                                                                 int64_t K, float alpha, int vec) {
+  using L = I8Layout<BM, BN, S, WY, NW>;
+  constexpr int FM = L::FM, FN = L::FN;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t tm, tn;
+  tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wy = wid / L::WX, wx = wid % L::WX;
+  const int r = lane & 31, h = lane >> 5;
+  const int row0 = wy * (BM / WY), col0 = wx * (BN / L::WX);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, M * K), rb = make_rsrc(b, N * K);
+  typename L::ADma adma;
+  adma.init(m0, M, K);
+  typename L::BDma bdma;
+  bdma.init(n0, N, K);
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    aoff[t] = uint32_t((row0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+    boff[t] = uint32_t(L::kA + (col0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+  }
+  const int nk = int(K / 64);
+
+  auto fetch = [&](int s) {
+    char* st = lds + (s % S) * L::kStage;
+    const int src = s < nk ? s : nk - 1;
+    adma.fetch(st, ra, uint32_t(src) * 64);
+    bdma.fetch(st + L::kA, rb, uint32_t(src) * 64);
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+
+  v8i fa[FM], bP[FN], bQ[FN];
+  auto read_a = [&](int i, const char* st) {
+    fa[i].lo = __builtin_bit_cast(v4i, lds16(st + aoff[0] + i * 32 * 64));
+    fa[i].hi = __builtin_bit_cast(v4i, lds16(st + aoff[1] + i * 32 * 64));
+  };
+  auto read_b = [&](v8i (&fb)[FN], const char* st) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      fb[j].lo = __builtin_bit_cast(v4i, lds16(st + boff[0] + j * 32 * 64));
+      fb[j].hi = __builtin_bit_cast(v4i, lds16(st + boff[1] + j * 32 * 64));
+    }
+  };
+  // MFMAs of the current strip (A in fa, B in fb) while the fragments of the
+  // next strip (at `next`) are read: B first, then A block by block behind
+  // the MFMAs that last use it.  `last` multiplies the final strip.
+  auto step = [&](const v8i (&fb)[FN], v8i (&fb_next)[FN], const char* next) {
+    read_b(fb_next, next);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+      read_a(i, next);
+    }
+  };
+  auto last = [&](const v8i (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+  };
+  auto order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x020, L::kLoads, 0);  // DMA issue
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * FN, 0);     // B reads
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);  // block i's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its A reads
+    }
+  };
+  auto cross = [&](int kt) {
+    wait_lds();
+    wait_vm<(S - 2) * L::kLoads>();
+    block_barrier();
+    fetch(kt + S);
+  };
+
+#pragma unroll
+  for (int s = 0; s < S; ++s) fetch(s);
+  wait_vm<(S - 1) * L::kLoads>();
+  block_barrier();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) read_a(i, lds);
+  read_b(bP, lds);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    cross(kt);
+    step(bP, bQ, lds + ((kt + 1) % S) * L::kStage);
+    order();
+    cross(kt + 1);
+    step(bQ, bP, lds + ((kt + 2) % S) * L::kStage);
+    order();
+  }
+  if (kt + 1 < nk) {  // two strips left: kt (A in fa, B in bP) and kt + 1
+    cross(kt);
+    step(bP, bQ, lds + ((kt + 1) % S) * L::kStage);
+    wait_lds();
+    last(bQ);
+  } else {
+    last(bP);
+  }
+  wait_vm<0>();  // no LDS write may land after the block ends
+
+  // acc[i][j][v] = C[m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + col0 + 32 j + r]
+  constexpr bool kSlabFits = kSlabBase + NW * Slab<OUT, FN, 32>::kBytes <= L::kLds;
+  if (kSlabFits && vec && m0 + BM <= M && n0 + BN <= N) {
+    block_barrier();  // every wave is done reading the last strip
+    const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) slab.put_f(8 * (v / 4) + 4 * h + (v % 4), 32 * j + r, acc[i][j][v] * alpha);
+      slab.flush(out, N, m0 + row0 + 32 * i, n0 + col0);
+      wait_lds();  // slab reads done before it is rewritten
+    }
+  } else {
+    const int64_t mw = m0 + row0 + 4 * h, nw = n0 + col0 + r;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = mw + 32 * i + 8 * (v / 4) + (v % 4);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = nw + 32 * j;
+          if (n < N) put_out<OUT>(out, m * N + n, acc[i][j][v] * alpha);
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int S, int WY, int NW>
+hipError_t launch_fp8_w8a8_cfg2(const uint8_t* a, const uint8_t* b, void* out, int out_bf16, int64_t M, int64_t N,
+                                int64_t K, float alpha, hipStream_t s) {
+  using L = I8Layout<BM, BN, S, WY, NW>;
+  const int64_t blocks = tiles(M, N, BM, BN);
+  const int vec = aligned16(out) && (N * (out_bf16 ? 2 : 4)) % 16 == 0;
+  if (out_bf16)
+    return launch_big_lds<fp8_w8a8_lds2_kernel<BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N,
+                                                                      K, alpha, vec);
+  return launch_big_lds<fp8_w8a8_lds2_kernel<BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N, K,
+                                                                    alpha, vec);
+}
+
 template <int BM, int BN, int S, int WY, int NW>
 hipError_t launch_fp8_w8a8_cfg(const uint8_t* a, const uint8_t* b, void* out, int out_bf16, int64_t M, int64_t N,
                                int64_t K, float alpha, hipStream_t s) {
@@ -1506,8 +1671,11 @@ hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales
 
 hipError_t launch_fp8_w8a8_lds(const uint8_t* xq, const uint8_t* w, void* out, int out_bf16, int64_t M, int64_t N,
                                int64_t K, float alpha, int num_cus, hipStream_t s) {
-  // No 256 x 256 tile: two register sets of 32-byte fragments plus its
-  // accumulators spill at two waves per SIMD (and at one).
+  // The 256 x 256 tile needs the in-place fragment refresh of
+  // fp8_w8a8_lds2_kernel to fit two waves per SIMD (4096 x 12288 x 3072:
+  // 175 us against 199 us for 256 x 128).
+  if (tiles(M, N, 256, 256) >= num_cus / 2)
+    return launch_fp8_w8a8_cfg2<256, 256, 4, 2, 8>(xq, w, out, out_bf16, M, N, K, alpha, s);
   if (tiles(M, N, 256, 128) >= num_cus / 2)
     return launch_fp8_w8a8_cfg<256, 128, 4, 2, 8>(xq, w, out, out_bf16, M, N, K, alpha, s);
   return launch_fp8_w8a8_cfg<128, 128, 4, 2, 8>(xq, w, out, out_bf16, M, N, K, alpha, s);
