@@ -177,6 +177,16 @@ __device__ __forceinline__ void store_epi(void* out, int64_t m, int64_t n, int64
   else reinterpret_cast<float*>(out)[i] = v;
 }
 
+// store_epi when the kernel instance carries the fused epilogue (FUSED),
+// else the plain store: kernels whose registers the epilogue code would
+// raise come in both forms.
+template <bool FUSED>
+__device__ __forceinline__ void store_maybe_epi(void* out, int64_t m, int64_t n, int64_t N, float acc, float alpha,
+                                                int out_bf16, const Epilogue& epi) {
+  if constexpr (FUSED) store_epi(out, m, n, N, acc, alpha, out_bf16, epi);
+  else store_out(out, m * N + n, acc, alpha, out_bf16);
+}
+
 // ---------------------------------------------------------------- wave reduction
 
 template <int CTRL, int ROW_MASK = 0xF>

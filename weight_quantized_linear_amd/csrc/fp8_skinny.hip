@@ -45,7 +45,7 @@ namespace {
 
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
-template <int G, int U, int NWV>
+template <int G, int U, int NWV, bool FUSED>
 __global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
     int out_bf16, int M, int64_t N, int64_t K, float alpha, Epilogue epi) {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) s += red[q][g][lane][wid];
     const int64_t n = n0 + 16 * g + r16;
-    if (m < M && n < N) store_epi(out, m, n, N, s, alpha, out_bf16, epi);
+    if (m < M && n < N) store_maybe_epi<FUSED>(out, m, n, N, s, alpha, out_bf16, epi);
   }
 }
 
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NWV * 64) void fp8_skinny_kernel(
 // contiguous weight.  Wave w then takes bytes [w KT/4, (w+1) KT/4) of every
 // row of the tile in 64-byte matrix-core steps.  The next tile's loads are
 // issued before the current tile's matrix-core work.
-template <int G, int KT>
+template <int G, int KT, bool FUSED>
 __global__ __launch_bounds__(256) void fp8_skinny_lds_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
     int out_bf16, int M, int64_t N, int64_t K, float alpha, Epilogue epi) {
@@ -197,14 +197,14 @@ __global__ __launch_bounds__(256) void fp8_skinny_lds_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) s += red[q][g][lane][wid];
     const int64_t n = n0 + 16 * g + r16;
-    if (m < M && n < N) store_epi(out, m, n, N, s, alpha, out_bf16, epi);
+    if (m < M && n < N) store_maybe_epi<FUSED>(out, m, n, N, s, alpha, out_bf16, epi);
   }
 }
 
 // 4x4x4 variant for M <= 4: each wave owns 4*G rows and all of K; lane
 // l = 4b + j loads weight row n0 + 4g + j and activation row j at byte/element
 // offset 256 s + 16 b of every 256-wide K step s.
-template <int G, int U>
+template <int G, int U, bool FUSED>
 __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
     int out_bf16, int M, int64_t N, int64_t K, float alpha, Epilogue epi) {
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void fp8_skinny4_kernel(
       if (n >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (i < M) store_epi(out, i, n, N, acc[g][i], alpha, out_bf16, epi);
+        if (i < M) store_maybe_epi<FUSED>(out, i, n, N, acc[g][i], alpha, out_bf16, epi);
     }
   }
 }
@@ -314,7 +314,7 @@ __device__ __forceinline__ void rs_halve(float* v, int lane, int mask) {
 // With few rows (KS > 1) the K chunks of a group are split over KS waves of
 // the block, whose partial outputs are added through LDS in a fixed order;
 // the block then walks NWB / KS groups per round.
-template <int MG, int NWB, int KS>
+template <int MG, int NWB, int KS, bool FUSED>
 __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
     int out_bf16, int M, int N, int K, float alpha, Epilogue epi) {
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
   auto store = [&](int grp, float val) {
     const int m = b >> (4 - kLogV);
     const int n = 4 * grp + j;
-    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N) store_epi(out, m, n, N, val, alpha, out_bf16, epi);
+    if ((b & ((1 << (4 - kLogV)) - 1)) == 0 && m < M && n < N) store_maybe_epi<FUSED>(out, m, n, N, val, alpha, out_bf16, epi);
   };
 
   int g = blockIdx.x * kGpb + gi;
@@ -475,17 +475,20 @@ constexpr int kMaxLds = 160 * 1024;
 template <int G, int U, int NWV>
 hipError_t launch_skinny16(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
                            int64_t K, float alpha, const Epilogue& epi, hipStream_t s) {
-  return launch(fp8_skinny_kernel<G, U, NWV>, dim3((N + 16 * G - 1) / (16 * G)), dim3(NWV * kWave), 0, s, w, x, out,
-                out_bf16, int(M), N, K, alpha, epi);
+  if (!epi.on)
+    return launch(fp8_skinny_kernel<G, U, NWV, false>, dim3((N + 16 * G - 1) / (16 * G)), dim3(NWV * kWave), 0, s, w,
+                  x, out, out_bf16, int(M), N, K, alpha, epi);
+  return launch(fp8_skinny_kernel<G, U, NWV, true>, dim3((N + 16 * G - 1) / (16 * G)), dim3(NWV * kWave), 0, s, w,
+                x, out, out_bf16, int(M), N, K, alpha, epi);
 }
 
 // Largest activation copy (bytes) the LDS holds: 4 MG padded rows x K bf16.
 int xlds_groups(int64_t M) { return M <= 4 ? 1 : (M <= 8 ? 2 : 4); }
 
-template <int MG, int NWB, int KS>
+template <int MG, int NWB, int KS, bool FUSED>
 hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
                            float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
-  auto kern = fp8_skinny_xlds_kernel<MG, NWB, KS>;
+  auto kern = fp8_skinny_xlds_kernel<MG, NWB, KS, FUSED>;
   static bool attr_set = false;  // one flag per instantiation
   if (!attr_set) {
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -502,8 +505,8 @@ hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int o
                 alpha, epi);
 }
 
-template <int MG>
-hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
+template <int MG, bool FUSED>
+hipError_t launch_xlds_f(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
                        float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
   // About a dozen waves per CU in total: one large block per CU when there
   // are enough 4-row groups, otherwise smaller blocks over more CUs, and
@@ -513,12 +516,19 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
   constexpr int kBig = MG == 1 ? 16 : (MG == 2 ? 12 : 8);
   const int64_t groups = (int64_t(N) + 3) / 4;
   if (groups >= int64_t(num_cus) * kBig)
-    return launch_xlds_nwb<MG, kBig, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+    return launch_xlds_nwb<MG, kBig, 1, FUSED>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
   if (groups >= int64_t(num_cus) * 8)
-    return launch_xlds_nwb<MG, 8, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+    return launch_xlds_nwb<MG, 8, 1, FUSED>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
   if (K >= 4096)
-    return launch_xlds_nwb<MG, 8, 4>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
-  return launch_xlds_nwb<MG, 4, 1>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+    return launch_xlds_nwb<MG, 8, 4, FUSED>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+  return launch_xlds_nwb<MG, 4, 1, FUSED>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+}
+
+template <int MG>
+hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
+                       float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
+  if (epi.on) return launch_xlds_f<MG, true>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+  return launch_xlds_f<MG, false>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
 }
 
 }  // namespace
@@ -544,16 +554,22 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
   if (M <= 4) {
     if (wide_n) {
       const int64_t blocks = (N + 63) / 64;  // 4 waves x 16 rows
-      return launch(fp8_skinny4_kernel<4, 2>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16, int(M), N,
-                    K, alpha, epi);
+      return epi.on ? launch(fp8_skinny4_kernel<4, 2, true>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16,
+                             int(M), N, K, alpha, epi)
+                    : launch(fp8_skinny4_kernel<4, 2, false>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16,
+                             int(M), N, K, alpha, epi);
     }
     const int64_t blocks = (N + 15) / 16;  // 4 waves x 4 rows
-    return launch(fp8_skinny4_kernel<1, 4>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16, int(M), N, K,
-                  alpha, epi);
+    return epi.on ? launch(fp8_skinny4_kernel<1, 4, true>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16,
+                           int(M), N, K, alpha, epi)
+                  : launch(fp8_skinny4_kernel<1, 4, false>, dim3(blocks), dim3(256), 0, s, w, x, out, out_bf16,
+                           int(M), N, K, alpha, epi);
   }
   if (wide_n)
-    return launch(fp8_skinny_lds_kernel<4, 512>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out, out_bf16,
-                  int(M), N, K, alpha, epi);
+    return epi.on ? launch(fp8_skinny_lds_kernel<4, 512, true>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out,
+                           out_bf16, int(M), N, K, alpha, epi)
+                  : launch(fp8_skinny_lds_kernel<4, 512, false>, dim3((N + 63) / 64), dim3(256), 0, s, w, x, out,
+                           out_bf16, int(M), N, K, alpha, epi);
   if (N >= 8192) return launch_skinny16<4, 2, 16>(w, x, out, out_bf16, M, N, K, alpha, epi, s);
   return launch_skinny16<1, 4, 16>(w, x, out, out_bf16, M, N, K, alpha, epi, s);
 }

@@ -535,8 +535,10 @@ struct WqLayout {
 // stores (out 16-byte aligned, N * element size a multiple of 16).
 // One BM x BN output tile at (m0, n0) of out[M, N] (leading dimension N).
 // Strips s0 .. s0 + ns - 1 of K (64 values each) are summed: all of K for
-// the plain GEMM, one slice for split-K partial sums.
-template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
+// the plain GEMM, one slice for split-K partial sums.  FUSED: the store
+// applies `epi` (a separate instance, so that the epilogue's code does not
+// raise the registers of the plain kernels).
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT, bool FUSED = false>
 __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ x, typename WP<BN, 1, NW>::Args wa,
                                         void* __restrict__ out, int64_t M, int64_t N, int64_t K, float alpha,
                                         int vec, int64_t m0, int64_t n0, int64_t s0, int64_t ns, const Epilogue& epi) {
@@ -653,8 +655,7 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
   // acc[i][j][v] = C[m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + col0 + 32 j + r]
   // Full tiles leave through the per-wave LDS slabs when they fit.  The
   // fused epilogue, when present, is applied to each element on its way.
-  auto store = [&](auto fused) {
-    constexpr bool FUSED = decltype(fused)::value;
+  {
     auto value = [&](float a, int64_t m, int64_t n) {
       if constexpr (FUSED) return epi_apply(epi, a * alpha, m, n);
       else return a * alpha;
@@ -690,12 +691,10 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
           }
         }
     }
-  };
-  if (epi.on) store(std::true_type{});
-  else store(std::false_type{});
+  }
 }
 
-template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT>
+template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT, bool FUSED>
 __global__ __launch_bounds__(64 * NW) void wq_gemm_kernel(const uint16_t* __restrict__ x,
                                                           typename WP<BN, 1, NW>::Args wa, void* __restrict__ out,
                                                           int64_t M, int64_t N, int64_t K, float alpha, int vec,
@@ -703,7 +702,8 @@ __global__ __launch_bounds__(64 * NW) void wq_gemm_kernel(const uint16_t* __rest
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0, K / 64, epi);
+  wq_tile<WP, BM, BN, S, WY, NW, OUT, FUSED>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0, K / 64,
+                                             epi);
 }
 
 // Split-K: block b computes slice b % splits of tile b / splits into the
@@ -855,11 +855,16 @@ hipError_t launch_wq(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, void* o
   const int64_t blocks = tiles(M, N, BM, BN);
   const int es = out_bf16 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
-  if (out_bf16)
-    return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N, K,
-                                                                     alpha, vec, epi);
-  return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N, K,
-                                                                   alpha, vec, epi);
+  auto go = [&](auto fused) {
+    constexpr bool F = decltype(fused)::value;
+    if (out_bf16)
+      return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 1, F>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M,
+                                                                          N, K, alpha, vec, epi);
+    return launch_big_lds<wq_gemm_kernel<WP, BM, BN, S, WY, NW, 0, F>>(L::kLds, blocks, 64 * NW, s, x, wa, out, M, N,
+                                                                        K, alpha, vec, epi);
+  };
+  if (epi.on) return go(std::true_type{});
+  return go(std::false_type{});
 }
 
 // Split-K launch: partial planes in the caller's float32 workspace.
