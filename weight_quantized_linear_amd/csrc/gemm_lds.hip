@@ -1438,23 +1438,15 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
 #pragma unroll
   for (int i = 0; i < FM; ++i) read_a(i, lds);
   read_b(bP, lds);
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     cross(kt);
     step(bP, bQ, lds + ((kt + 1) % S) * L::kStage);
     order();
-    cross(kt + 1);
-    step(bQ, bP, lds + ((kt + 2) % S) * L::kStage);
-    order();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bP[j] = bQ[j];
   }
-  if (kt + 1 < nk) {  // two strips left: kt (A in fa, B in bP) and kt + 1
-    cross(kt);
-    step(bP, bQ, lds + ((kt + 1) % S) * L::kStage);
-    wait_lds();
-    last(bQ);
-  } else {
-    last(bP);
-  }
+  wait_lds();
+  last(bP);
   wait_vm<0>();  // no LDS write may land after the block ends
 
   // acc[i][j][v] = C[m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4][n0 + col0 + 32 j + r]
