@@ -68,7 +68,8 @@ typedef enum qlinear_path {
   QLINEAR_PATH_AUTO = 0,
   QLINEAR_PATH_GEMV = 1,    /* vector-ALU GEMV, 1 <= M <= 4                         */
   QLINEAR_PATH_SKINNY = 2,  /* matrix-core skinny GEMM, 1 <= M <= 16                */
-  QLINEAR_PATH_TILED = 3    /* LDS-tiled matrix-core GEMM, any M                     */
+  QLINEAR_PATH_TILED = 3,   /* LDS-tiled matrix-core GEMM, any M                     */
+  QLINEAR_PATH_SPLITK = 4   /* split-K skinny GEMM, M <= 16, K % 64 == 0, aligned    */
 } qlinear_path;
 
 /* Activation of a fused epilogue. */
@@ -142,7 +143,11 @@ int qlinear_fp8_gemm(const void* w, const void* x, void* out, int out_dtype,
 /*
  * As qlinear_fp8_gemm, with the kernel family forced (tests compare the
  * families with each other).  A family that cannot take the given M returns
- * QLINEAR_ERR_INVALID_ARG.
+ * QLINEAR_ERR_INVALID_ARG.  QLINEAR_PATH_SPLITK (K split over blocks, float32
+ * partial planes in the library's workspace added by a second kernel in a
+ * fixed order) returns QLINEAR_ERR_UNSUPPORTED, launching nothing, when the
+ * shape leaves fewer than two K slices of 256 values or the partial planes
+ * exceed the workspace; the automatic choice then takes the skinny kernel.
  */
 int qlinear_fp8_gemm_path(const void* w, const void* x, void* out, int out_dtype,
                           int64_t M, int64_t N, int64_t K, float alpha, int path,

@@ -75,6 +75,10 @@ DYADIC = [
     ("skinny", 12, 66003, 4096), ("skinny", 5, 1, 256),
     # 16x16x32 activation-in-LDS kernel (5 <= M <= 16, K % 64 == 0): the largest K, uneven K split
     ("skinny", 16, 300, 4864), ("skinny", 6, 2050, 4800),
+    # split-K skinny kernel: K slices of 64-value chunks with a ragged last slice, fewer columns than
+    # one block, every M, and the automatic choice at M = 12, K = 8192
+    ("splitk", 16, 4096, 14336), ("splitk", 3, 1000, 4096), ("splitk", 9, 300, 2112), ("splitk", 16, 70, 1024),
+    ("splitk", 1, 129, 512), ("auto", 12, 2000, 8192),
 ]
 
 
@@ -190,3 +194,22 @@ def test_gemm_rejects_mismatched_shapes(q):
     x = torch.zeros((2, 32), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(ValueError):
         q.fp8_gemm(w, x)
+
+
+def test_splitk_reports_unsuitable_shapes(q):
+    """A K too short for two slices gives QLINEAR_ERR_UNSUPPORTED and launches
+    nothing; the automatic choice takes the skinny kernel instead."""
+    wc = synth.dyadic_fp8_weight((14,), 70000, 256)
+    xc = synth.dyadic_activation((15,), 12, 256)
+    w, x = to_dev_u8(wc), to_dev_bf16(xc)
+    out = torch.full((12, 70000), 7.0, dtype=torch.float32, device="cuda:0")
+    show("splitk unsuitable")
+    with pytest.raises(q.QLinearError) as e:
+        q.fp8_gemm(w, x, out=out, out_dtype=torch.float32, path="splitk")
+    assert e.value.status == q.ERR_UNSUPPORTED
+    assert torch.all(out == 7.0)
+    w2 = to_dev_u8(synth.dyadic_fp8_weight((16,), 100, 208))  # K % 64 != 0
+    x2 = to_dev_bf16(synth.dyadic_activation((17,), 12, 208))
+    with pytest.raises(q.QLinearError) as e:
+        q.fp8_gemm(w2, x2, out_dtype=torch.float32, path="splitk")
+    assert e.value.status == q.ERR_INVALID_ARG

@@ -43,7 +43,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlinear.
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16, I32 = 0, 1, 2
-PATHS = {"auto": 0, "gemv": 1, "skinny": 2, "tiled": 3}
+PATHS = {"auto": 0, "gemv": 1, "skinny": 2, "tiled": 3, "splitk": 4}
 
 _p, _i, _i64, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
 

@@ -465,6 +465,83 @@ __global__ __launch_bounds__(NWB * 64) void fp8_skinny_xlds_kernel(
   }
 }
 
+// Split-K skinny kernel (M <= 16, K % 64 == 0): block (bx, s) owns output
+// columns 16 NW bx .. +16 NW - 1 and K slice s (ksl values, a multiple of
+// 64).  The block first copies the activation slice, zero-padded to 16 rows,
+// into LDS (row stride 2 ksl + 16 bytes: the 16 rows of one read fall in
+// distinct banks); wave w then streams weight rows 16 w .. 16 w + 15 of the
+// block over the slice, lane (r, q) loading bytes 64 c + 16 q .. +15 of row
+// r for chunk c, U chunks in flight, and multiplies with
+// v_mfma_f32_16x16x32_bf16 (activation rows as A, weight rows as B; both
+// operands put k = 64 c + 16 q + 8 h + e in k-slot 8 q + e of MFMA h).  The
+// 16 x 16 partial sums go to plane s of a float32 workspace [splits, M, N];
+// a second kernel adds the planes in a fixed order.  Narrow, long-K shapes
+// thus keep every CU streaming while each block reads only its slice of the
+// activation once.
+template <int NW, int U>
+__global__ __launch_bounds__(NW * 64) void fp8_skinny_splitk_kernel(const uint8_t* __restrict__ w,
+                                                                    const uint16_t* __restrict__ x,
+                                                                    float* __restrict__ part, int M, int64_t N,
+                                                                    int64_t K, int ksl) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t slice = blockIdx.y;
+  const int64_t k0 = slice * ksl;
+  const int klen = int(K - k0 < ksl ? K - k0 : ksl);  // > 0, a multiple of 64
+  const int row_bytes = 2 * ksl + 16;
+
+  const int64_t n0 = int64_t(blockIdx.x) * 16 * NW + 16 * wid;
+  int64_t n = n0 + r16;
+  if (n >= N) n = N - 1;  // padding columns re-read the last row; never stored
+  const uint8_t* wrow = w + n * K + k0 + 16 * q;
+  const int nck = klen / 64;
+  auto load = [&](u32x4 (&wv)[U], int c0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      wv[u] = c0 + u < nck ? ld16_stream(wrow + 64 * (c0 + u)) : u32x4{0u, 0u, 0u, 0u};
+  };
+  // The first weight chunks are in flight while the activation is copied.
+  u32x4 wa[U], wb[U];
+  load(wa, 0);
+
+  // Activation slice: 16 rows x klen bf16 as 16-byte chunks (rows >= M are zero).
+  const int cpr = klen / 8;
+  for (int c = threadIdx.x; c < 16 * cpr; c += NW * kWave) {
+    const int m = c / cpr, j = c % cpr;
+    const u32x4 v = m < M ? ld16(x + int64_t(m) * K + k0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds + m * row_bytes + 16 * j) = v;
+  }
+  __syncthreads();
+
+  const char* xrow = lds + r16 * row_bytes + 32 * q;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nck; c0 += U) {
+    if (c0 + U < nck) load(wb, c0 + U);  // next chunks in flight during this batch
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u >= nck) break;  // uniform
+      const char* xa = xrow + 128 * (c0 + u);
+      const v8bf a0 = *reinterpret_cast<const v8bf*>(xa);
+      const v8bf a1 = *reinterpret_cast<const v8bf*>(xa + 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, e4m3x8_to_bf16x8(wa[u].x, wa[u].y), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, e4m3x8_to_bf16x8(wa[u].z, wa[u].w), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) wa[u] = wb[u];
+  }
+
+  // acc[v] = D[m = 4 q + v][column n0 + r16]
+  const int64_t col = n0 + r16;
+  if (col < N) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * q + v;
+      if (m < M) part[(slice * M + m) * N + col] = acc[v];
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -532,6 +609,37 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
 }
 
 }  // namespace
+
+// Split-K skinny GEMM: K slices of at least 256 values, enough (row block,
+// slice) pairs to give every CU a block, partial planes within the
+// workspace.  Returns hipErrorInvalidValue when the shape or workspace does
+// not suit it (the caller then takes another kernel).
+hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
+                                   int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
+                                   hipStream_t s, const Epilogue& epi) {
+  constexpr int kNW = 8, kU = 4;
+  if (M < 1 || M > 16 || K % 64 != 0 || !ws) return hipErrorInvalidValue;
+  const int64_t row_blocks = (N + 16 * kNW - 1) / (16 * kNW);
+  int64_t splits = (num_cus + row_blocks - 1) / row_blocks;
+  splits = std::min<int64_t>(splits, K / 256);
+  if (splits < 2) return hipErrorInvalidValue;
+  int64_t ksl = ((K + splits - 1) / splits + 63) / 64 * 64;
+  ksl = std::min<int64_t>(ksl, 4096);
+  splits = (K + ksl - 1) / ksl;
+  if (size_t(splits) * size_t(M) * size_t(N) * 4 > ws_bytes) return hipErrorInvalidValue;
+  const int lds = int(16 * (2 * ksl + 16));
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fp8_skinny_splitk_kernel<kNW, kU>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds))
+      return e;
+    attr_set = true;
+  }
+  if (hipError_t e = launch(fp8_skinny_splitk_kernel<kNW, kU>, dim3(unsigned(row_blocks), unsigned(splits)),
+                            dim3(kNW * kWave), size_t(lds), s, w, x, ws, int(M), N, K, int(ksl)))
+    return e;
+  return launch_splitk_reduce(ws, out, out_bf16, M, N, int(splits), alpha, s, epi);
+}
 
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&

@@ -1572,6 +1572,14 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
+hipError_t launch_splitk_reduce(const float* part, void* out, int out_bf16, int64_t M, int64_t N, int splits,
+                                float alpha, hipStream_t s, const Epilogue& epi) {
+  const int64_t count = M * N, rblocks = (count + 1023) / 1024;
+  if (out_bf16)
+    return launch(wq_reduce_kernel<1>, dim3(rblocks), dim3(256), 0, s, part, out, count, splits, alpha, N, epi);
+  return launch(wq_reduce_kernel<0>, dim3(rblocks), dim3(256), 0, s, part, out, count, splits, alpha, N, epi);
+}
+
 bool bf16_lds_supported(const void* x, const void* w, int64_t M, int64_t N, int64_t K) {
   return K >= 64 && K % 64 == 0 && aligned16(x) && aligned16(w) && M * K * 2 < (int64_t(1) << 32) &&
          N * K * 2 < (int64_t(1) << 32);

@@ -34,6 +34,16 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s, const Epilogue& epi = Epilogue{});
 
+// Split-K skinny GEMM (M <= 16, K % 64 == 0, aligned, workspace present):
+// hipErrorInvalidValue when the shape does not suit it.  The second kernel
+// (gemm_lds.hip) adds the float32 partial planes [splits, M, N] in order,
+// then applies alpha and the epilogue.
+hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
+                                   int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
+                                   hipStream_t s, const Epilogue& epi = Epilogue{});
+hipError_t launch_splitk_reduce(const float* part, void* out, int out_bf16, int64_t M, int64_t N, int splits,
+                                float alpha, hipStream_t s, const Epilogue& epi = Epilogue{});
+
 // gemm_bf16.hip (dispatches to gemm_lds.hip when K % 64 == 0 and operands are aligned)
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
                             int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,

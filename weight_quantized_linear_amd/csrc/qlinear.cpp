@@ -133,6 +133,7 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   if (!float_out_ok(out_dtype)) return QLINEAR_ERR_INVALID_ARG;
   if (!aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
   const bool wide = K % 16 == 0 && aligned(w, 16) && aligned(x, 16);
+  bool auto_splitk = false;
   if (path == QLINEAR_PATH_AUTO) {
     // Measured on the decode shapes: the vector-ALU GEMV wins for M <= 2
     // below 65536 output features and for M <= 4 on small weights; the
@@ -141,10 +142,15 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
     // applies) and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
     const bool big = N >= 65536 ||
                      (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K));
+    // For 9 <= M <= 16 with a long K and fewer than 65536 output features
+    // the split-K skinny kernel wins (M = 16, N = 4096, K = 14336: 19.2 us
+    // against 23.1 us), when the workspace is there.
     if (M == 1) path = QLINEAR_PATH_GEMV;
     else if (M <= 4) path = (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
-    else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
+    else if (M <= 16 && wide) path = (M > 8 && K >= 8192 && K % 64 == 0 && N < 65536) ? QLINEAR_PATH_SPLITK
+                                                                                      : QLINEAR_PATH_SKINNY;
     else path = QLINEAR_PATH_TILED;
+    auto_splitk = path == QLINEAR_PATH_SPLITK;
   }
   switch (path) {
     case QLINEAR_PATH_GEMV:
@@ -154,6 +160,9 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
       if (M > 16 || !wide) return QLINEAR_ERR_INVALID_ARG;
       break;
     case QLINEAR_PATH_TILED:
+      break;
+    case QLINEAR_PATH_SPLITK:
+      if (M > 16 || !wide || K % 64 != 0) return QLINEAR_ERR_INVALID_ARG;
       break;
     default:
       return QLINEAR_ERR_INVALID_ARG;
@@ -167,6 +176,14 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   auto* wp = static_cast<const uint8_t*>(w);
   auto* xp = static_cast<const uint16_t*>(x);
   const int bf16 = out_dtype == QLINEAR_BF16;
+  if (path == QLINEAR_PATH_SPLITK) {
+    const hipError_t e = launch_fp8_skinny_splitk(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s),
+                                                  kWorkspaceBytes, s, epi);
+    if (e != hipErrorInvalidValue) return finish(e);
+    // Shape or workspace unsuitable (nothing was launched).
+    if (!auto_splitk) return QLINEAR_ERR_UNSUPPORTED;
+    path = QLINEAR_PATH_SKINNY;
+  }
   if (path == QLINEAR_PATH_GEMV)
     return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
   if (path == QLINEAR_PATH_SKINNY)
