@@ -61,7 +61,9 @@ def test_gemv_one_hot_returns_dequantised_column(q):
 
 NVFP4_DYADIC = [("gemv", 1, 7, 4096), ("gemv", 1, 515, 48), ("gemv", 3, 129, 2048), ("gemv", 4, 1000, 4096),
                 ("gemv", 2, 65, 4112), ("tiled", 5, 100, 4096), ("tiled", 128, 300, 1024),
-                ("tiled", 200, 129, 2064), ("tiled", 1, 17, 16)]
+                ("tiled", 200, 129, 2064), ("tiled", 1, 17, 16),
+                # 128x256 tiles (ragged N) and 256x256 tiles (ragged M)
+                ("tiled", 2048, 2100, 64), ("tiled", 4100, 4096, 64)]
 
 
 @pytest.mark.parametrize("path,m,n,k", NVFP4_DYADIC)

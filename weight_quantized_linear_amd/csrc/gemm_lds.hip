@@ -1566,7 +1566,10 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   }
   // The FP4 decode is the expensive part: waves side by side along N (WY = 1)
   // where the tile is wide enough, so that no two waves decode the same
-  // weight rows.
+  // weight rows.  With a 256 x 256 tile for every CU, its halved L2 -> LDS
+  // traffic wins instead (M = N = K = 4096: 156 -> 143 us).
+  if (tiles(M, N, 256, 256) >= num_cus)
+    return launch_wq<Nvfp4Weight, 256, 256, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   if (tiles(M, N, 128, 256) >= num_cus / 2)
     return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
