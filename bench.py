@@ -421,7 +421,7 @@ def build_grouped_nvfp4(dev, q, synth, np, torch):
 
     return dict(metric="Grouped MoE W4A16 NVFP4 achieved HBM GB/s", unit="GB/s", per="bytes", cases=cases,
                 dominant=cases[0], bound="hbm", peak=HBM_PEAK_GBS,
-                kernel="grouped_gemm_kernel<Nvfp4Weight, 64, 128> (64 experts, N=1536, K=2048, 4096 tokens)",
+                kernel="grouped_gemm_kernel<Nvfp4Weight, 64, 256> (64 experts, N=1536, K=2048, 4096 tokens)",
                 dtype="bf16",
                 config={"workload": f"grouped_moe_w4a16_nvfp4: E=64 [64,1536,2048] NVFP4, T=4096 bf16 tokens, "
                                     f"Zipf(1.2) groups, {len(active)} active experts, {rows_active} active tokens"},
