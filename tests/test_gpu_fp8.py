@@ -96,6 +96,41 @@ def test_dyadic_inputs_are_bit_exact(q, path, m, n, k, out_dtype):
         assert np.array_equal(bf16_bits(out), F.f64_to_bf16_bits(ref))
 
 
+# GEMV weight rows at any byte offset (K % 16 != 0, or a weight view that
+# starts off a 16-byte boundary): 16-byte loads shifted into place.  One and
+# two rows per wave, one and several passes over K, K below one chunk.  The
+# bytes around the view are NaN codes, so a byte read past a row's end and not
+# cleared shows up as NaN.
+@pytest.mark.parametrize("m,n,k", [(1, 515, 2050), (1, 4100, 2050), (1, 70, 4100), (2, 300, 1000),
+                                   (3, 70, 24), (1, 64, 7), (4, 4097, 4096)])
+@pytest.mark.parametrize("offset", [0, 1, 6, 15])
+def test_gemv_weight_rows_at_any_offset(q, m, n, k, offset):
+    wc = synth.dyadic_fp8_weight((14, m, n, k), n, k)
+    xc = synth.dyadic_activation((15, m, n, k), m, k)
+    ref, _ = R.fp8_linear(wc, xc)
+    flat = np.full(n * k + 32, 0x7F, np.uint8)
+    flat[offset:offset + n * k] = wc.reshape(-1)
+    w = to_dev_u8(flat)[offset:offset + n * k].view(n, k)
+    show("gemv weight offset", m, n, k, offset)
+    out = q.fp8_gemm(w, to_dev_bf16(xc), out_dtype=torch.float32, path="gemv")
+    assert np.array_equal(out.cpu().numpy(), ref.astype(np.float32))
+
+
+# An activation that starts off a 16-byte boundary takes the byte-load kernel.
+@pytest.mark.parametrize("m,k", [(1, 2050), (2, 4096)])
+def test_gemv_unaligned_activation(q, m, k):
+    n = 300
+    wc = synth.dyadic_fp8_weight((16, m, k), n, k)
+    xc = synth.dyadic_activation((17, m, k), m, k)
+    ref, _ = R.fp8_linear(wc, xc)
+    xbuf = to_dev_bf16(np.concatenate([np.zeros(1, xc.dtype), xc.reshape(-1)]))
+    x = xbuf[1:].view(m, k)
+    assert x.data_ptr() % 16 != 0
+    show("gemv unaligned x", m, k)
+    out = q.fp8_gemm(to_dev_u8(wc), x, out_dtype=torch.float32, path="gemv")
+    assert np.array_equal(out.cpu().numpy(), ref.astype(np.float32))
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_gemv_and_skinny_agree_on_exact_inputs(q, m):
     wc = synth.dyadic_fp8_weight((12, m), 777, 4096)
