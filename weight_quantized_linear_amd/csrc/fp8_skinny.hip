@@ -505,12 +505,22 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_splitk_kernel(const uint8_
   u32x4 wa[U], wb[U];
   load(wa, 0);
 
-  // Activation slice: 16 rows x klen bf16 as 16-byte chunks (rows >= M are zero).
+  // Activation slice: 16 rows x klen bf16 as 16-byte chunks (rows >= M are
+  // zero), kBatch loads per thread in flight before their LDS stores.
   const int cpr = klen / 8;
-  for (int c = threadIdx.x; c < 16 * cpr; c += NW * kWave) {
-    const int m = c / cpr, j = c % cpr;
-    const u32x4 v = m < M ? ld16(x + int64_t(m) * K + k0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(lds + m * row_bytes + 16 * j) = v;
+  constexpr int kT = NW * kWave, kBatch = 8;
+  for (int c0 = threadIdx.x; c0 < 16 * cpr; c0 += kT * kBatch) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int c = c0 + t * kT, m = c / cpr, j = c % cpr;
+      v[t] = c < 16 * cpr && m < M ? ld16(x + int64_t(m) * K + k0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int c = c0 + t * kT, m = c / cpr, j = c % cpr;
+      if (c < 16 * cpr) *reinterpret_cast<u32x4*>(lds + m * row_bytes + 16 * j) = v[t];
+    }
   }
   __syncthreads();
 
