@@ -1560,6 +1560,14 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
                                  size_t ws_bytes, hipStream_t s, const Epilogue& epi) {
   const Nvfp4Args wa{packed, scales};
   if (ws) {
+    // Up to 256 rows, 64-row tiles with four waves side by side (no weight
+    // row decoded twice) and half the partial planes of 128-row tiles
+    // (M = 128, N = K = 4096: 22.2 -> 18.4 us); larger M keeps 128 x 128.
+    if (M <= 256) {
+      const int sp = splitk_count(tiles(M, N, 64, 128), M, N, K, num_cus, ws_bytes);
+      if (sp > 1)
+        return launch_wq_splitk<Nvfp4Weight, 64, 128, 4, 1, 4>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
+    }
     const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
     if (sp > 1)
       return launch_wq_splitk<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
