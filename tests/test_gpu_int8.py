@@ -48,6 +48,36 @@ def test_quantizer_shapes_bit_exact(q, m, k):
     assert np.array_equal(qd.cpu().numpy(), want_q)
 
 
+def test_quantizer_quotients_near_half_integers(q):
+    """Rows whose quotients x / scale fall on or next to half-integers (the
+    kernel multiplies by 1 / scale and lets the IEEE division decide near a
+    rounding boundary), plus a row whose scale is subnormal (division only)."""
+    targets = [1.0 / 3.0, 0.7, 1e-3 * np.pi, 5.5e-30, 2.3e-5]
+    n = np.arange(-126, 127, dtype=np.float64)
+    rows = []
+    for s_t in targets:
+        vals = [127.0 * s_t]
+        for eps in (0.0, 2.0 ** -10, -(2.0 ** -10), 2.0 ** -14, -(2.0 ** -14), 2.0 ** -7):
+            vals.extend((n + 0.5 + eps) * s_t)
+        rows.append(np.array(vals))
+    k = max(len(r) for r in rows)
+    x = np.zeros((len(rows) + 1, k), np.uint16)
+    for i, r in enumerate(rows):
+        x[i, :len(r)] = F.f64_to_bf16_bits(r)
+    x[-1, :4] = [0x0001, 0x8003, 0x0007, 0x0000]  # bf16 subnormals: the scale is subnormal too
+    want_q, want_s = R.int8_quantize_act(x)
+    # the boundary cases are really there: fp32 quotients within 2^-14 of a half-integer
+    xf = F.bf16_bits_to_f64(x[:-1]).astype(np.float32)
+    ratio = np.divide(xf, want_s[:-1, None], dtype=np.float32)
+    near = np.abs(np.abs(ratio - np.rint(ratio)) - 0.5) < 2.0 ** -14
+    assert near.sum() >= 30
+    assert want_s[-1] < np.float32(2.0 ** -126) and want_s[-1] > 0
+    show("int8 quantize near halves")
+    qd, sd = q.int8_quantize_act(to_dev_bf16(x))
+    assert np.array_equal(sd.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(qd.cpu().numpy(), want_q)
+
+
 def test_quantizer_unaligned_view(q):
     x = synth.bf16_activation((61,), 1, 4 * 1000 + 1)
     xd = to_dev_bf16(x)[0, 1:].reshape(4, 1000)            # base not 16-byte aligned
