@@ -740,8 +740,19 @@ __global__ __launch_bounds__(256) void wq_reduce_kernel(const float* __restrict_
     return;
   }
   if (i + 4 <= count && count % 4 == 0) {
-    v4f acc = *reinterpret_cast<const v4f*>(part + i);
-    for (int p = 1; p < splits; ++p) acc += *reinterpret_cast<const v4f*>(part + p * count + i);
+    // Up to eight planes' loads in flight at a time, added in plane order.
+    auto plane = [&](int p) { return *reinterpret_cast<const v4f*>(part + p * count + i); };
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < splits; p0 += 8) {
+      v4f t[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t[q] = p0 + q < splits ? plane(p0 + q) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (p0 + q >= splits) break;
+        acc = p0 + q == 0 ? t[q] : acc + t[q];  // no +0 added: a -0 sum keeps its sign
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) put_out<OUT>(out, i + e, acc[e] * alpha);
   } else {
