@@ -124,8 +124,11 @@ const char* qlinear_status_string(int status);
  * w: float8_e4m3fn [N, K]; x: bfloat16 [K]; out: [N] of out_dtype (F32 or
  * BF16).  alpha = 1 returns the raw product; any other alpha is the
  * per-tensor weight_scale folded in float32 before the single output
- * rounding.  Any K >= 1 and any alignment are accepted; rows that are
- * 16-byte aligned (K % 16 == 0, aligned bases) take the wide-load path.
+ * rounding.  Any K >= 1 and any alignment are accepted.  With x 16-byte
+ * aligned the weight is read with 16-byte loads at any K and weight
+ * alignment (rows that start off a 16-byte boundary, e.g. K = 2050, are
+ * shifted into place in registers; the loads stay inside the 16-byte blocks
+ * that hold the weight's bytes); an unaligned x takes a byte-load kernel.
  */
 int qlinear_fp8_gemv(const void* w, const void* x, void* out, int out_dtype,
                      int64_t N, int64_t K, float alpha, void* stream);
