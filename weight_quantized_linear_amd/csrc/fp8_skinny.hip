@@ -576,13 +576,8 @@ template <int MG, int NWB, int KS, bool FUSED>
 hipError_t launch_xlds_nwb(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int M, int N, int K,
                            float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
   auto kern = fp8_skinny_xlds_kernel<MG, NWB, KS, FUSED>;
-  static bool attr_set = false;  // one flag per instantiation
-  if (!attr_set) {
-    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds))
-      return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // per instantiation, one bit per device
+  if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), kMaxLds, lds_set)) return e;
   const int64_t lds = int64_t(K / 256) * MG * 2048 + (KS > 1 ? NWB * kWave * 4 : 0);
   const int64_t groups = (int64_t(N) + 3) / 4;
   constexpr int kGpb = NWB / KS;
@@ -638,13 +633,10 @@ hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* o
   splits = (K + ksl - 1) / ksl;
   if (size_t(splits) * size_t(M) * size_t(N) * 4 > ws_bytes) return hipErrorInvalidValue;
   const int lds = int(16 * (2 * ksl + 16));
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fp8_skinny_splitk_kernel<kNW, kU>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds))
-      return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(fp8_skinny_splitk_kernel<kNW, kU>), kMaxLds,
+                                     lds_set))
+    return e;
   if (hipError_t e = launch(fp8_skinny_splitk_kernel<kNW, kU>, dim3(unsigned(row_blocks), unsigned(splits)),
                             dim3(kNW * kWave), size_t(lds), s, w, x, ws, int(M), N, K, int(ksl)))
     return e;

@@ -498,13 +498,8 @@ struct Slab {
 // Raise the kernel's dynamic LDS limit once per kernel, then launch.
 template <auto Kernel, class... Args>
 hipError_t launch_big_lds(int lds_bytes, int64_t blocks, int threads, hipStream_t s, Args... args) {
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // per kernel, one bit per device
+  if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(Kernel), lds_bytes, lds_set)) return e;
   return launch(Kernel, dim3(blocks), dim3(threads), lds_bytes, s, args...);
 }
 
@@ -1644,13 +1639,8 @@ hipError_t launch_grouped_cfg(typename WP<BN, 1, NW>::Args wa, const uint16_t* x
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   auto go = [&](auto kernel) -> hipError_t {
     // The LDS size depends on G: raise the kernel's limit to the maximum once.
-    static bool attr = false;
-    if (!attr) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kernel), kMaxLds, lds_set)) return e;
     return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, x, wa, a_offsets, expert_ids, expert_scale, out, G,
                   T, N, K, E, vec);
   };
@@ -1739,13 +1729,8 @@ hipError_t launch_int8_grouped_cfg(const int8_t* a, const int8_t* b, const float
   const int es = out_mode == 1 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   auto go = [&](auto kernel) -> hipError_t {
-    static bool attr = false;
-    if (!attr) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kernel), kMaxLds, lds_set)) return e;
     return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, a, b, sa, sb, bias, a_offsets, expert_ids, out,
                   G, T, N, K, E, vec);
   };

@@ -6,9 +6,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "epilogue.hpp"
 
 namespace qlinear {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device: the attribute belongs to the device the call is made on, so a
+// process that launches on several GPUs sets it on each.  `done` keeps one
+// bit per device id below 64 (higher ids set it on every call); concurrent
+// first calls from several host threads may both set it, which is harmless.
+inline hipError_t raise_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  if (hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); e != hipSuccess)
+    return e;
+  done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 template <typename T> struct same_type { using type = T; };
 
