@@ -78,3 +78,36 @@ def test_gemm_rejects_bad_arguments(q):
     assert L.qlinear_fp8_gemm_path(FAKE, FAKE, FAKE, 0, 4, 8, 16, 1.0, 9, None) == q.ERR_INVALID_ARG
     assert L.qlinear_fp8_materialize(FAKE, None, 0, 4, 4, None) == q.ERR_INVALID_ARG
     assert L.qlinear_fp8_materialize(FAKE, FAKE, 2, 4, 4, None) == q.ERR_INVALID_ARG
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "qlinear.h"
+int main(void) {
+  if (qlinear_abi_version() != 1) return 1;
+  if (strcmp(qlinear_status_string(QLINEAR_OK), "ok") != 0) return 2;
+  if (qlinear_fp8_gemv(NULL, NULL, NULL, QLINEAR_F32, 8, 16, 1.0f, NULL) != QLINEAR_ERR_INVALID_ARG) return 3;
+  if (qlinear_int8_quantize_act(NULL, NULL, NULL, 4, 4, NULL) != QLINEAR_ERR_INVALID_ARG) return 4;
+  puts("c client ok");
+  return 0;
+}
+"""
+
+
+@pytest.mark.skipif(subprocess.run(["which", "gcc"], capture_output=True).returncode != 0, reason="no gcc")
+def test_plain_c_client_compiles_links_and_runs(q, tmp_path):
+    """The header is plain C99 (and valid C++17); a C program links against
+    the library and calls it (no device work: version, status text, argument
+    rejection)."""
+    inc = os.path.join(ROOT, "include")
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(q.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{inc}", str(src),
+                    f"-L{libdir}", "-lqlinear", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    run = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert run.returncode == 0 and run.stdout.strip() == "c client ok", (run.returncode, run.stdout, run.stderr)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", "c++",
+                    HEADER], check=True)
