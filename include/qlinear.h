@@ -15,21 +15,22 @@
  * - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
  *   stream).  Every call only enqueues work on it and returns; nothing
  *   synchronises.  Outputs are valid once the stream has reached the work.
- * - Ownership: the caller owns every buffer.  The library keeps no pointer
- *   past the call.  Its state is a per-device cache of the device's
- *   properties and one 32 MiB float32 workspace per device, allocated with
- *   hipMalloc by the first tiled fp8/NVFP4 call on that device that is not
- *   being captured into a graph, and held until the process ends.  Tiled
- *   calls with few output tiles (small M) split K over several blocks and
- *   add the partial sums from that workspace; calls made before it exists
- *   (or if its allocation failed) use whole-K tiles.  Because the workspace
- *   is shared, tiled fp8/NVFP4 calls on one device must not run
- *   concurrently: issue them on one stream, or order the streams.
+ * - Ownership: the caller owns every buffer, including the optional
+ *   float32 workspace of the *_ws calls (split-K partial sums; size from
+ *   qlinear_gemm_workspace_size).  The library allocates and frees nothing,
+ *   keeps no pointer past the call and has no workspace of its own; its only
+ *   state is a per-device cache of the device's properties (architecture,
+ *   CU count).  A call's kernel choice, and so its summation order and
+ *   output bits, depends only on its arguments (shapes, operand alignment,
+ *   the workspace size given) and the device's CU count, never on earlier
+ *   calls.  Calls without a workspace run whole-K tiles.
  * - Errors: the return value (a qlinear_status) is the only error channel.
  *   Arguments are validated before anything is enqueued; on an error nothing
  *   is written.  Device-side contents (offsets, ids) are not validated by the
  *   host; the kernels guard them as documented per call.
- * - Inputs and outputs must not alias.  Calls are thread-safe.
+ * - Inputs and outputs must not alias.  Calls are stateless and
+ *   thread-safe; two calls that run at once (different streams) need
+ *   different output buffers and, if they take one, different workspaces.
  * - Accumulation is float32 (int32 for int8 x int8); float outputs are
  *   rounded once, to nearest even.
  *
@@ -47,12 +48,12 @@
 extern "C" {
 #endif
 
-#define QLINEAR_ABI_VERSION 1
+#define QLINEAR_ABI_VERSION 2
 
 typedef enum qlinear_status {
   QLINEAR_OK = 0,
   QLINEAR_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, bad dtype, bad layout */
-  QLINEAR_ERR_UNSUPPORTED = 2,  /* current device is not gfx950 */
+  QLINEAR_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or a forced kernel family cannot run the call */
   QLINEAR_ERR_DEVICE = 3,       /* no usable HIP device / device query failed */
   QLINEAR_ERR_LAUNCH = 4        /* a kernel launch reported an error */
 } qlinear_status;
@@ -71,6 +72,13 @@ typedef enum qlinear_path {
   QLINEAR_PATH_TILED = 3,   /* LDS-tiled matrix-core GEMM, any M                     */
   QLINEAR_PATH_SPLITK = 4   /* split-K skinny GEMM, M <= 16, K % 64 == 0, aligned    */
 } qlinear_path;
+
+/* Weight format of qlinear_gemm_workspace_size. */
+typedef enum qlinear_weight_format {
+  QLINEAR_WEIGHT_FP8 = 0,    /* qlinear_fp8_gemm_ws   */
+  QLINEAR_WEIGHT_NVFP4 = 1,  /* qlinear_nvfp4_gemm_ws */
+  QLINEAR_WEIGHT_BF16 = 2    /* qlinear_bf16_gemm_ws  */
+} qlinear_weight_format;
 
 /* Activation of a fused epilogue. */
 typedef enum qlinear_activation {
@@ -147,10 +155,9 @@ int qlinear_fp8_gemm(const void* w, const void* x, void* out, int out_dtype,
  * As qlinear_fp8_gemm, with the kernel family forced (tests compare the
  * families with each other).  A family that cannot take the given M returns
  * QLINEAR_ERR_INVALID_ARG.  QLINEAR_PATH_SPLITK (K split over blocks, float32
- * partial planes in the library's workspace added by a second kernel in a
- * fixed order) returns QLINEAR_ERR_UNSUPPORTED, launching nothing, when the
- * shape leaves fewer than two K slices of 256 values or the partial planes
- * exceed the workspace; the automatic choice then takes the skinny kernel.
+ * partial planes added by a second kernel in a fixed order) needs a
+ * workspace, so through this call (which has none) it returns
+ * QLINEAR_ERR_UNSUPPORTED and launches nothing; see qlinear_fp8_gemm_ws.
  */
 int qlinear_fp8_gemm_path(const void* w, const void* x, void* out, int out_dtype,
                           int64_t M, int64_t N, int64_t K, float alpha, int path,
@@ -198,8 +205,9 @@ int qlinear_fp8_grouped_gemm(const void* w, const void* x, const uint32_t* a_off
  * code(n, 2j+1) in the high nibble; w_scale: float8_e4m3fn [N, K/16];
  * x: bfloat16 [M, K]; out: [M, N] of out_dtype (F32 or BF16).  K % 16 == 0.
  * alpha is the per-tensor global scale (weight_scale_2; 1 = raw), applied in
- * float32 before the single output rounding.  M <= 4 runs on the vector ALU,
- * larger M dequantises weight tiles to bfloat16 in LDS for the matrix cores.
+ * float32 before the single output rounding.  M <= 4 runs on the vector ALU;
+ * larger M stages the packed codes and block scales in LDS, and each lane
+ * decodes its own matrix-core operand fragment to bfloat16 in registers.
  */
 int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x, void* out,
                        int out_dtype, int64_t M, int64_t N, int64_t K, float alpha,
@@ -305,8 +313,8 @@ int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const 
  * float32 accumulation of exact products.  Any K >= 1 and alignment (both
  * operands 2-byte aligned); K % 8 == 0 with 16-byte aligned operands takes
  * the wide-load kernels.  The kernel families are those of
- * qlinear_fp8_gemm: GEMV (M <= 4), skinny (M <= 16), tiled (any M; the
- * tiled GEMM shares the split-K workspace and its stream-ordering rule).
+ * qlinear_fp8_gemm: GEMV (M <= 4), skinny (M <= 16), tiled (any M; with a
+ * workspace, qlinear_bf16_gemm_ws, small-M tiles split K).
  */
 int qlinear_bf16_gemm(const void* w, const void* x, void* out, int out_dtype,
                       int64_t M, int64_t N, int64_t K, float alpha, void* stream);
@@ -319,7 +327,7 @@ int qlinear_bf16_gemm_path(const void* w, const void* x, void* out, int out_dtyp
 /*
  * qlinear_fp8_gemm / qlinear_nvfp4_gemm / qlinear_bf16_gemm with a fused
  * epilogue (qlinear_epilogue; NULL = the plain call).  Same operands, kernel
- * choice, workspace rule and errors as the plain calls; the _path variant
+ * choice (no workspace) and errors as the plain calls; the _path variant
  * forces the kernel family as qlinear_fp8_gemm_path does.
  */
 int qlinear_fp8_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype,
@@ -334,6 +342,55 @@ int qlinear_nvfp4_gemm_epilogue(const void* w_packed, const void* w_scale, const
 int qlinear_bf16_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype,
                                int64_t M, int64_t N, int64_t K, float alpha,
                                const qlinear_epilogue* epilogue, void* stream);
+
+/*
+ * Split-K workspace size, pages "Matmul2dFp8" (the tiled W8A16 GEMM) and
+ * "fp4_matmul" (the NVFP4 GEMM): with few output tiles (small M) the tiled
+ * and skinny matrix-core kernels split K over several blocks, each writing
+ * a float32 partial-sum plane [M, N] into a caller-provided workspace, and a
+ * second kernel adds the planes in a fixed order.  This only changes the
+ * order of the float32 additions, never what is computed.
+ * *bytes receives the workspace size with which the *_ws call of
+ * `weight_format` (a qlinear_weight_format) and `path` (a qlinear_path)
+ * takes its fastest kernel for (M, N, K) on the current device, assuming
+ * 16-byte aligned operands; 0 means the call takes no workspace there.  A
+ * smaller workspace is not an error: the call then uses fewer K slices or
+ * whole-K tiles.  Reads no device memory and launches nothing.  Returns
+ * QLINEAR_ERR_INVALID_ARG for a null `bytes`, a non-positive size, an unknown
+ * format or path, or NVFP4 K % 16 != 0.
+ */
+int qlinear_gemm_workspace_size(int weight_format, int path, int64_t M, int64_t N, int64_t K,
+                                int64_t* bytes);
+
+/*
+ * The W8A16, NVFP4 and bf16 matmuls with every option: a fused epilogue
+ * (NULL = none), a kernel family (`path`, QLINEAR_PATH_AUTO = the automatic
+ * choice) and a caller-owned split-K workspace: `workspace` is device memory
+ * on the current device, 16-byte aligned, of `workspace_bytes` bytes (NULL
+ * with 0 = none).  Its contents on entry do not matter and on return are
+ * unspecified; it must not be in use by another call that runs at the same
+ * time.  Operands, results and errors otherwise exactly as
+ * qlinear_fp8_gemm(_epilogue_path), qlinear_nvfp4_gemm(_epilogue) and
+ * qlinear_bf16_gemm(_epilogue); the result bits depend only on the
+ * arguments.  A misaligned workspace, workspace_bytes < 0, or a NULL
+ * workspace with workspace_bytes > 0 gives QLINEAR_ERR_INVALID_ARG.
+ * QLINEAR_PATH_SPLITK (qlinear_fp8_gemm_ws only) returns
+ * QLINEAR_ERR_UNSUPPORTED, launching nothing, when the shape leaves fewer
+ * than two K slices of 256 values or the partial planes exceed the
+ * workspace.
+ */
+int qlinear_fp8_gemm_ws(const void* w, const void* x, void* out, int out_dtype,
+                        int64_t M, int64_t N, int64_t K, float alpha,
+                        const qlinear_epilogue* epilogue, int path, void* workspace,
+                        int64_t workspace_bytes, void* stream);
+int qlinear_nvfp4_gemm_ws(const void* w_packed, const void* w_scale, const void* x, void* out,
+                          int out_dtype, int64_t M, int64_t N, int64_t K, float alpha,
+                          const qlinear_epilogue* epilogue, int path, void* workspace,
+                          int64_t workspace_bytes, void* stream);
+int qlinear_bf16_gemm_ws(const void* w, const void* x, void* out, int out_dtype,
+                         int64_t M, int64_t N, int64_t K, float alpha,
+                         const qlinear_epilogue* epilogue, int path, void* workspace,
+                         int64_t workspace_bytes, void* stream);
 
 /*
  * Grouped matmuls with the per-expert weight scale folded in: page

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(q):
 
 
 def test_version_and_status_strings(q):
-    assert q.lib.qlinear_abi_version() == 1
+    assert q.lib.qlinear_abi_version() == 2
     assert q.lib.qlinear_status_string(0) == b"ok"
     for s in range(1, 5):
         assert q.lib.qlinear_status_string(s) not in (b"ok", b"unknown status")
@@ -80,15 +80,38 @@ def test_gemm_rejects_bad_arguments(q):
     assert L.qlinear_fp8_materialize(FAKE, FAKE, 2, 4, 4, None) == q.ERR_INVALID_ARG
 
 
+def test_workspace_arguments_rejected_before_device_work(q):
+    """The caller-owned split-K workspace: a misaligned one, a negative size or
+    a NULL one with a size are argument errors, answered before any device
+    query; so are bad arguments of the size query."""
+    L = q.lib
+    ws_bad = [(ctypes.c_void_p(0x10008), 1024), (FAKE, -1), (None, 64)]
+    for ws, nb in ws_bad:
+        assert L.qlinear_fp8_gemm_ws(FAKE, FAKE, FAKE, 0, 32, 64, 64, 1.0, None, 0, ws, nb, None) == q.ERR_INVALID_ARG
+        assert L.qlinear_bf16_gemm_ws(FAKE, FAKE, FAKE, 0, 32, 64, 64, 1.0, None, 0, ws, nb, None) == \
+            q.ERR_INVALID_ARG
+        assert L.qlinear_nvfp4_gemm_ws(FAKE, FAKE, FAKE, FAKE, 0, 32, 64, 64, 1.0, None, 0, ws, nb, None) == \
+            q.ERR_INVALID_ARG
+    b = ctypes.c_int64(-5)
+    assert L.qlinear_gemm_workspace_size(0, 0, 16, 64, 64, None) == q.ERR_INVALID_ARG
+    assert L.qlinear_gemm_workspace_size(3, 0, 16, 64, 64, ctypes.byref(b)) == q.ERR_INVALID_ARG  # format
+    assert b.value == 0
+    assert L.qlinear_gemm_workspace_size(0, 5, 16, 64, 64, ctypes.byref(b)) == q.ERR_INVALID_ARG  # path
+    assert L.qlinear_gemm_workspace_size(1, 0, 16, 64, 40, ctypes.byref(b)) == q.ERR_INVALID_ARG  # NVFP4 K % 16
+    assert L.qlinear_gemm_workspace_size(0, 0, 0, 64, 64, ctypes.byref(b)) == q.ERR_INVALID_ARG  # M = 0
+
+
 C_CLIENT = r"""
 #include <stdio.h>
 #include <string.h>
 #include "qlinear.h"
 int main(void) {
-  if (qlinear_abi_version() != 1) return 1;
+  if (qlinear_abi_version() != QLINEAR_ABI_VERSION) return 1;
   if (strcmp(qlinear_status_string(QLINEAR_OK), "ok") != 0) return 2;
   if (qlinear_fp8_gemv(NULL, NULL, NULL, QLINEAR_F32, 8, 16, 1.0f, NULL) != QLINEAR_ERR_INVALID_ARG) return 3;
   if (qlinear_int8_quantize_act(NULL, NULL, NULL, 4, 4, NULL) != QLINEAR_ERR_INVALID_ARG) return 4;
+  if (qlinear_gemm_workspace_size(QLINEAR_WEIGHT_FP8, QLINEAR_PATH_AUTO, 16, 64, 64, NULL) != QLINEAR_ERR_INVALID_ARG)
+    return 5;
   puts("c client ok");
   return 0;
 }

@@ -37,6 +37,10 @@ __all__ = [
     "int8_quantize_act",
     "int8_gemm",
     "PATHS",
+    "gemm_workspace_bytes",
+    "WEIGHT_FP8",
+    "WEIGHT_NVFP4",
+    "WEIGHT_BF16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlinear.so")
@@ -83,7 +87,13 @@ EXPORTED = {
     "qlinear_fp8_grouped_gemm_scaled": [_p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_nvfp4_grouped_gemm_scaled": [_p, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
     "qlinear_int8_grouped_gemm": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i64, _i64, _i64, _p],
+    "qlinear_gemm_workspace_size": [_i, _i, _i64, _i64, _i64, ctypes.POINTER(_i64)],
+    "qlinear_fp8_gemm_ws": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p, _i64, _p],
+    "qlinear_nvfp4_gemm_ws": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p, _i64, _p],
+    "qlinear_bf16_gemm_ws": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p, _i64, _p],
 }
+
+WEIGHT_FP8, WEIGHT_NVFP4, WEIGHT_BF16 = 0, 1, 2
 
 
 def _load():
@@ -183,14 +193,42 @@ def _epi_ref(d):
     return ctypes.byref(d) if d is not None else None
 
 
+def gemm_workspace_bytes(weight_format: int, m: int, n: int, k: int, path: str = "auto") -> int:
+    """Bytes of split-K workspace the ``*_gemm_ws`` call of ``weight_format``
+    (WEIGHT_FP8 / WEIGHT_NVFP4 / WEIGHT_BF16) takes for (m, n, k) on the
+    current device (``qlinear_gemm_workspace_size``); 0 = none."""
+    b = _i64(0)
+    _check(lib.qlinear_gemm_workspace_size(weight_format, PATHS[path], m, n, k, ctypes.byref(b)),
+           "qlinear_gemm_workspace_size")
+    return int(b.value)
+
+
+def _workspace(workspace, weight_format: int, m: int, n: int, k: int, path: str, device):
+    """(pointer, bytes, tensor) of the split-K workspace: "auto" allocates what
+    the call takes (a torch tensor, so torch's caching allocator serves it),
+    None passes none (whole-K tiles), a tensor is used as given."""
+    if workspace is None:
+        return None, 0, None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a device tensor")
+        nbytes = gemm_workspace_bytes(weight_format, m, n, k, path)
+        if nbytes == 0:
+            return None, 0, None
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _require(workspace, "workspace")
+    return _ptr(workspace), workspace.numel() * workspace.element_size(), workspace
+
+
 def fp8_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
              out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto",
              row_scale: torch.Tensor | None = None, col_scale: torch.Tensor | None = None,
              bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-             activation: str = "none") -> torch.Tensor:
-    """out[M, N] = alpha * x[M, K] @ dec_e4m3(w[N, K])^T (``qlinear_fp8_gemm``); with
-    any of row_scale / col_scale / bias / residual / activation, the fused epilogue
-    of ``qlinear_fp8_gemm_epilogue_path``."""
+             activation: str = "none", workspace="auto") -> torch.Tensor:
+    """out[M, N] = alpha * x[M, K] @ dec_e4m3(w[N, K])^T (``qlinear_fp8_gemm_ws``), with
+    the fused epilogue of any of row_scale / col_scale / bias / residual / activation,
+    the kernel family ``path`` and the split-K ``workspace`` ("auto": allocated to the
+    size ``qlinear_gemm_workspace_size`` gives; None: none)."""
     w = _as_u8(w, "w")
     x = _as_bf16(x, "x")
     _require(w, "w")
@@ -201,14 +239,10 @@ def fp8_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     n = w.shape[0]
     out = _out(out, (m, n), out_dtype, x.device)
     d = _epilogue(m, n, row_scale, col_scale, bias, residual, activation)
-    if d is not None:
-        st = lib.qlinear_fp8_gemm_epilogue_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
-                                                float(alpha), _epi_ref(d), PATHS[path], _stream(x))
-        _check(st, "qlinear_fp8_gemm_epilogue")
-        return out
-    st = lib.qlinear_fp8_gemm_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
-                                   float(alpha), PATHS[path], _stream(x))
-    _check(st, "qlinear_fp8_gemm")
+    wsp, wsb, _keep = _workspace(workspace, WEIGHT_FP8, m, n, k, path, x.device)
+    st = lib.qlinear_fp8_gemm_ws(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k, float(alpha),
+                                 _epi_ref(d), PATHS[path], wsp, wsb, _stream(x))
+    _check(st, "qlinear_fp8_gemm_ws")
     return out
 
 
@@ -216,9 +250,9 @@ def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
               out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto",
               row_scale: torch.Tensor | None = None, col_scale: torch.Tensor | None = None,
               bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-              activation: str = "none") -> torch.Tensor:
-    """Dense bf16 control: out[M, N] = alpha * x[M, K] @ w[N, K]^T (``qlinear_bf16_gemm``);
-    with an epilogue argument, ``qlinear_bf16_gemm_epilogue`` (automatic kernel choice)."""
+              activation: str = "none", workspace="auto") -> torch.Tensor:
+    """Dense bf16 control: out[M, N] = alpha * x[M, K] @ w[N, K]^T (``qlinear_bf16_gemm_ws``);
+    epilogue, ``path`` and ``workspace`` as ``fp8_gemm``."""
     w = _as_bf16(w, "w")
     x = _as_bf16(x, "x")
     _require(w, "w")
@@ -229,16 +263,10 @@ def bf16_gemm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     n = w.shape[0]
     out = _out(out, (m, n), out_dtype, x.device)
     d = _epilogue(m, n, row_scale, col_scale, bias, residual, activation)
-    if d is not None:
-        if path != "auto":
-            raise ValueError("the bf16 epilogue call chooses its kernel itself (path='auto')")
-        st = lib.qlinear_bf16_gemm_epilogue(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
-                                            float(alpha), _epi_ref(d), _stream(x))
-        _check(st, "qlinear_bf16_gemm_epilogue")
-        return out
-    st = lib.qlinear_bf16_gemm_path(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
-                                    float(alpha), PATHS[path], _stream(x))
-    _check(st, "qlinear_bf16_gemm")
+    wsp, wsb, _keep = _workspace(workspace, WEIGHT_BF16, m, n, k, path, x.device)
+    st = lib.qlinear_bf16_gemm_ws(_ptr(w), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k, float(alpha),
+                                  _epi_ref(d), PATHS[path], wsp, wsb, _stream(x))
+    _check(st, "qlinear_bf16_gemm_ws")
     return out
 
 
@@ -384,9 +412,9 @@ def nvfp4_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, o
                out_dtype: torch.dtype = torch.bfloat16, alpha: float = 1.0, path: str = "auto",
                row_scale: torch.Tensor | None = None, col_scale: torch.Tensor | None = None,
                bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-               activation: str = "none") -> torch.Tensor:
-    """out[M, N] = alpha * x[M, K] @ D^T, D the NVFP4 weight (``qlinear_nvfp4_gemm``); with
-    an epilogue argument, ``qlinear_nvfp4_gemm_epilogue`` (automatic kernel choice)."""
+               activation: str = "none", workspace="auto") -> torch.Tensor:
+    """out[M, N] = alpha * x[M, K] @ D^T, D the NVFP4 weight (``qlinear_nvfp4_gemm_ws``);
+    epilogue, ``path`` and ``workspace`` as ``fp8_gemm``."""
     p = _as_u8(w_packed, "w_packed")
     sc = _as_u8(w_scale, "w_scale")
     x = _as_bf16(x, "x")
@@ -398,16 +426,10 @@ def nvfp4_gemm(w_packed: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, o
         raise ValueError("w_packed must be [N, K/2] and w_scale [N, K/16]")
     out = _out(out, (m, n), out_dtype, x.device)
     d = _epilogue(m, n, row_scale, col_scale, bias, residual, activation)
-    if d is not None:
-        if path != "auto":
-            raise ValueError("the NVFP4 epilogue call chooses its kernel itself (path='auto')")
-        st = lib.qlinear_nvfp4_gemm_epilogue(_ptr(p), _ptr(sc), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
-                                             float(alpha), _epi_ref(d), _stream(x))
-        _check(st, "qlinear_nvfp4_gemm_epilogue")
-        return out
-    st = lib.qlinear_nvfp4_gemm_path(_ptr(p), _ptr(sc), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
-                                     float(alpha), PATHS[path], _stream(x))
-    _check(st, "qlinear_nvfp4_gemm")
+    wsp, wsb, _keep = _workspace(workspace, WEIGHT_NVFP4, m, n, k, path, x.device)
+    st = lib.qlinear_nvfp4_gemm_ws(_ptr(p), _ptr(sc), _ptr(x), _ptr(out), _OUT_CODES[out_dtype], m, n, k,
+                                   float(alpha), _epi_ref(d), PATHS[path], wsp, wsb, _stream(x))
+    _check(st, "qlinear_nvfp4_gemm_ws")
     return out
 
 

@@ -619,18 +619,42 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
 // slice) pairs to give every CU a block, partial planes within the
 // workspace.  Returns hipErrorInvalidValue when the shape or workspace does
 // not suit it (the caller then takes another kernel).
+namespace {
+
+constexpr int kSplitNW = 8, kSplitU = 4;
+
+// K slices of the split-K skinny kernel for (M, N, K): slices of at most
+// 4096 and at least 256 values, enough (row block, slice) pairs to cover
+// the CUs.  Fills *ksl; 0 when the shape does not suit the kernel.
+int64_t skinny_splits(int64_t M, int64_t N, int64_t K, int num_cus, int64_t* ksl) {
+  if (M < 1 || M > 16 || K % 64 != 0) return 0;
+  const int64_t row_blocks = (N + 16 * kSplitNW - 1) / (16 * kSplitNW);
+  int64_t splits = (num_cus + row_blocks - 1) / row_blocks;
+  splits = std::min<int64_t>(splits, K / 256);
+  if (splits < 2) return 0;
+  int64_t k = ((K + splits - 1) / splits + 63) / 64 * 64;
+  k = std::min<int64_t>(k, 4096);
+  *ksl = k;
+  return (K + k - 1) / k;
+}
+
+}  // namespace
+
+size_t fp8_skinny_splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+  int64_t ksl = 0;
+  const int64_t splits = skinny_splits(M, N, K, num_cus, &ksl);
+  return splits > 1 ? size_t(splits) * size_t(M) * size_t(N) * 4 : 0;
+}
+
 hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
                                    int64_t N, int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes,
                                    hipStream_t s, const Epilogue& epi) {
-  constexpr int kNW = 8, kU = 4;
-  if (M < 1 || M > 16 || K % 64 != 0 || !ws) return hipErrorInvalidValue;
-  const int64_t row_blocks = (N + 16 * kNW - 1) / (16 * kNW);
-  int64_t splits = (num_cus + row_blocks - 1) / row_blocks;
-  splits = std::min<int64_t>(splits, K / 256);
+  constexpr int kNW = kSplitNW, kU = kSplitU;
+  if (!ws) return hipErrorInvalidValue;
+  int64_t ksl = 0;
+  const int64_t splits = skinny_splits(M, N, K, num_cus, &ksl);
   if (splits < 2) return hipErrorInvalidValue;
-  int64_t ksl = ((K + splits - 1) / splits + 63) / 64 * 64;
-  ksl = std::min<int64_t>(ksl, 4096);
-  splits = (K + ksl - 1) / ksl;
+  const int64_t row_blocks = (N + 16 * kNW - 1) / (16 * kNW);
   if (size_t(splits) * size_t(M) * size_t(N) * 4 > ws_bytes) return hipErrorInvalidValue;
   const int lds = int(16 * (2 * ksl + 16));
   static std::atomic<uint64_t> lds_set{0};

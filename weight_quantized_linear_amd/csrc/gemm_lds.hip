@@ -906,6 +906,9 @@ int splitk_count(int64_t nt, int64_t M, int64_t N, int64_t K, int num_cus, size_
   return sp < 2 ? 1 : int(sp);
 }
 
+// Partial-plane bytes of `sp` K slices of an [M, N] output (0 for whole-K).
+size_t planes_bytes(int sp, int64_t M, int64_t N) { return sp > 1 ? size_t(sp) * size_t(M) * size_t(N) * 4 : 0; }
+
 // ---------------------------------------------------------------- W8A8 int8
 //
 // Strips are 64 bytes per row (4 chunks); step t, half h reads chunk 2t + h
@@ -1587,6 +1590,25 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   if (tiles(M, N, 128, 256) >= num_cus / 2)
     return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+}
+
+// Workspace bytes with which the launchers above take their split-K kernels
+// for (M, N, K) on a device with num_cus CUs (0: they run whole-K tiles).
+// These mirror the launchers' own choice made with an unbounded workspace.
+size_t fp8_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, SIZE_MAX), M, N);
+}
+
+size_t nvfp4_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+  if (M <= 256) {
+    const int sp = splitk_count(tiles(M, N, 64, 128), M, N, K, num_cus, SIZE_MAX);
+    if (sp > 1) return planes_bytes(sp, M, N);
+  }
+  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, SIZE_MAX), M, N);
+}
+
+size_t bf16_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+  return fp8_gemm_lds_ws_bytes(M, N, K, num_cus);
 }
 
 hipError_t launch_splitk_reduce(const float* part, void* out, int out_bf16, int64_t M, int64_t N, int splits,

@@ -61,6 +61,8 @@ hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* o
                                    hipStream_t s, const Epilogue& epi = Epilogue{});
 hipError_t launch_splitk_reduce(const float* part, void* out, int out_bf16, int64_t M, int64_t N, int splits,
                                 float alpha, hipStream_t s, const Epilogue& epi = Epilogue{});
+// Workspace bytes the split-K skinny kernel takes for (M, N, K) (0: it does not apply).
+size_t fp8_skinny_splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
 
 // gemm_bf16.hip (dispatches to gemm_lds.hip when K % 64 == 0 and operands are aligned)
 hipError_t launch_fp8_tiled(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
@@ -72,9 +74,13 @@ hipError_t launch_nvfp4_tiled(const uint8_t* packed, const uint8_t* scales, cons
 
 // gemm_lds.hip
 bool gemm_lds_supported(const void* x, const void* w, const void* scales, int64_t M, int64_t N, int64_t K);
-// ws / ws_bytes: float32 workspace for split-K partial sums (null: whole-K tiles only).
+// ws / ws_bytes: the caller's float32 workspace for split-K partial sums (null: whole-K tiles only).
 hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
                                int64_t K, float alpha, int num_cus, float* ws, size_t ws_bytes, hipStream_t s, const Epilogue& epi = Epilogue{});
+// Workspace bytes with which the LDS GEMMs take their split-K kernels (0: whole-K tiles).
+size_t fp8_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
+size_t nvfp4_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
+size_t bf16_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
 bool int8_lds_supported(const void* a, const void* b, int64_t M, int64_t N, int64_t K);
 hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
                                 const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,

@@ -18,24 +18,15 @@ using namespace qlinear;
 
 constexpr int kMaxDevices = 64;
 
-// Split-K partial sums of small-M tiled GEMMs need a float32 workspace; the
-// library holds one per device for the life of the process.  Tiled calls on
-// one device therefore must not run concurrently (one stream, or streams
-// ordered by events), as the header states.
-constexpr size_t kWorkspaceBytes = size_t(32) << 20;
-
 struct DeviceInfo {
   std::atomic<int> state{0};  // 0 unknown, 1 gfx950, 2 other arch, 3 query failed
   int num_cus = 0;
-  std::atomic<float*> ws{nullptr};
-  bool ws_failed = false;
 };
 DeviceInfo g_devices[kMaxDevices];
 std::mutex g_device_mutex;
 
-// Status of the current device, cached per device index; fills num_cus (and
-// the device slot, for the workspace).
-int current_device(int* num_cus, DeviceInfo** info = nullptr) {
+// Status of the current device, cached per device index; fills num_cus.
+int current_device(int* num_cus) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLINEAR_ERR_DEVICE;
   DeviceInfo& d = g_devices[dev];
@@ -57,31 +48,7 @@ int current_device(int* num_cus, DeviceInfo** info = nullptr) {
   if (st == 3) return QLINEAR_ERR_DEVICE;
   if (st == 2) return QLINEAR_ERR_UNSUPPORTED;
   *num_cus = d.num_cus > 0 ? d.num_cus : 256;
-  if (info) *info = &d;
   return QLINEAR_OK;
-}
-
-// The device's split-K workspace, allocated on the first tiled call that is
-// not being captured into a graph.  Null (whole-K tiles only) before that or
-// if the allocation failed.
-float* workspace(DeviceInfo* d, hipStream_t s) {
-  float* w = d->ws.load(std::memory_order_acquire);
-  if (w) return w;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  std::lock_guard<std::mutex> lock(g_device_mutex);
-  w = d->ws.load(std::memory_order_relaxed);
-  if (!w && !d->ws_failed) {
-    void* p = nullptr;
-    if (hipMalloc(&p, kWorkspaceBytes) == hipSuccess) {
-      w = static_cast<float*>(p);
-      d->ws.store(w, std::memory_order_release);
-    } else {
-      d->ws_failed = true;
-      (void)hipGetLastError();
-    }
-  }
-  return w;
 }
 
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
@@ -125,41 +92,71 @@ int to_epilogue(const qlinear_epilogue* e, int64_t M, int64_t N, Epilogue* out) 
   return QLINEAR_OK;
 }
 
-int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
-                  int64_t K, float alpha, int path, void* stream, const qlinear_epilogue* epilogue = nullptr) {
+// A caller's split-K workspace: NULL (with 0 bytes) for none, else at least
+// 16-byte aligned device memory of workspace_bytes >= 0 bytes.
+int check_workspace(const void* ws, int64_t ws_bytes) {
+  if (ws_bytes < 0 || (!ws && ws_bytes != 0) || (ws && !aligned(ws, 16))) return QLINEAR_ERR_INVALID_ARG;
+  return QLINEAR_OK;
+}
+
+// The FP8 kernel family that a call takes: `path` if forced, else the
+// automatic choice, which depends on the shape, the operands' alignment and
+// whether a workspace of at least `ws_need` bytes is given (and on nothing
+// else, so that a call is reproducible from its arguments).
+int fp8_choose(int path, int64_t M, int64_t N, int64_t K, bool wide, bool splitk_ok) {
+  if (path != QLINEAR_PATH_AUTO) return path;
+  // Measured on the decode shapes: the vector-ALU GEMV wins for M <= 2
+  // below 65536 output features and for M <= 4 on small weights; the
+  // matrix-core skinny kernels win above that (for 3 <= M <= 4 from 8192
+  // output features or a K of 8192 when the activation-in-LDS kernel
+  // applies) and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
+  const bool big = N >= 65536 || (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K));
+  if (M == 1) return QLINEAR_PATH_GEMV;
+  if (M <= 4) return (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
+  // For 9 <= M <= 16 with a long K and fewer than 65536 output features the
+  // split-K skinny kernel wins (M = 16, N = 4096, K = 14336: 19.2 us against
+  // 23.1 us) when the caller gives it a workspace.
+  if (M <= 16 && wide)
+    return (splitk_ok && M > 8 && K >= 8192 && K % 64 == 0 && N < 65536) ? QLINEAR_PATH_SPLITK
+                                                                          : QLINEAR_PATH_SKINNY;
+  return QLINEAR_PATH_TILED;
+}
+
+int nvfp4_choose(int path, int64_t M) {
+  if (path != QLINEAR_PATH_AUTO) return path;
+  return M <= 4 ? QLINEAR_PATH_GEMV : QLINEAR_PATH_TILED;
+}
+
+int bf16_choose(int path, int64_t M, bool wide) {
+  if (path != QLINEAR_PATH_AUTO) return path;
+  if (M <= 4) return QLINEAR_PATH_GEMV;
+  if (M <= 16 && wide) return QLINEAR_PATH_SKINNY;
+  return QLINEAR_PATH_TILED;
+}
+
+}  // namespace
+
+namespace qlinear {
+
+int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                  float alpha, int path, void* ws, int64_t ws_bytes, void* stream,
+                  const qlinear_epilogue* epilogue = nullptr) {
   if (!w || !x || !out) return QLINEAR_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return QLINEAR_ERR_INVALID_ARG;
   if (!float_out_ok(out_dtype)) return QLINEAR_ERR_INVALID_ARG;
   if (!aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
+  if (int st = check_workspace(ws, ws_bytes)) return st;
   const bool wide = K % 16 == 0 && aligned(w, 16) && aligned(x, 16);
-  bool auto_splitk = false;
-  if (path == QLINEAR_PATH_AUTO) {
-    // Measured on the decode shapes: the vector-ALU GEMV wins for M <= 2
-    // below 65536 output features and for M <= 4 on small weights; the
-    // matrix-core skinny kernels win above that (for 3 <= M <= 4 from 8192
-    // output features or a K of 8192 when the activation-in-LDS kernel
-    // applies) and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
-    const bool big = N >= 65536 ||
-                     (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K));
-    // For 9 <= M <= 16 with a long K and fewer than 65536 output features
-    // the split-K skinny kernel wins (M = 16, N = 4096, K = 14336: 19.2 us
-    // against 23.1 us), when the workspace is there.
-    if (M == 1) path = QLINEAR_PATH_GEMV;
-    else if (M <= 4) path = (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
-    else if (M <= 16 && wide) path = (M > 8 && K >= 8192 && K % 64 == 0 && N < 65536) ? QLINEAR_PATH_SPLITK
-                                                                                      : QLINEAR_PATH_SKINNY;
-    else path = QLINEAR_PATH_TILED;
-    auto_splitk = path == QLINEAR_PATH_SPLITK;
-  }
   switch (path) {
+    case QLINEAR_PATH_AUTO:
+    case QLINEAR_PATH_TILED:
+      break;
     case QLINEAR_PATH_GEMV:
       if (M > 4) return QLINEAR_ERR_INVALID_ARG;
       break;
     case QLINEAR_PATH_SKINNY:
       if (M > 16 || !wide) return QLINEAR_ERR_INVALID_ARG;
-      break;
-    case QLINEAR_PATH_TILED:
       break;
     case QLINEAR_PATH_SPLITK:
       if (M > 16 || !wide || K % 64 != 0) return QLINEAR_ERR_INVALID_ARG;
@@ -170,37 +167,50 @@ int fp8_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_
   Epilogue epi;
   if (int st = to_epilogue(epilogue, M, N, &epi)) return st;
   int num_cus = 0;
-  DeviceInfo* dev = nullptr;
-  if (int st = current_device(&num_cus, &dev)) return st;
+  if (int st = current_device(&num_cus)) return st;
+  const size_t splitk_need = fp8_skinny_splitk_ws_bytes(M, N, K, num_cus);
+  const bool splitk_ok = ws && splitk_need > 0 && splitk_need <= size_t(ws_bytes);
+  path = fp8_choose(path, M, N, K, wide, splitk_ok);
+  // Forced split-K with fewer than two K slices or planes beyond the workspace.
+  if (path == QLINEAR_PATH_SPLITK && !splitk_ok) return QLINEAR_ERR_UNSUPPORTED;
   auto s = static_cast<hipStream_t>(stream);
   auto* wp = static_cast<const uint8_t*>(w);
   auto* xp = static_cast<const uint16_t*>(x);
+  auto* wsp = static_cast<float*>(ws);
   const int bf16 = out_dtype == QLINEAR_BF16;
-  if (path == QLINEAR_PATH_SPLITK) {
-    const hipError_t e = launch_fp8_skinny_splitk(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s),
-                                                  kWorkspaceBytes, s, epi);
-    if (e != hipErrorInvalidValue) return finish(e);
-    // Shape or workspace unsuitable (nothing was launched).
-    if (!auto_splitk) return QLINEAR_ERR_UNSUPPORTED;
-    path = QLINEAR_PATH_SKINNY;
-  }
+  if (path == QLINEAR_PATH_SPLITK)
+    return finish(launch_fp8_skinny_splitk(wp, xp, out, bf16, M, N, K, alpha, num_cus, wsp, size_t(ws_bytes), s, epi));
   if (path == QLINEAR_PATH_GEMV)
     return finish(launch_fp8_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
   if (path == QLINEAR_PATH_SKINNY)
     return finish(launch_fp8_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
-  return finish(
-      launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s, epi));
+  return finish(launch_fp8_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, wsp, size_t(ws_bytes), s, epi));
 }
 
-int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, int out_dtype, int64_t M,
-                    int64_t N, int64_t K, float alpha, int path, void* stream,
+int fp8_gemm_ws_need(int path, int64_t M, int64_t N, int64_t K, int num_cus, int64_t* bytes) {
+  *bytes = 0;
+  if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N)) return QLINEAR_ERR_INVALID_ARG;
+  const size_t splitk = fp8_skinny_splitk_ws_bytes(M, N, K, num_cus);
+  path = fp8_choose(path, M, N, K, K % 16 == 0, splitk > 0);
+  if (path == QLINEAR_PATH_SPLITK) *bytes = int64_t(splitk);
+  else if (path == QLINEAR_PATH_TILED && K % 64 == 0) *bytes = int64_t(fp8_gemm_lds_ws_bytes(M, N, K, num_cus));
+  return QLINEAR_OK;
+}
+
+}  // namespace qlinear
+
+namespace {
+
+int nvfp4_gemm_impl(const void* wp, const void* wsc, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
+                    int64_t K, float alpha, int path, void* ws, int64_t ws_bytes, void* stream,
                     const qlinear_epilogue* epilogue = nullptr) {
-  if (!wp || !ws || !x || !out) return QLINEAR_ERR_INVALID_ARG;
+  if (!wp || !wsc || !x || !out) return QLINEAR_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return QLINEAR_ERR_INVALID_ARG;
   if (!float_out_ok(out_dtype) || !aligned(x, 2) || !aligned(out, out_size(out_dtype)))
     return QLINEAR_ERR_INVALID_ARG;
-  if (path == QLINEAR_PATH_AUTO) path = M <= 4 ? QLINEAR_PATH_GEMV : QLINEAR_PATH_TILED;
+  if (int st = check_workspace(ws, ws_bytes)) return st;
+  path = nvfp4_choose(path, M);
   if (path == QLINEAR_PATH_GEMV) {
     if (M > 4) return QLINEAR_ERR_INVALID_ARG;
   } else if (path != QLINEAR_PATH_TILED) {
@@ -209,32 +219,29 @@ int nvfp4_gemm_impl(const void* wp, const void* ws, const void* x, void* out, in
   Epilogue epi;
   if (int st = to_epilogue(epilogue, M, N, &epi)) return st;
   int num_cus = 0;
-  DeviceInfo* dev = nullptr;
-  if (int st = current_device(&num_cus, &dev)) return st;
+  if (int st = current_device(&num_cus)) return st;
   auto s = static_cast<hipStream_t>(stream);
   auto* p = static_cast<const uint8_t*>(wp);
-  auto* sc = static_cast<const uint8_t*>(ws);
+  auto* sc = static_cast<const uint8_t*>(wsc);
   auto* xp = static_cast<const uint16_t*>(x);
   const int bf16 = out_dtype == QLINEAR_BF16;
   if (path == QLINEAR_PATH_GEMV)
     return finish(launch_nvfp4_gemv(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
-  return finish(
-      launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s, epi));
+  return finish(launch_nvfp4_tiled(p, sc, xp, out, bf16, M, N, K, alpha, num_cus, static_cast<float*>(ws),
+                                   size_t(ws_bytes), s, epi));
 }
 
 int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
-                   float alpha, int path, void* stream, const qlinear_epilogue* epilogue = nullptr) {
+                   float alpha, int path, void* ws, int64_t ws_bytes, void* stream,
+                   const qlinear_epilogue* epilogue = nullptr) {
   if (!w || !x || !out) return QLINEAR_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N))
     return QLINEAR_ERR_INVALID_ARG;
   if (!float_out_ok(out_dtype)) return QLINEAR_ERR_INVALID_ARG;
   if (!aligned(w, 2) || !aligned(x, 2) || !aligned(out, out_size(out_dtype))) return QLINEAR_ERR_INVALID_ARG;
+  if (int st = check_workspace(ws, ws_bytes)) return st;
   const bool wide = bf16_wide(w, x, K);
-  if (path == QLINEAR_PATH_AUTO) {
-    if (M <= 4) path = QLINEAR_PATH_GEMV;
-    else if (M <= 16 && wide) path = QLINEAR_PATH_SKINNY;
-    else path = QLINEAR_PATH_TILED;
-  }
+  path = bf16_choose(path, M, wide);
   switch (path) {
     case QLINEAR_PATH_GEMV:
       if (M > 4) return QLINEAR_ERR_INVALID_ARG;
@@ -250,8 +257,7 @@ int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64
   Epilogue epi;
   if (int st = to_epilogue(epilogue, M, N, &epi)) return st;
   int num_cus = 0;
-  DeviceInfo* dev = nullptr;
-  if (int st = current_device(&num_cus, &dev)) return st;
+  if (int st = current_device(&num_cus)) return st;
   auto s = static_cast<hipStream_t>(stream);
   auto* wp = static_cast<const uint16_t*>(w);
   auto* xp = static_cast<const uint16_t*>(x);
@@ -260,8 +266,8 @@ int bf16_gemm_impl(const void* w, const void* x, void* out, int out_dtype, int64
     return finish(launch_bf16_gemv(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
   if (path == QLINEAR_PATH_SKINNY)
     return finish(launch_bf16_skinny(wp, xp, out, bf16, M, N, K, alpha, num_cus, s, epi));
-  return finish(
-      launch_bf16_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, workspace(dev, s), kWorkspaceBytes, s, epi));
+  return finish(launch_bf16_tiled(wp, xp, out, bf16, M, N, K, alpha, num_cus, static_cast<float*>(ws),
+                                  size_t(ws_bytes), s, epi));
 }
 
 }  // namespace
@@ -283,17 +289,17 @@ const char* qlinear_status_string(int status) {
 
 int qlinear_fp8_gemv(const void* w, const void* x, void* out, int out_dtype, int64_t N, int64_t K,
                      float alpha, void* stream) {
-  return fp8_gemm_impl(w, x, out, out_dtype, 1, N, K, alpha, QLINEAR_PATH_GEMV, stream);
+  return fp8_gemm_impl(w, x, out, out_dtype, 1, N, K, alpha, QLINEAR_PATH_GEMV, nullptr, 0, stream);
 }
 
 int qlinear_fp8_gemm(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
                      int64_t K, float alpha, void* stream) {
-  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, nullptr, 0, stream);
 }
 
 int qlinear_fp8_gemm_path(const void* w, const void* x, void* out, int out_dtype, int64_t M,
                           int64_t N, int64_t K, float alpha, int path, void* stream) {
-  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream);
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, nullptr, 0, stream);
 }
 
 int qlinear_fp8_materialize(const void* w, void* out, int out_dtype, int64_t N, int64_t K,
@@ -389,13 +395,13 @@ int qlinear_nvfp4_grouped_gemm_scaled(const void* w_packed, const void* w_scale,
 
 int qlinear_nvfp4_gemm(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
                        int64_t M, int64_t N, int64_t K, float alpha, void* stream) {
-  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, nullptr, 0, stream);
 }
 
 int qlinear_nvfp4_gemm_path(const void* w_packed, const void* w_scale, const void* x, void* out,
                             int out_dtype, int64_t M, int64_t N, int64_t K, float alpha, int path,
                             void* stream) {
-  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, path, stream);
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, path, nullptr, 0, stream);
 }
 
 int qlinear_nvfp4_dequant(const void* w_packed, const void* w_scale, void* out, int out_dtype, int64_t N,
@@ -441,33 +447,33 @@ int qlinear_int8_gemm(const void* a, const void* b, const float* a_scale, const 
 
 int qlinear_bf16_gemm(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
                       float alpha, void* stream) {
-  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream);
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, nullptr, 0, stream);
 }
 
 int qlinear_bf16_gemm_path(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
                            float alpha, int path, void* stream) {
-  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream);
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, nullptr, 0, stream);
 }
 
 int qlinear_fp8_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
                               int64_t K, float alpha, const qlinear_epilogue* epilogue, void* stream) {
-  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, nullptr, 0, stream, epilogue);
 }
 
 int qlinear_fp8_gemm_epilogue_path(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
                                    int64_t K, float alpha, const qlinear_epilogue* epilogue, int path, void* stream) {
-  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, stream, epilogue);
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, nullptr, 0, stream, epilogue);
 }
 
 int qlinear_nvfp4_gemm_epilogue(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
                                 int64_t M, int64_t N, int64_t K, float alpha, const qlinear_epilogue* epilogue,
                                 void* stream) {
-  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, nullptr, 0, stream, epilogue);
 }
 
 int qlinear_bf16_gemm_epilogue(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N,
                                int64_t K, float alpha, const qlinear_epilogue* epilogue, void* stream) {
-  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, stream, epilogue);
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, QLINEAR_PATH_AUTO, nullptr, 0, stream, epilogue);
 }
 
 int qlinear_int8_grouped_gemm(const void* a, const void* b, const float* a_scale, const float* b_scale,
@@ -496,6 +502,50 @@ int qlinear_int8_grouped_gemm(const void* a, const void* b, const float* a_scale
                                     mode == 2 ? nullptr : static_cast<const uint16_t*>(bias), a_offsets, expert_ids,
                                     out, mode, num_groups, max_tokens_per_group, num_experts, T, N, K, num_cus,
                                     static_cast<hipStream_t>(stream)));
+}
+
+int qlinear_gemm_workspace_size(int weight_format, int path, int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes) return QLINEAR_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (M <= 0 || N <= 0 || K <= 0 || !fits(N, K) || !fits(M, K) || !fits(M, N)) return QLINEAR_ERR_INVALID_ARG;
+  if (path < QLINEAR_PATH_AUTO || path > QLINEAR_PATH_SPLITK) return QLINEAR_ERR_INVALID_ARG;
+  if (weight_format < QLINEAR_WEIGHT_FP8 || weight_format > QLINEAR_WEIGHT_BF16) return QLINEAR_ERR_INVALID_ARG;
+  if (weight_format == QLINEAR_WEIGHT_NVFP4 && K % 16 != 0) return QLINEAR_ERR_INVALID_ARG;
+  int num_cus = 0;
+  if (int st = current_device(&num_cus)) return st;
+  switch (weight_format) {
+    case QLINEAR_WEIGHT_FP8:
+      return fp8_gemm_ws_need(path, M, N, K, num_cus, bytes);
+    case QLINEAR_WEIGHT_NVFP4:
+      if (nvfp4_choose(path, M) == QLINEAR_PATH_TILED && K % 64 == 0)
+        *bytes = int64_t(nvfp4_gemm_lds_ws_bytes(M, N, K, num_cus));
+      return QLINEAR_OK;
+    case QLINEAR_WEIGHT_BF16:
+      if (bf16_choose(path, M, K % 8 == 0) == QLINEAR_PATH_TILED && K % 64 == 0)
+        *bytes = int64_t(bf16_gemm_lds_ws_bytes(M, N, K, num_cus));
+      return QLINEAR_OK;
+    default:
+      return QLINEAR_ERR_INVALID_ARG;
+  }
+}
+
+int qlinear_fp8_gemm_ws(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                        float alpha, const qlinear_epilogue* epilogue, int path, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  return fp8_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, workspace, workspace_bytes, stream, epilogue);
+}
+
+int qlinear_nvfp4_gemm_ws(const void* w_packed, const void* w_scale, const void* x, void* out, int out_dtype,
+                          int64_t M, int64_t N, int64_t K, float alpha, const qlinear_epilogue* epilogue, int path,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+  return nvfp4_gemm_impl(w_packed, w_scale, x, out, out_dtype, M, N, K, alpha, path, workspace, workspace_bytes,
+                         stream, epilogue);
+}
+
+int qlinear_bf16_gemm_ws(const void* w, const void* x, void* out, int out_dtype, int64_t M, int64_t N, int64_t K,
+                         float alpha, const qlinear_epilogue* epilogue, int path, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  return bf16_gemm_impl(w, x, out, out_dtype, M, N, K, alpha, path, workspace, workspace_bytes, stream, epilogue);
 }
 
 }  // extern "C"
