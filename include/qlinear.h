@@ -282,8 +282,11 @@ int qlinear_nvfp4_dequant(const void* w_packed, const void* w_scale, void* out, 
  *     a_scale[m] = absmax_k |x[m, k]| / 127      (IEEE float32 division)
  *     q[m, k]    = clamp(round_half_even(x[m, k] / a_scale[m]), -127, 127)
  * with IEEE float32 division per element; an all-zero row gives a_scale 0
- * and zero codes; -128 is never produced.  x: bfloat16 [M, K]; q: int8
- * [M, K]; a_scale: float32 [M].  Reads x once per row when K <= 4096.
+ * and zero codes; -128 is never produced.  Non-finite inputs follow the
+ * same formulas: a row holding a NaN gets a_scale NaN, one holding an
+ * infinity (and no NaN) a_scale +inf, and either gets zero codes, so its
+ * dequantised outputs are NaN.  x: bfloat16 [M, K]; q: int8 [M, K];
+ * a_scale: float32 [M].  Reads x once per row when K <= 4096.
  */
 int qlinear_int8_quantize_act(const void* x, void* q, float* a_scale, int64_t M, int64_t K,
                               void* stream);

@@ -35,6 +35,9 @@ __all__ = [
     "clause2_budget",
     "check_f32_tau",
     "epilogue_tolerance",
+    "CLAUSE2_SHARE_F32",
+    "CLAUSE2_SHARE_EPILOGUE",
+    "CLAUSE2_SHARE_F8F6F4",
 ]
 
 REL_TOL = 2e-3
@@ -136,16 +139,35 @@ def check_bf16(gpu_bits, ref, tau) -> CheckResult:
     return CheckResult(True, 0, None, n_clause2=n_c2)
 
 
-def clause2_budget(ref, share: float = 1e-3) -> int:
-    """How many outputs may legitimately need clause 2 of ``check_bf16``.
+# How many outputs may need clause 2 of ``check_bf16``, as a share of the
+# outputs, by the kind of arithmetic behind them.  Each share is a measured
+# rate times a stated margin; the CPU pins of these numbers model the
+# arithmetic and show that plausible mistakes exceed them.
+#
+# * Float32 sums of exact products (W8A16, NVFP4, bf16, grouped, int8
+#   epilogue): clause 1 fails only where the float32 summation error exceeds
+#   one bfloat16 ulp of the result, i.e. for results very near zero.  Plain
+#   sequential float32 summation, the least accurate order, measured 1.05e-5
+#   of 2^20 outputs at K = 4096 (error grows like sqrt(K): about 2e-5 at
+#   K = 14336); the kernels' blocked and tree orders do better.  Share 1e-4.
+# * Fused epilogues: the same rate as float32 sums once the activations are
+#   evaluated without overflow or cancellation (as x sigmoid(z) from
+#   exp(-|z|)): a float32 model of the whole epilogue on the sequential
+#   float32 sum, at real layer magnitudes, measured 1.5e-5 to 3e-5.
+#   Share 1e-4.
+# * The gfx950 fp8 matrix instruction (W8A8): it adds its 64 products more
+#   coarsely than a float32 sum (measured error up to 3e-5 B); about 0.3 % of
+#   the W8A8 workload's outputs need clause 2.  A model that rounds each
+#   64-product block to 14 bits below its sum of magnitudes gives the same
+#   rate.  Share 1e-2.
+CLAUSE2_SHARE_F32 = 1e-4
+CLAUSE2_SHARE_EPILOGUE = 1e-4
+CLAUSE2_SHARE_F8F6F4 = 1e-2
 
-    Clause 1 fails only where the float32 summation error exceeds one
-    bfloat16 ulp of the result, i.e. |result| below about 2^8 sqrt(K) 2^-24
-    times the typical magnitude of the partial sums; for Gaussian data and
-    K <= 14336 that is well under 1e-3 of the outputs.  A kernel whose
-    accumulation is coarser than a float32 sum (still inside the tolerance
-    of ``fp_tolerance``) passes a larger ``share``.  Returns that share of the
-    outputs, plus 2."""
+
+def clause2_budget(ref, share: float = CLAUSE2_SHARE_F32) -> int:
+    """How many outputs may legitimately need clause 2 of ``check_bf16``:
+    ``share`` of the outputs (one of the CLAUSE2_SHARE_* constants), plus 2."""
     return int(share * np.asarray(ref).size) + 2
 
 
@@ -154,17 +176,19 @@ def clause2_budget(ref, share: float = 1e-3) -> int:
 ACT_LIPSCHITZ = {"none": 1.0, "relu": 1.0, "silu": 1.1, "gelu_tanh": 1.13}
 
 
-def epilogue_tolerance(bound, parts, act: str) -> np.ndarray:
+def epilogue_tolerance(bound, parts, act: str, matmul_exact: bool = False) -> np.ndarray:
     """Tolerance of a fused-epilogue output (``oracle.ref.apply_epilogue``).
 
     The matmul's own error, at most ``fp_tolerance(B)``, is multiplied by the
-    scales; the scale products and the bias addition each round once in
-    float32 (u = 2^-24 relative); the activation moves an input error by at
-    most its Lipschitz constant and, evaluated with float32 exp / tanh, adds a
-    few ulps of its input and output magnitude (8 u); the residual addition
-    and the final float32 value round once more."""
+    scales (``matmul_exact``: the raw product is exact -- dyadic inputs -- and
+    this term is zero); the scale products and the bias addition each round
+    once in float32 (u = 2^-24 relative); the activation moves an input error
+    by at most its Lipschitz constant and, evaluated with float32 exp / tanh,
+    adds a few ulps of its input and output magnitude (8 u); the residual
+    addition and the final float32 value round once more."""
     u = 2.0 ** -24
     lip = ACT_LIPSCHITZ[act]
-    t = parts["scale"] * fp_tolerance(bound) + 4 * u * (np.abs(parts["scaled"]) + np.abs(parts["pre"]))
+    mm = 0.0 if matmul_exact else parts["scale"] * fp_tolerance(bound)
+    t = mm + 4 * u * (np.abs(parts["scaled"]) + np.abs(parts["pre"]))
     return lip * t + 8 * u * (np.abs(parts["post"]) + np.abs(parts["pre"])) + \
         2 * u * (parts["residual"] + np.abs(parts["out"]))

@@ -209,7 +209,10 @@ def int8_quantize_act(x_bits):
     returned scale): absmax = max_k |x[m,k]| (exact); a_scale = absmax / 127
     with one IEEE float32 division; q = round-half-even(x / a_scale) with one
     IEEE float32 division, clamped to [-127, 127]; an all-zero row gets
-    a_scale = 0 and q = 0.
+    a_scale = 0 and q = 0.  Non-finite inputs (outside the page's workloads)
+    follow the same formulas: a NaN makes the row's absmax and a_scale NaN,
+    an infinity makes them +inf; such a row's codes are all 0 (every
+    quotient is then NaN or 0), so its dequantised outputs are NaN.
     """
     x = bf16_bits_to_f64(x_bits).astype(np.float32)   # exact widening
     if x.ndim != 2:
@@ -217,7 +220,7 @@ def int8_quantize_act(x_bits):
     absmax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
     a_scale = np.divide(absmax, np.float32(127.0), dtype=np.float32)
     q = np.zeros(x.shape, dtype=np.int8)
-    rows = a_scale > 0
+    rows = (a_scale > 0) & np.isfinite(a_scale)
     if np.any(rows):
         ratio = np.divide(x[rows], a_scale[rows, None], dtype=np.float32)
         q[rows] = np.clip(np.rint(ratio), -127, 127).astype(np.int8)
@@ -253,7 +256,8 @@ def int8_epilogue(acc, a_scale, b_scale, bias_bits=None):
     acc = np.asarray(acc, dtype=np.float64)
     a_s = np.asarray(a_scale, dtype=np.float32).astype(np.float64)
     b_s = np.asarray(b_scale, dtype=np.float32).astype(np.float64)
-    prod = acc * a_s[:, None] * b_s[None, :]
+    with np.errstate(invalid="ignore"):   # 0 * inf: a row whose a_scale is not finite gives NaN
+        prod = acc * a_s[:, None] * b_s[None, :]
     if bias_bits is None:
         bias = np.zeros(acc.shape[1])
     else:
@@ -306,7 +310,8 @@ def fp8_quantize_act(x_bits, input_scale: float) -> np.ndarray:
     s = np.float32(input_scale)
     if not s > 0:
         raise ValueError("input_scale must be positive")
-    v = np.divide(x, s, dtype=np.float32)
+    with np.errstate(over="ignore"):      # quotients beyond float32 saturate at the clamp
+        v = np.divide(x, s, dtype=np.float32)
     v = np.clip(v, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return f64_to_e4m3_codes(v.astype(np.float64))
 
@@ -359,7 +364,11 @@ ACTIVATIONS = ("none", "relu", "silu", "gelu_tanh")
 def activation(v, name: str) -> np.ndarray:
     """The epilogue activations by their definitions, in float64: ReLU
     max(v, 0); SiLU v / (1 + e^-v); GELU in its tanh form
-    0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))."""
+    0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3).  The GELU is
+    evaluated through the identity 1 + tanh(u) = 2 / (1 + e^-2u), i.e. as
+    v / (1 + e^-2u): the same function, but the literal form cancels to 0 in
+    double precision once u < -19 (v below about -6), where the result is
+    still a normal bfloat16 number."""
     v = np.asarray(v, dtype=np.float64)
     if name == "none":
         return v.copy()
@@ -369,7 +378,9 @@ def activation(v, name: str) -> np.ndarray:
         with np.errstate(over="ignore"):
             return v / (1.0 + np.exp(-v))
     if name == "gelu_tanh":
-        return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+        u = np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)
+        with np.errstate(over="ignore"):
+            return v / (1.0 + np.exp(-2.0 * u))
     raise ValueError(f"unknown activation {name!r}")
 
 

@@ -78,6 +78,32 @@ def test_quantizer_quotients_near_half_integers(q):
     assert np.array_equal(qd.cpu().numpy(), want_q)
 
 
+def test_quantizer_non_finite_rows(q):
+    """Rows holding a NaN, +inf or -inf (the reading of the oracle): a_scale
+    NaN / +inf and zero codes, on the vector kernel and on the element-wise
+    kernel (unaligned view); finite rows stay bit-exact."""
+    m, k = 8, 1024
+    x = synth.bf16_activation((62,), m, k + 1, outlier_p=0.01)
+    nan, pinf, ninf = 0x7FC0, 0x7F80, 0xFF80
+    x[1, 17] = nan
+    x[2, 500] = pinf
+    x[3, 3] = ninf
+    x[4, 0], x[4, 900] = pinf, nan
+    x[5, 1000] = 0xFFC1                                   # a negative NaN with a payload
+    for name, xd, xs in (("vector", to_dev_bf16(np.ascontiguousarray(x[:, :k])), x[:, :k]),
+                         ("element-wise", to_dev_bf16(x.reshape(-1))[1:1 + m * k].reshape(m, k),
+                          x.reshape(-1)[1:1 + m * k].reshape(m, k))):
+        show("int8 quantize non-finite", name)
+        qd, sd = q.int8_quantize_act(xd)
+        want_q, want_s = R.int8_quantize_act(xs)
+        got_s = sd.cpu().numpy()
+        assert np.array_equal(np.isnan(got_s), np.isnan(want_s)), name
+        fin = ~np.isnan(want_s)
+        assert np.array_equal(got_s[fin].view(np.uint32), want_s[fin].view(np.uint32)), name
+        assert np.array_equal(qd.cpu().numpy(), want_q), name
+        assert np.sum(~np.isfinite(want_s)) >= 4
+
+
 def test_quantizer_unaligned_view(q):
     x = synth.bf16_activation((61,), 1, 4 * 1000 + 1)
     xd = to_dev_bf16(x)[0, 1:].reshape(4, 1000)            # base not 16-byte aligned

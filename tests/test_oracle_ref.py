@@ -259,6 +259,24 @@ def test_int8_quantize_zero_and_ties():
     assert s[1] == 1.0 and q[1].tolist() == [127, 0, -2]
 
 
+def test_int8_quantize_non_finite_rows():
+    """Reading for inputs outside the workloads: the row formulas applied as
+    written -- a NaN makes absmax and a_scale NaN, an infinity makes them
+    +inf -- and such a row's codes are all zero, so the dequantised output
+    of the row is NaN in every column."""
+    nan, inf = float("nan"), float("inf")
+    rows = np.array([[1.0, nan, -3.0, 2.0], [1.0, inf, -3.0, 2.0], [-inf, 0.5, 4.0, 0.0],
+                     [inf, nan, 1.0, 1.0], [127.0, 1.0, -2.5, 0.0]])
+    q, s = R.int8_quantize_act(F.f64_to_bf16_bits(rows))
+    assert np.isnan(s[0]) and np.isnan(s[3])
+    assert s[1] == np.inf and s[2] == np.inf
+    assert np.all(q[:4] == 0)
+    assert s[4] == 1.0 and q[4].tolist() == [127, 1, -2, 0]
+    b = np.array([[1, -2, 3, 4], [5, 6, -7, 8]], np.int8)
+    out, _ = R.int8_epilogue(R.int8_accumulate(q, b), s, np.array([0.5, 0.25], np.float32))
+    assert np.all(np.isnan(out[:4])) and np.all(np.isfinite(out[4]))
+
+
 def test_int8_accumulate_brute_force():
     r = np.random.default_rng(21)
     for (m, n, k) in ((3, 4, 5), (2, 3, 200), (1, 1, 1)):
@@ -433,6 +451,39 @@ def test_activations_match_torch(name, fn):
     # absolute in |v|: where the factor 1 + tanh(.) cancels (large negative v)
     # the two float64 evaluations agree only to a few ulps of v, not of the result
     assert np.all(np.abs(got - want) <= 1e-14 * (1 + np.abs(v)))
+
+
+def _decimal_activation(v, name):
+    """SiLU / tanh-form GELU from their literal definitions in 400-digit
+    decimal arithmetic (tanh through exp; enough digits that 1 + tanh(u)
+    keeps 40 of them down to v = -20), rounded to float64 at the end."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 400
+        D = decimal.Decimal
+        d = D(repr(float(v)))
+        if name == "silu":
+            return float(d / (1 + (-d).exp()))
+        pi = D("3.14159265358979323846264338327950288419716939937510582097494459230781640628620899")
+        u = (2 / pi).sqrt() * (d + D("0.044715") * d * d * d)
+        e2 = (2 * u).exp()
+        return float(D("0.5") * d * (1 + (e2 - 1) / (e2 + 1)))
+
+
+@pytest.mark.parametrize("name", ["silu", "gelu_tanh"])
+def test_activations_match_high_precision_definition(name):
+    """Relative agreement with the literal definition evaluated in 60 digits,
+    over the whole range that bfloat16 outputs can hold, tails included
+    (for the GELU the float64 literal form would give 0 below v = -6)."""
+    v = np.concatenate([np.linspace(-9, 9, 181), [-12.5, -11.0, -10.25, -7.25, 25.0]])
+    if name == "silu":
+        v = np.concatenate([v, [-95.0, -80.0, -60.0]])
+    got = R.activation(v, name)
+    want = np.array([_decimal_activation(t, name) for t in v])
+    assert np.all(np.abs(got - want) <= 1e-13 * np.abs(want)), np.max(np.abs(got - want) / np.abs(want))
+    if name == "gelu_tanh":      # far tail: far below the smallest bfloat16 (2^-133), as defined
+        tail = R.activation(np.array([-20.0, -40.0, -1e3]), name)
+        assert np.all(np.abs(tail) < 1e-200) and np.all(tail <= 0)
 
 
 @pytest.mark.parametrize("name", ["silu", "gelu_tanh"])

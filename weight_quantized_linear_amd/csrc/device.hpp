@@ -147,6 +147,15 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float acc, float
 // ---------------------------------------------------------------- fused epilogue
 
 // Fused epilogue (the steps are listed at Epilogue) of output element (m, n).
+// x * sigmoid(z), accurate to a few float32 ulps of the result at every z:
+// e = exp(-|z|) never overflows, and neither branch subtracts nearly equal
+// numbers (for z < 0, x e / (1 + e) rather than x / (1 + e^-z)).
+__device__ __forceinline__ float mul_sigmoid(float x, float z) {
+  const float e = expf(-fabsf(z));
+  const float d = 1.f + e;
+  return z >= 0.f ? x / d : x * e / d;
+}
+
 __device__ __forceinline__ float epi_apply(const Epilogue& e, float v, int64_t m, int64_t n) {
   if (e.row_scale) v *= e.row_scale[m];
   if (e.col_scale) v *= e.col_scale[n];
@@ -154,10 +163,12 @@ __device__ __forceinline__ float epi_apply(const Epilogue& e, float v, int64_t m
   if (e.act == 1) {
     v = v > 0.f ? v : 0.f;
   } else if (e.act == 2) {
-    v = v / (1.f + expf(-v));
+    v = mul_sigmoid(v, v);  // SiLU
   } else if (e.act == 3) {
+    // GELU, tanh form: 0.5 v (1 + tanh(u)) = v sigmoid(2 u), which keeps its
+    // relative accuracy where 1 + tanh(u) would cancel (v below about -4).
     const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-    v = 0.5f * v * (1.f + tanhf(u));
+    v = mul_sigmoid(v, 2.f * u);
   }
   if (e.residual) {
     const int64_t i = m * e.ld + n;

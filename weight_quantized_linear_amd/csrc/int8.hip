@@ -11,12 +11,14 @@
 //
 // Quantiser (gfx950): one wave per row.  The row is read once into registers
 // (16-byte loads, up to 64 x 8 x CHUNKS elements), the absmax is a wave-wide
-// max reduction, and the codes are produced from the registers: q =
+// max reduction over the values' magnitude bits (so that a NaN or an
+// infinity reaches it), and the codes are produced from the registers: q =
 // round-half-even(x / scale) with IEEE float32 division, clamped to +-127
-// (an all-zero row gives scale 0 and zero codes).  Rows longer than the
+// (an all-zero row gives scale 0 and zero codes; a row with a NaN or an
+// infinity gives scale NaN or +inf and zero codes).  Rows longer than the
 // register budget are read a second time for the quantisation pass.
 //
-// GEMM: K % 128 == 0 with aligned operands runs the pipelined direct-to-LDS
+// GEMM: K % 64 == 0 with aligned operands runs the pipelined direct-to-LDS
 // kernel of gemm_lds.hip.  This file's kernel serves every other shape: a
 // 256-thread block computes a 128 x 128 int32 tile in 128-byte K strips
 // staged in LDS through registers (zero-filled past K); four waves (2 x 2,
@@ -30,11 +32,25 @@ namespace {
 
 // ---------------------------------------------------------------- quantiser
 
-__device__ __forceinline__ float wave_max(float v) {
+// |x| of a bfloat16 as its magnitude bits: for non-negative values the bit
+// patterns order like the values, with +inf above every finite value and
+// NaN above +inf, so an integer max over them is an absmax that a NaN or an
+// infinity reaches (fmaxf would drop a NaN).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), off, kWave)));
   return v;
 }
+
+// Max of the magnitude bits of the two bfloat16 values in each dword.
+__device__ __forceinline__ uint32_t abs_bits_max(uint32_t m, uint32_t v) {
+  return max(max(m, v & 0x7FFFu), (v >> 16) & 0x7FFFu);
+}
+
+// Quantise with this row's scale when it is usable: a finite, positive
+// absmax.  A zero row, or one holding a NaN (absmax NaN) or an infinity
+// (absmax +inf: every quotient 0 or NaN), gets zero codes.
+__device__ __forceinline__ bool amax_usable(uint32_t amax_bits) { return amax_bits - 1u < 0x7F80u - 1u; }
 
 __device__ __forceinline__ int8_t quantize_one(float x, float scale) {
   float q = rintf(x / scale);  // IEEE division, round half to even
@@ -57,7 +73,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
   const bool fits = nchunks <= int64_t(kWave) * CHUNKS;
 
   u32x4 v[CHUNKS];
-  float amax = 0.f;
+  uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < CHUNKS; ++i) {
     const int64_t c = int64_t(i) * kWave + lane;
@@ -74,11 +90,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) amax = fmaxf(amax, fmaxf(fabsf(bf16lo(v[i][d])), fabsf(bf16hi(v[i][d]))));
+      for (int d = 0; d < 4; ++d) amax_bits = abs_bits_max(amax_bits, v[i][d]);
     if (fits) break;
   }
-  amax = wave_max(amax);
-  const float scale = amax / 127.f;
+  amax_bits = wave_max_u32(amax_bits);
+  const float scale = __uint_as_float(amax_bits << 16) / 127.f;
+  const bool usable = amax_usable(amax_bits);
   if (lane == 0) a_scale[row] = scale;
   for (int64_t c0 = 0; c0 < nchunks; c0 += int64_t(kWave) * CHUNKS) {
     if (!fits) {
@@ -93,7 +110,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
       const int64_t c = c0 + int64_t(i) * kWave + lane;
       if (c >= nchunks) continue;
       uint32_t packed[2] = {0u, 0u};
-      if (amax > 0.f) {
+      if (usable) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const uint32_t lo = uint8_t(quantize_one(bf16lo(v[i][d]), scale));
@@ -116,13 +133,14 @@ __global__ __launch_bounds__(256) void quantize_rows_any_kernel(const uint16_t* 
   const int64_t row = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (row >= M) return;
   const uint16_t* xr = x + row * K;
-  float amax = 0.f;
-  for (int64_t k = lane; k < K; k += kWave) amax = fmaxf(amax, fabsf(bf16_to_f32(xr[k])));
-  amax = wave_max(amax);
-  const float scale = amax / 127.f;
+  uint32_t amax_bits = 0;
+  for (int64_t k = lane; k < K; k += kWave) amax_bits = max(amax_bits, uint32_t(xr[k] & 0x7FFFu));
+  amax_bits = wave_max_u32(amax_bits);
+  const float scale = __uint_as_float(amax_bits << 16) / 127.f;
+  const bool usable = amax_usable(amax_bits);
   if (lane == 0) a_scale[row] = scale;
   for (int64_t k = lane; k < K; k += kWave)
-    q[row * K + k] = amax > 0.f ? quantize_one(bf16_to_f32(xr[k]), scale) : int8_t(0);
+    q[row * K + k] = usable ? quantize_one(bf16_to_f32(xr[k]), scale) : int8_t(0);
 }
 
 // ---------------------------------------------------------------- GEMM
