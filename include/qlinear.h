@@ -55,7 +55,9 @@ typedef enum qlinear_status {
   QLINEAR_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, bad dtype, bad layout */
   QLINEAR_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or a forced kernel family cannot run the call */
   QLINEAR_ERR_DEVICE = 3,       /* no usable HIP device / device query failed */
-  QLINEAR_ERR_LAUNCH = 4        /* a kernel launch reported an error */
+  QLINEAR_ERR_LAUNCH = 4,       /* a kernel launch reported an error */
+  QLINEAR_ERR_SCRATCH_LIMIT = 5 /* qlinear_fp8_gemm_noalloc: the shape needs more split-K
+                                   scratch than the library's fixed buffer holds */
 } qlinear_status;
 
 typedef enum qlinear_dtype {
@@ -394,6 +396,25 @@ int qlinear_bf16_gemm_ws(const void* w, const void* x, void* out, int out_dtype,
                          int64_t M, int64_t N, int64_t K, float alpha,
                          const qlinear_epilogue* epilogue, int path, void* workspace,
                          int64_t workspace_bytes, void* stream);
+
+/*
+ * qlinear_fp8_gemm_ws for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, hosts that forbid allocation):
+ * the split-K partial sums go to a fixed 8 MiB buffer of the library on the
+ * current device (each device has its own copy, held from the library's load
+ * until the process ends) instead of a caller-given workspace.  The call
+ * allocates nothing; the caller still passes inputs and outputs.  Kernels,
+ * results and errors are those of qlinear_fp8_gemm_ws with a workspace of
+ * the size qlinear_gemm_workspace_size gives (bit-identical output).  A
+ * shape whose workspace size exceeds 8 MiB returns QLINEAR_ERR_SCRATCH_LIMIT
+ * and launches nothing.  The buffer is shared by every call on a device and
+ * keeps the last call's partial sums: two calls of this function that can
+ * run at the same time on one device (different streams, host threads
+ * without stream ordering) race on it and give undefined results.
+ */
+int qlinear_fp8_gemm_noalloc(const void* w, const void* x, void* out, int out_dtype,
+                             int64_t M, int64_t N, int64_t K, float alpha,
+                             const qlinear_epilogue* epilogue, int path, void* stream);
 
 /*
  * Grouped matmuls with the per-expert weight scale folded in: page

@@ -45,7 +45,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlinear.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
 F32, BF16, I32 = 0, 1, 2
 PATHS = {"auto": 0, "gemv": 1, "skinny": 2, "tiled": 3, "splitk": 4}
 
@@ -91,6 +91,7 @@ EXPORTED = {
     "qlinear_fp8_gemm_ws": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p, _i64, _p],
     "qlinear_nvfp4_gemm_ws": [_p, _p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p, _i64, _p],
     "qlinear_bf16_gemm_ws": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p, _i64, _p],
+    "qlinear_fp8_gemm_noalloc": [_p, _p, _p, _i, _i64, _i64, _i64, _f, _EP, _i, _p],
 }
 
 WEIGHT_FP8, WEIGHT_NVFP4, WEIGHT_BF16 = 0, 1, 2

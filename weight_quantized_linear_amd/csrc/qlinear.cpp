@@ -283,6 +283,7 @@ const char* qlinear_status_string(int status) {
     case QLINEAR_ERR_UNSUPPORTED: return "unsupported device or configuration";
     case QLINEAR_ERR_DEVICE: return "no usable HIP device";
     case QLINEAR_ERR_LAUNCH: return "kernel launch failed";
+    case QLINEAR_ERR_SCRATCH_LIMIT: return "shape needs more split-K scratch than the library's fixed buffer";
     default: return "unknown status";
   }
 }
