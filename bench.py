@@ -137,6 +137,64 @@ def write_traffic(workload, fetch_csv, write_csv, kernel_substr):
     print(json.dumps(out))
 
 
+# rocprofv3 --pmc passes behind profiles/counters_<workload>.md (each pass a
+# run of its own; at most 8 SQ, 4 TCC, 4 TCP and 2 GRBM counters per pass)
+COUNTER_PASSES = [
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+    "SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum TCP_TCP_TA_DATA_STALL_CYCLES_sum SQ_INSTS_VALU SQ_WAIT_INST_ANY SQ_WAVES GRBM_GUI_ACTIVE",
+]
+
+
+def write_counters(workload, csvs, kernel_substr, num_cus=256):
+    """profiles/counters_<workload>.md from rocprofv3 --pmc runs of
+    ``bench.py --profile`` (COUNTER_PASSES): per-dispatch medians of every
+    counter for the dominant kernel, and the derived figures -- matrix-core
+    busy share of SIMD time, LDS bank-conflict cycles per LDS-active cycle,
+    L2 hit rate."""
+    import csv
+    vals = {}
+    for path in csvs:
+        names = set()
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                names.add(row["Counter_Name"])
+        for name in sorted(names):
+            vals[name] = counter_per_dispatch(path, name, lambda k: kernel_substr in k)[0]
+    g = vals.get("GRBM_GUI_ACTIVE")
+    derived = {}
+    if g and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+        derived["MFMA busy, % of SIMD cycles"] = 100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 4 * num_cus)
+    if "SQ_LDS_IDX_ACTIVE" in vals and "SQ_LDS_BANK_CONFLICT" in vals:
+        act = vals["SQ_LDS_IDX_ACTIVE"] - vals["SQ_LDS_BANK_CONFLICT"]
+        derived["LDS bank-conflict cycles per conflict-free LDS cycle"] = vals["SQ_LDS_BANK_CONFLICT"] / max(act, 1)
+        if g:
+            derived["LDS active, % of CU cycles"] = 100 * vals["SQ_LDS_IDX_ACTIVE"] / (g * num_cus)
+    if "SQ_WAIT_INST_LDS" in vals and "SQ_WAVE_CYCLES" in vals:
+        derived["wave cycles waiting to issue LDS instructions, %"] = \
+            100 * vals["SQ_WAIT_INST_LDS"] / max(vals["SQ_WAVE_CYCLES"], 1)
+    if "SQ_WAIT_INST_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
+        derived["wave cycles waiting for any instruction's data, %"] = \
+            100 * vals["SQ_WAIT_INST_ANY"] / max(vals["SQ_WAVE_CYCLES"], 1)
+    if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
+        derived["L2 hit rate, %"] = 100 * vals["TCC_HIT_sum"] / max(vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"], 1)
+    lines = [f"# Counters: {kernel_substr}, workload `{workload}`", "",
+             f"Kernel sources hash: {kernel_source_hash()}.  Per-dispatch medians over the dominant kernel's "
+             "dispatches of `bench.py --profile 20`, one rocprofv3 run per pass:", ""]
+    for c in COUNTER_PASSES:
+        lines.append(f"    cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <outdir> -o p -- "
+                     f"python3 <repo>/bench.py --workload {workload} --profile 20")
+    lines += ["", f"    python3 bench.py --workload {workload} --counters-from <outdir_1>/p_counter_collection.csv "
+                  "<outdir_2>/p_counter_collection.csv", "", "| Derived | Value |", "|---|---|"]
+    lines += [f"| {k} | {v:.3f} |" for k, v in derived.items()]
+    lines += ["", "| Counter | Per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {v:.0f} |" for k, v in sorted(vals.items())]
+    out = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"workload": workload, "derived": derived}))
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -149,8 +207,9 @@ class Case:
     """One launch of the step: ``run(copy)`` enqueues it on the current stream
     using weight copy ``copy`` of its pool."""
 
-    def __init__(self, name, run, nbytes, work, copies=1):
+    def __init__(self, name, run, nbytes, work, copies=1, weight_bytes=None):
         self.name, self.run, self.bytes, self.work, self.copies = name, run, nbytes, work, copies
+        self.weight_bytes = weight_bytes
 
 
 def copies_for(nbytes):
@@ -188,7 +247,10 @@ def build_decode(dev, q, synth, np, torch):
     weights, scales, heads = {}, {}, {}
     for si, (n, k) in enumerate(shapes):
         codes, s = synth.fp8_weight((2, si, 0), n, k)
-        weights[si] = torch.from_numpy(codes).to(dev)
+        w0 = torch.from_numpy(codes).to(dev)
+        # weights the 256 MB last-level cache could hold get a pool of >= 1 GiB
+        # of copies, so that every timed read (step or per case) comes from HBM
+        weights[si] = [w0] + [w0.clone() for _ in range(copies_for(n * k) - 1)]
         scales[si] = float(s)
         heads[si] = codes[:12288].copy()
         del codes
@@ -198,10 +260,11 @@ def build_decode(dev, q, synth, np, torch):
             x = bf16_dev(synth.bf16_activation((2, si, 1, m), m, k), dev, np, torch)
             out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             nbytes = n * k + m * k * 2 + m * n * 2
+            pool = weights[si]
 
-            def run(copy, w=weights[si], x=x, out=out, a=scales[si]):
-                q.fp8_gemm(w, x, out=out, out_dtype=torch.bfloat16, alpha=a)
-            cases.append(Case(f"fp8 m={m} n={n} k={k}", run, nbytes, 2 * m * n * k))
+            def run(copy, pool=pool, x=x, out=out, a=scales[si]):
+                q.fp8_gemm(pool[copy % len(pool)], x, out=out, out_dtype=torch.bfloat16, alpha=a)
+            cases.append(Case(f"fp8 m={m} n={n} k={k}", run, nbytes, 2 * m * n * k, len(pool), weight_bytes=n * k))
     dominant = cases[3]  # M = 1 over the 128256 x 4096 weight
 
     def baseline():
@@ -226,7 +289,9 @@ def build_decode(dev, q, synth, np, torch):
         kernel="fp8_gemv_wide_kernel<1,2,4> (M=1, N=128256, K=4096)",
         dtype="f32",
         config={"workload": "fp8_w8a16_decode: M in {1,4,16} x (N,K) in {(4096,4096),(14336,4096),"
-                            "(4096,14336),(128256,4096)}, E4M3 weight, bf16 activation, bf16 out"},
+                            "(4096,14336),(128256,4096)}, E4M3 weight, bf16 activation, bf16 out",
+                "value": "algorithmic bytes of all 12 cases (weights + activations + outputs, each once) / step "
+                         "time; the M=1 GEMV alone is roofline.achieved"},
         baseline=baseline)
 
 
@@ -238,7 +303,8 @@ def build_bf16_decode(dev, q, synth, np, torch):
     weights, heads = {}, {}
     for si, (n, k) in enumerate(shapes):
         wb = synth.bf16_weight((34, si), n, k)
-        weights[si] = bf16_dev(wb, dev, np, torch)
+        w0 = bf16_dev(wb, dev, np, torch)
+        weights[si] = [w0] + [w0.clone() for _ in range(copies_for(2 * n * k) - 1)]
         heads[si] = wb[:12288].copy()
         del wb
     cases = []
@@ -248,9 +314,10 @@ def build_bf16_decode(dev, q, synth, np, torch):
             out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             nbytes = n * k * 2 + m * k * 2 + m * n * 2
 
-            def run(copy, w=weights[si], x=x, out=out):
-                q.bf16_gemm(w, x, out=out, out_dtype=torch.bfloat16)
-            cases.append(Case(f"bf16 m={m} n={n} k={k}", run, nbytes, 2 * m * n * k))
+            def run(copy, pool=weights[si], x=x, out=out):
+                q.bf16_gemm(pool[copy % len(pool)], x, out=out, out_dtype=torch.bfloat16)
+            cases.append(Case(f"bf16 m={m} n={n} k={k}", run, nbytes, 2 * m * n * k, len(weights[si]),
+                              weight_bytes=2 * n * k))
     dominant = cases[3]
 
     def baseline():
@@ -292,7 +359,7 @@ def build_gemv2048(dev, q, synth, np, torch):
 
         def run(copy, pool=pool, x=x, out=out):
             q.fp8_gemv(pool[copy % len(pool)], x, out=out, out_dtype=torch.float32)
-        cases.append(Case(c.name, run, n * k + k * 2 + n * 4, 2 * n * k, copies))
+        cases.append(Case(c.name, run, n * k + k * 2 + n * 4, 2 * n * k, copies, weight_bytes=n * k))
 
     def baseline():
         from oracle import ref
@@ -340,7 +407,7 @@ def build_nvfp4(dev, q, synth, np, torch):
                 "sample": f"first {rows} weight rows for M in (1, 128, 2048), full K, {passes} passes ({el:.1f} s)"}
 
     return dict(metric="W4A16 NVFP4 dequant-GEMM TFLOP/s", unit="TFLOP/s", per="work", cases=cases,
-                dominant=cases[2], bound="mfma", peak=BF16_PEAK_TFLOPS,
+                dominant=cases[2], bound="mfma", peak=BF16_PEAK_TFLOPS, mfma_dtype=0,
                 kernel="wq_gemm_kernel<Nvfp4Weight, 128, 256> (M=2048, N=K=4096)",
                 dtype="bf16",
                 config={"workload": "nvfp4_w4a16: M in {1,128,2048}, N=K=4096, E2M1 + E4M3 per-16 scales, bf16 out"},
@@ -520,7 +587,7 @@ def build_int8(dev, q, synth, np, torch):
                           f"({el:.1f} s)"}
 
     return dict(metric="W8A8 int8 GEMM TOPS (quantiser + GEMM + dequant epilogue)", unit="TOPS", per="work",
-                cases=cases, dominant=cases[2], bound="mfma", peak=INT8_PEAK_TOPS,
+                cases=cases, dominant=cases[2], bound="mfma", peak=INT8_PEAK_TOPS, mfma_dtype=1,
                 kernel="int8_gemm_lds_kernel<256, 256> (M=4096, N=12288, K=3072)", dtype="i8",
                 config={"workload": "w8a8_int8: quantise bf16 [4096,3072] + int8 GEMM N in {3072,12288}, bf16 out"},
                 baseline=baseline)
@@ -563,7 +630,7 @@ def build_fp8_w8a8(dev, q, synth, np, torch):
                           f"({el:.1f} s)"}
 
     return dict(metric="FP8 W8A8 GEMM TFLOP/s (static per-tensor activation quantiser + fp8 GEMM)", unit="TFLOP/s",
-                per="work", cases=cases, dominant=cases[2], bound="mfma", peak=FP8_PEAK_TFLOPS,
+                per="work", cases=cases, dominant=cases[2], bound="mfma", peak=FP8_PEAK_TFLOPS, mfma_dtype=2,
                 kernel="fp8_w8a8_lds2_kernel<256, 256> (M=4096, N=12288, K=3072)", dtype="f8",
                 config={"workload": "fp8_w8a8: quantise bf16 [4096,3072] to E4M3 + fp8 GEMM N in {3072,12288}, "
                                     "bf16 out"},
@@ -592,6 +659,97 @@ def capture(torch, fn):
     return g
 
 
+def read_clocks():
+    """GPU 0's current clocks and power as the SMI tool reports them (its
+    clock / power lines, at most 16), or None where no tool answers."""
+    import re
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "-p"], ["rocm-smi", "-d", "0", "--showclocks", "--showpower"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode == 0:
+            keep = [" ".join(ln.split()) for ln in r.stdout.splitlines()
+                    if re.search(r"(?i)clk|power|freq|mhz|watt", ln)]
+            if keep:
+                return {"tool": " ".join(cmd), "lines": keep[:16]}
+    return None
+
+
+def measure_ceilings(torch, dev, weight_sizes, mfma_dtype):
+    """Attainable figures on this GPU (libqlinear_ceiling.so): GB/s of a
+    read-only stream over each weight size (a pool of >= 1 GiB of buffers
+    cycled, so it reads HBM; best of a one-round grid and a grid-stride one)
+    and TFLOP/s (TOPS) of back-to-back matrix-core instructions of the
+    workload's dtype (0 bf16, 1 int8, 2 fp8)."""
+    import ctypes
+    path = os.path.join(ROOT, "weight_quantized_linear_amd", "libqlinear_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built; run python weight_quantized_linear_amd/build.py")
+    lib = ctypes.CDLL(path)
+    lib.qlinear_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+    lib.qlinear_ceiling_stream_dma.argtypes = lib.qlinear_ceiling_stream_read.argtypes
+    lib.qlinear_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.qlinear_ceiling_mfma_ops_per_wave_round.argtypes = [ctypes.c_int]
+    lib.qlinear_ceiling_mfma_ops_per_wave_round.restype = ctypes.c_int64
+    num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    out = {"stream_read_gbs": {}, "stream_dma_gbs": {}}
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for nbytes in weight_sizes:
+        nb = nbytes // 16 * 16
+        copies = copies_for(nb)
+        stride = -(-nb // 256) * 256
+        pool = torch.empty(stride * copies, dtype=torch.uint8, device=dev).fill_(1)
+        # (span KiB per wave, blocks): one span per wave at once, or a grid
+        # of 8 or 16 blocks per CU striding over the spans
+        configs = [(span, blocks) for span in (4, 8, 16)
+                   for blocks in (-(-nb // (span * 1024 * 4)), num_cus * 8, num_cus * 16)]
+        for key, call in (("stream_read_gbs", lib.qlinear_ceiling_stream_read),
+                          ("stream_dma_gbs", lib.qlinear_ceiling_stream_dma)):
+            best = None
+            for span, blocks in configs:
+                reps = max(8, copies)
+
+                def fn(span=span, blocks=blocks, reps=reps, call=call):
+                    for i in range(reps):
+                        st = call(ctypes.c_void_p(pool.data_ptr() + (i % copies) * stride), nb, span, blocks,
+                                  ctypes.c_void_p(sink.data_ptr()), stream())
+                        if st:
+                            raise RuntimeError(f"ceiling stream kernel failed ({st})")
+                g = capture(torch, fn)
+                g.replay()
+                us = time_graph(torch, g, 3) * 1e3 / reps
+                gbs = nb / (us * 1e-6) / 1e9
+                if os.environ.get("QLINEAR_BENCH_VERBOSE"):
+                    print(f"[bench] {key} {nbytes} span {span} KiB blocks {blocks}: {gbs:.0f} GB/s",
+                          file=sys.stderr, flush=True)
+                best = gbs if best is None else max(best, gbs)
+                del g
+            out[key][str(nbytes)] = round(best, 1)
+        del pool
+    if mfma_dtype is not None:
+        blocks, iters = num_cus * 2, 20000
+        lib.qlinear_ceiling_mfma(mfma_dtype, blocks, 10, ctypes.c_void_p(sink.data_ptr()), stream())
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a_ev.record()
+        st = lib.qlinear_ceiling_mfma(mfma_dtype, blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream())
+        b_ev.record()
+        torch.cuda.synchronize()
+        if st:
+            raise RuntimeError(f"qlinear_ceiling_mfma failed ({st})")
+        ops = blocks * 4 * iters * lib.qlinear_ceiling_mfma_ops_per_wave_round(mfma_dtype)
+        out["mfma_tflops"] = round(ops / (a_ev.elapsed_time(b_ev) * 1e-3) / 1e12, 1)
+        out["mfma_dtype"] = {0: "bf16 32x32x16", 1: "int8 32x32x32", 2: "fp8 32x32x64 f8f6f4"}[mfma_dtype]
+    return out
+
+
 def time_graph(torch, g, replays):
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -615,12 +773,21 @@ def main():
                          "calibration copy, print nothing else")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two --profile counter runs")
+    ap.add_argument("--counters-from", nargs="+", metavar="CSV",
+                    help="write profiles/counters_<workload>.md from the --profile runs of COUNTER_PASSES")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the quantized linear kernels run on a single device "
               f"and this build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
+    kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
+               "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
+               "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds2_kernel",
+               "bf16_decode": "bf16_gemv_wide_kernel", "grouped_int8": "int8_grouped_kernel"}
+    if args.counters_from:
+        write_counters(args.workload, args.counters_from, kernels[args.workload])
+        return
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
                    "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
@@ -643,6 +810,7 @@ def main():
     print(f"[bench] {args.workload}: inputs generated and resident in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
     cases = wl["cases"]
+    clocks_before = read_clocks()
     if args.profile:
         dom = wl["dominant"]
         for i in range(args.profile):
@@ -657,29 +825,52 @@ def main():
         return
     r = max(c.copies for c in cases)  # steps per graph: consecutive steps read different copies
 
-    def steps_fn():
-        for i in range(r):
-            for c in cases:
-                c.run(i)
+    def steps_fn(count):
+        def fn():
+            for i in range(count):
+                for c in cases:
+                    c.run(i)
+        return fn
 
-    g = capture(torch, steps_fn)
-    for _ in range(max(1, -(-args.warmup // r))):
-        g.replay()
+    # Exactly W warm-up and K timed steps: full graphs of r steps, then one
+    # graph of the remaining steps (step i of a graph uses weight copy i).
+    g_full = capture(torch, steps_fn(r))
+    rem_k = args.steps % r
+    rem_w = args.warmup % r
+    g_rem = {n: capture(torch, steps_fn(n)) for n in {rem_k, rem_w} if n}
+
+    def run_steps(n):
+        for _ in range(n // r):
+            g_full.replay()
+        if n % r:
+            g_rem[n % r].replay()
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
-    replays = max(1, -(-args.steps // r))
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ms_graph = time_graph(torch, g, replays)
+    a_ev.record()
+    run_steps(args.steps)
+    b_ev.record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = ms_graph / r
-    steps_timed = replays * r
+    ms_per_step = a_ev.elapsed_time(b_ev) / args.steps
+    steps_timed = args.steps
     per = wl["per"]
     step_amount = sum((c.bytes if per == "bytes" else c.work) for c in cases)
     scale = 1e9 if wl["unit"] == "GB/s" else 1e12
     value = step_amount / (ms_per_step * 1e-3) / scale
-    del g
+    del g_full, g_rem
+
+    # ceilings measured on this GPU in this run: read-only streams of each
+    # weight size the workload has, and the matrix-core loop of its dtype
+    ceil = measure_ceilings(torch, dev, sorted({c.weight_bytes for c in cases if c.weight_bytes}),
+                            wl.get("mfma_dtype"))
+    print(f"[bench] ceilings: {json.dumps(ceil)}", file=sys.stderr, flush=True)
 
     # per-case and dominant-kernel durations: a graph of back-to-back launches
-    # of one case (cycling its copies), timed with events on its stream
+    # of one case (cycling its copies, so weights come from HBM), timed with
+    # events on its stream
     per_case = []
     dom_ms = None
     for c in cases:
@@ -694,6 +885,10 @@ def main():
         entry = {"case": c.name, "us": round(us, 2), "gbs": round(c.bytes / (us * 1e-6) / 1e9, 1)}
         if c.work:
             entry["tflops"] = round(c.work / (us * 1e-6) / 1e12, 2)
+        if c.weight_bytes and str(c.weight_bytes) in ceil.get("stream_read_gbs", {}):
+            cg = ceil["stream_read_gbs"][str(c.weight_bytes)]
+            entry["frac_hbm_peak"] = round(entry["gbs"] / HBM_PEAK_GBS, 4)
+            entry["frac_stream_ceiling"] = round(entry["gbs"] / cg, 4)
         per_case.append(entry)
         if c is wl["dominant"]:
             dom_ms = us * 1e-3
@@ -704,9 +899,17 @@ def main():
     if wl["bound"] == "hbm":
         achieved = dom.bytes / (dom_ms * 1e-3) / 1e9
         unit, alg_key, alg = "GB/s", "algorithmic_bytes", dom.bytes
+        attainable = ceil.get("stream_read_gbs", {}).get(str(dom.weight_bytes)) if dom.weight_bytes else None
     else:
         achieved = dom.work / (dom_ms * 1e-3) / 1e12
         unit, alg_key, alg = ("TFLOP/s" if wl["unit"] == "TFLOP/s" else "TOPS"), "algorithmic_ops", dom.work
+        attainable = ceil.get("mfma_tflops")
+    roof = {"bound": wl["bound"], "achieved": round(achieved, 1), "peak": wl["peak"], "unit": unit,
+            "frac": round(achieved / wl["peak"], 4), "traffic": measured_traffic(args.workload),
+            "kernel": wl["kernel"], alg_key: alg, "avg_launch_us": round(dom_ms * 1e3, 2)}
+    if attainable:
+        roof["attainable"] = round(attainable, 1)
+        roof["frac_attainable"] = round(achieved / attainable, 4)
     line = {
         "metric": wl["metric"],
         "value": round(value, 2),
@@ -721,9 +924,9 @@ def main():
         "dtype": wl["dtype"],
         "data": "synthetic",
         "config": dict(wl["config"], step_amount=step_amount, graph_steps=r, wall_s=round(wall, 3)),
-        "roofline": {"bound": wl["bound"], "achieved": round(achieved, 1), "peak": wl["peak"], "unit": unit,
-                     "frac": round(achieved / wl["peak"], 4), "traffic": measured_traffic(args.workload),
-                     "kernel": wl["kernel"], alg_key: alg, "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "roofline": roof,
+        "ceilings": ceil,
+        "clocks": {"before": clocks_before, "after": read_clocks()},
         "cases": per_case,
     }
     if not args.no_cpu_baseline:

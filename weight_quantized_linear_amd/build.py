@@ -21,6 +21,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlinear.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# The benchmark's ceiling kernels (stream read, matrix-core loop): a library
+# of their own, not part of libqlinear's ABI.
+CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
+CEILING_PATH = os.path.join(PKG, "libqlinear_ceiling.so")
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any kernel.  No fast-math:
@@ -59,20 +63,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source, link libqlinear.so and the benchmark's
+    libqlinear_ceiling.so; returns the path of libqlinear.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources() + [CEILING_SRC]
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB_PATH, verbose)
+    _link(objs[-1:], CEILING_PATH, verbose)
     return LIB_PATH
 
 
