@@ -79,6 +79,10 @@ DYADIC = [
     # one block, every M, and the automatic choice at M = 12, K = 8192
     ("splitk", 16, 4096, 14336), ("splitk", 3, 1000, 4096), ("splitk", 9, 300, 2112), ("splitk", 16, 70, 1024),
     ("splitk", 1, 129, 512), ("auto", 12, 2000, 8192),
+    # streaming skinny kernel (5 <= M <= 16, N >= 65536, K in {1024, 2048, 3072, 4096}): every ring
+    # depth, a ragged last 16-row tile, every M class
+    ("skinny", 16, 65553, 2048), ("skinny", 5, 65536, 3072), ("auto", 9, 65537, 1024),
+    ("skinny", 16, 131087, 4096), ("auto", 6, 100003, 4096),
 ]
 
 

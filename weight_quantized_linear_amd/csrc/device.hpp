@@ -198,6 +198,47 @@ __device__ __forceinline__ void store_maybe_epi(void* out, int64_t m, int64_t n,
   else store_out(out, m * N + n, acc, alpha, out_bf16);
 }
 
+
+// ---------------------------------------------------------------- LDS DMA and waits
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes
+// land at lds + 16 i (lds is uniform over the wave).
+__device__ __forceinline__ void dma16(const char* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// dma16 with the non-temporal hint (cache-policy bit 1, "nt"), for data that
+// is read once, as the GEMV's weight loads are.
+__device__ __forceinline__ void dma16_nt(const char* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 2);
+}
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding.  The memory clobber keeps the compiler from moving LDS
+// accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// the fences would wait for every outstanding vector-memory operation,
+// including the strips still in flight.  Callers wait for what must be
+// complete (their share of the next strip, their own LDS reads) first; the
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- wave reduction
 
 template <int CTRL, int ROW_MASK = 0xF>

@@ -8,7 +8,7 @@
 // on the matrix cores.  The E4M3 -> bf16 widening is exact, so the matrix
 // cores see exactly the decoded weight; accumulation is float32.
 //
-// Four kernels, chosen by shape (all measured on the decode shapes):
+// Six kernels, chosen by shape (all measured on the decode shapes):
 //
 // * fp8_skinny_kernel (v_mfma_f32_16x16x32_bf16): a block of NWV waves owns
 //   16*G output columns; its waves take interleaved 64-byte K steps, each
@@ -30,6 +30,11 @@
 // * fp8_skinny_xlds_kernel (the same instruction, M <= 8, K % 256 == 0): the
 //   activation is copied to LDS once per block and every wave streams whole
 //   4 KiB weight row segments; described at the kernel.
+// * fp8_skinny_stream_kernel (16x16x32, 5 <= M <= 16, N >= 65536, K up to
+//   4096): whole weight rows DMA'd into an LDS ring, the activation held in
+//   registers; described at the kernel.
+// * fp8_skinny_splitk_kernel (16x16x32, long K): K slices over blocks into
+//   float32 partial planes of the caller's workspace.
 //
 // In every kernel the same k-slot assignment is used for both operands, so
 // the pairing of activation and weight elements does not depend on how the
@@ -552,6 +557,145 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_splitk_kernel(const uint8_
   }
 }
 
+// Streaming matrix-core kernel for many output features (M <= 16, K in
+// {1024, 2048, 3072, 4096}, aligned operands).  The weight is read the way
+// the GEMV reads it -- whole contiguous row segments, non-temporal -- but by
+// the DMA unit straight into LDS, and the matrix cores take their operand
+// layout from there:
+// * a persistent block of NW waves walks tiles of 16 weight rows; a tile is
+//   KS LDS stages of 16 rows x K / KS bytes, S stages form a ring, and the
+//   block keeps the next S - 1 stages in flight while it multiplies one.
+//   Every DMA instruction moves 1 KiB of one row (64 lanes x 16 bytes);
+//   16-byte chunk c of a stage row r sits at slot c ^ r, which the DMA
+//   lanes realise by choosing which chunk each one fetches, so that the 16
+//   rows of one ds_read_b128 pass fall in 16 distinct bank groups;
+// * in stage h of a tile, wave w owns the K range h K / KS + [w, w + 1) K /
+//   (KS NW), and it holds the activation of all its ranges (rows
+//   zero-padded to 16) in registers for the whole kernel, read once;
+// * per 64 K values a lane (r, q) reads 16 weight bytes of row r, widens
+//   them exactly to bf16 and runs two v_mfma_f32_16x16x32_bf16 (activation
+//   rows as A, weight rows as B; k = 64 c + 16 q + 8 h + e goes to k-slot
+//   8 q + e of instruction h on both operands);
+// * after a tile's last stage the NW partial 16 x 16 tiles meet in LDS and
+//   one wave (a different one each tile) adds them in wave order and stores.
+template <int NW, int SPW, int KS, int S, bool FUSED>
+__global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
+    int out_bf16, int M, int64_t N, float alpha, Epilogue epi) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int K = 64 * NW * SPW;          // the kernel is instantiated per K
+  constexpr int kRow = K / KS;              // bytes of a row in one stage
+  constexpr int kSteps = SPW / KS;          // 64-value steps of a wave per stage
+  constexpr int kRowParts = kRow / 1024;    // 1 KiB DMA instructions per stage row
+  constexpr int kStage = 16 * kRow;
+  static_assert(SPW % KS == 0 && kRow % 1024 == 0 && (16 * kRowParts) % NW == 0,
+                "stages of whole KiB rows, DMA instructions split evenly over the waves");
+  constexpr int kDmaPerWave = 16 * kRowParts / NW;
+  static_assert((S - 1) * kDmaPerWave < 64, "wait counts fit the vmcnt field");
+  v4f* red = reinterpret_cast<v4f*>(lds + S * kStage);
+
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t t0 = blockIdx.x;
+  const int64_t cnt = t0 < tiles ? (tiles - 1 - t0) / gridDim.x + 1 : 0;
+  if (cnt == 0) return;  // uniform: the grid never exceeds the tiles
+  const int64_t stages = cnt * KS;
+
+  // DMA of this block's stage j (tile j / KS, part j % KS) into its ring
+  // slot: instruction i of wave w moves 1 KiB (part p) of stage row r.  A
+  // stage past the block's last one re-fetches the last one (only in the
+  // prologue of a block with fewer than S stages), so that the prologue
+  // always issues the same loads.
+  auto issue = [&](int64_t j) {
+    if (j >= stages) j = stages - 1;
+    const int64_t t = t0 + (j / KS) * gridDim.x;
+    const int h = int(j % KS);
+    char* slot = lds + (j % S) * kStage;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int ins = wid * kDmaPerWave + i;
+      const int r = ins / kRowParts, p = ins % kRowParts;
+      int64_t n = 16 * t + r;
+      if (n >= N) n = N - 1;  // rows past N re-read the last row; never stored
+      dma16_nt(reinterpret_cast<const char*>(w + n * K + h * kRow) + 16 * (64 * p + (lane ^ r)),
+               slot + r * kRow + 1024 * p);
+    }
+  };
+
+  issue(0);
+  // Activation of this wave: xa[h][c][e] = x[r16][h K / KS + wid K / (KS NW)
+  // + 64 c + 16 q + 8 e .. + 8], loaded between the first stage and the rest
+  // of the prologue so that its wait does not cover the later stages.
+  v8bf xa[KS][kSteps][2];
+#pragma unroll
+  for (int h = 0; h < KS; ++h)
+#pragma unroll
+    for (int c = 0; c < kSteps; ++c)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        xa[h][c][e] = r16 < M ? __builtin_bit_cast(v8bf, ld16(x + int64_t(r16) * K + h * kRow +
+                                                                wid * (kRow / NW) + 64 * c + 16 * q + 8 * e))
+                              : v8bf{};
+#pragma unroll
+  for (int j = 1; j < S; ++j) issue(j);
+
+  v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t j = 0; j < stages; ++j) {
+    // Stage j has landed once at most `ahead` later stages' loads are pending
+    // (loads complete in order).
+    const int64_t ahead = stages - 1 - j < S - 1 ? stages - 1 - j : S - 1;
+    if (ahead >= S - 1) wait_vm<(S - 1) * kDmaPerWave>();
+    else if (ahead >= 4) wait_vm<4 * kDmaPerWave>();
+    else if (ahead >= 2) wait_vm<2 * kDmaPerWave>();
+    else if (ahead == 1) wait_vm<kDmaPerWave>();
+    else wait_vm<0>();
+    block_barrier();
+
+    const int h = int(j % KS);
+    const char* row = lds + (j % S) * kStage + r16 * kRow;
+    u32x4 wv[kSteps];
+#pragma unroll
+    for (int c = 0; c < kSteps; ++c) {
+      const int g = 4 * (wid * kSteps + c) + q;  // 16-byte chunk of the stage row
+      wv[c] = *reinterpret_cast<const u32x4*>(row + 16 * (g ^ r16));
+    }
+#pragma unroll
+    for (int hh = 0; hh < KS; ++hh) {
+      if (hh != h) continue;  // uniform; keeps the register arrays statically indexed
+#pragma unroll
+      for (int c = 0; c < kSteps; ++c) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[hh][c][0], e4m3x8_to_bf16x8(wv[c].x, wv[c].y), acc0, 0,
+                                                       0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[hh][c][1], e4m3x8_to_bf16x8(wv[c].z, wv[c].w), acc1, 0,
+                                                       0, 0);
+      }
+    }
+    const bool last = h == KS - 1;
+    if (last) red[wid * kWave + lane] = acc0 + acc1;
+    wait_lds();
+    block_barrier();  // every wave's reads of the slot (and, at a tile's end, its partial tile) are done
+    if (j + S < stages) issue(j + S);
+    if (last) {
+      const int64_t i = j / KS;
+      if (wid == int(i % NW)) {
+        v4f sum = red[lane];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) sum += red[v * kWave + lane];
+        // sum[e] = out[m = 4 q + e][n = 16 t + r16]
+        const int64_t n = 16 * (t0 + i * gridDim.x) + r16;
+        if (n < N) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q + e < M) store_maybe_epi<FUSED>(out, 4 * q + e, n, N, sum[e], alpha, out_bf16, epi);
+        }
+      }
+      acc0 = v4f{0.f, 0.f, 0.f, 0.f};
+      acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -667,6 +811,55 @@ hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* o
   return launch_splitk_reduce(ws, out, out_bf16, M, N, int(splits), alpha, s, epi);
 }
 
+namespace {
+
+template <int SPW, int KS, int S, bool FUSED>
+hipError_t launch_stream_k(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                           float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
+  constexpr int kNW = 8;
+  constexpr int K = 64 * kNW * SPW;
+  constexpr int kLds = S * 16 * (K / KS) + kNW * kWave * 16;
+  static_assert(kLds <= kMaxLds, "ring and partial tiles fit in LDS");
+  auto kern = fp8_skinny_stream_kernel<kNW, SPW, KS, S, FUSED>;
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), kLds, lds_set)) return e;
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t blocks = std::min<int64_t>(tiles, num_cus);
+  return launch(kern, dim3(unsigned(blocks)), dim3(kNW * kWave), size_t(kLds), s, w, x, out, out_bf16, int(M), N,
+                alpha, epi);
+}
+
+template <bool FUSED>
+hipError_t launch_stream(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M, int64_t N,
+                         int64_t K, float alpha, int num_cus, const Epilogue& epi, hipStream_t s) {
+  // 128 KiB of stages in the ring (S x 16 rows x K / KS bytes).  At K = 4096
+  // whole-K stages (S = 2) and half-K stages (S = 4) measured the same on
+  // the 128256-row weight at M = 16 (94 us), quarter-K stages 100 us.
+  switch (K) {
+    case 1024: return launch_stream_k<2, 1, 8, FUSED>(w, x, out, out_bf16, M, N, alpha, num_cus, epi, s);
+    case 2048: return launch_stream_k<4, 2, 8, FUSED>(w, x, out, out_bf16, M, N, alpha, num_cus, epi, s);
+    case 3072: return launch_stream_k<6, 3, 8, FUSED>(w, x, out, out_bf16, M, N, alpha, num_cus, epi, s);
+    case 4096: return launch_stream_k<8, 1, 2, FUSED>(w, x, out, out_bf16, M, N, alpha, num_cus, epi, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool fp8_skinny_stream_supported(const void* w, const void* x, int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 16 && (K == 1024 || K == 2048 || K == 3072 || K == 4096) && N >= 16 &&
+         N <= (int64_t(1) << 31) / 16 && reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(x) % 16 == 0;
+}
+
+hipError_t launch_fp8_skinny_stream(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
+                                    int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s,
+                                    const Epilogue& epi) {
+  if (!fp8_skinny_stream_supported(w, x, M, N, K)) return hipErrorInvalidValue;
+  if (epi.on) return launch_stream<true>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+  return launch_stream<false>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
+}
+
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&
          int64_t(xlds_groups(M)) * K * 8 + 16 * kWave * 4 <= kMaxLds;
@@ -675,6 +868,12 @@ bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s, const Epilogue& epi) {
+  // Very many output features: the streaming kernel (whole weight rows into
+  // an LDS ring) for 5 <= M <= 16 (M = 16, N = 128256, K = 4096: 94 us
+  // against 102 us for the 4x4x4 kernel; at M = 4 the 4x4x4 kernel keeps
+  // the lead, 86 against 91 us).
+  if (M > 4 && N >= 65536 && fp8_skinny_stream_supported(w, x, M, N, K))
+    return launch_fp8_skinny_stream(w, x, out, out_bf16, M, N, K, alpha, num_cus, s, epi);
   // Measured: for 5 <= M <= 8 the activation-in-LDS kernel wins only at
   // very many output features, where its whole-row weight bursts matter most.
   if (fp8_skinny_xlds_supported(M, N, K) && (M <= 4 || N >= 65536)) {

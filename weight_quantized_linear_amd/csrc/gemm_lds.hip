@@ -54,16 +54,10 @@ namespace qlinear {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
 // Blocks have NW = 4 or 8 waves (one or two per SIMD; with two, one wave's
 // MFMAs cover the other's stalls); the kernels take NW as a parameter.
 constexpr int kMaxLds = 160 * 1024;
 
-__device__ __forceinline__ void dma16(const char* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
-}
 __device__ __forceinline__ void dma4(const char* g, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 4, 0, 0);
 }
@@ -84,29 +78,6 @@ __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, u
 }
 __device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 4, voff, soff, 0, 0);
-}
-
-// Wait until at most N vector-memory operations of this wave are
-// outstanding.  The memory clobber keeps the compiler from moving LDS
-// accesses across the wait.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until every LDS access of this wave has completed.
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// the fences would wait for every outstanding vector-memory operation,
-// including the strips still in flight.  Callers wait for what must be
-// complete (their share of the next strip, their own LDS reads) first; the
-// asm statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ u32x4 lds16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }

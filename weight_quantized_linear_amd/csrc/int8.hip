@@ -9,14 +9,16 @@
 // adds the optional per-column bias after the dequantisation and casts to
 // bfloat16.
 //
-// Quantiser (gfx950): one wave per row.  The row is read once into registers
-// (16-byte loads, up to 64 x 8 x CHUNKS elements), the absmax is a wave-wide
-// max reduction over the values' magnitude bits (so that a NaN or an
-// infinity reaches it), and the codes are produced from the registers: q =
-// round-half-even(x / scale) with IEEE float32 division, clamped to +-127
-// (an all-zero row gives scale 0 and zero codes; a row with a NaN or an
-// infinity gives scale NaN or +inf and zero codes).  Rows longer than the
-// register budget are read a second time for the quantisation pass.
+// Quantiser (gfx950): one wave per row.  A row of up to 4096 values is read
+// once into registers (16-byte loads, all issued at once); the absmax is a
+// wave-wide max over the values' magnitude bits (so that a NaN or an
+// infinity reaches it); the codes are q = round-half-even(x / scale),
+// clamped to +-127, produced from the registers, with the quotient taken
+// from a once-per-row reciprocal and two fma corrections, which gives the
+// codes of the IEEE float32 division exactly (quantize_rcp; rows with a
+// subnormal scale divide).  An all-zero row gives scale 0 and zero codes; a
+// row with a NaN or an infinity gives scale NaN or +inf and zero codes.
+// Longer rows are read a second time for the quantisation pass.
 //
 // GEMM: K % 64 == 0 with aligned operands runs the pipelined direct-to-LDS
 // kernel of gemm_lds.hip.  This file's kernel serves every other shape: a
@@ -121,6 +123,78 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
       *reinterpret_cast<u32x2*>(qr + c * 8) = u32x2{packed[0], packed[1]};
     }
     if (fits) break;
+  }
+}
+
+// q = clamp(rint(x / s), +-127) from r = 1/s (correctly rounded, once per
+// row): q0 = x r, e = x - q0 s (exact, one fma), q1 = q0 + e r (one fma) is
+// the correctly rounded quotient x / s wherever that quotient is a normal
+// float32 (Markstein's correction step), and tiny quotients round to code 0
+// either way, so the codes equal those of the IEEE division.  Checked on the
+// CPU over every finite bfloat16 x for 3000 random and edge-case normal
+// scales (exact rational arithmetic where float64 emulation could double
+// round); rows with a subnormal scale keep the division.
+__device__ __forceinline__ int8_t quantize_rcp(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  const float q1 = __builtin_fmaf(e, r, q0);
+  const float q = fminf(fmaxf(rintf(q1), -127.f), 127.f);
+  return int8_t(int(q));
+}
+
+// Rows of up to 512 CH values (K % 8 == 0, x 16-byte and q 8-byte
+// aligned): a wave owns R consecutive rows and issues all R x CH 16-byte
+// loads of them before it reduces or quantises any, so that the second
+// row's data streams in while the first is quantised and stored.
+template <int CH, int R>
+__global__ __launch_bounds__(256) void quantize_rows_pipe_kernel(const uint16_t* __restrict__ x,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ a_scale, int64_t M,
+                                                                 int64_t K) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row0 = (int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave)) * R;
+  if (row0 >= M) return;
+  const int64_t nchunks = K >> 3;  // 8 elements per 16-byte chunk, at most 64 CH
+  u32x4 v[R][CH];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t c = int64_t(i) * kWave + lane;
+      v[r][i] = row0 + r < M && c < nchunks ? ld16(x + (row0 + r) * K + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= M) break;  // uniform
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) amax_bits = abs_bits_max(amax_bits, v[r][i][d]);
+    amax_bits = wave_max_u32(amax_bits);
+    const float scale = __uint_as_float(amax_bits << 16) / 127.f;
+    if (lane == 0) a_scale[row] = scale;
+    const bool usable = amax_usable(amax_bits);
+    const bool normal = scale >= 0x1p-126f;  // 1 / scale finite, quotients in the normal range
+    const float rcp = 1.f / scale;
+    int8_t* qr = q + row * K;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t c = int64_t(i) * kWave + lane;
+      if (c >= nchunks) continue;
+      uint32_t packed[2] = {0u, 0u};
+      if (usable) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float lo = bf16lo(v[r][i][d]), hi = bf16hi(v[r][i][d]);
+          const uint32_t ql = uint8_t(normal ? quantize_rcp(lo, scale, rcp) : quantize_one(lo, scale));
+          const uint32_t qh = uint8_t(normal ? quantize_rcp(hi, scale, rcp) : quantize_one(hi, scale));
+          packed[d >> 1] |= (ql | (qh << 8)) << (16 * (d & 1));
+        }
+      }
+      *reinterpret_cast<u32x2*>(qr + c * 8) = u32x2{packed[0], packed[1]};
+    }
   }
 }
 
@@ -342,6 +416,16 @@ hipError_t launch_int8_quantize(const uint16_t* x, int8_t* q, float* a_scale, in
                    (reinterpret_cast<uintptr_t>(q) % 8 == 0);
   const int64_t blocks = (M + 3) / 4;
   if (!vec) return launch(quantize_rows_any_kernel, dim3(blocks), dim3(256), 0, s, x, q, a_scale, M, K);
+  // One row per wave: with two or four rows a wave the launch has fewer
+  // waves to cover the load latency (4096 x 3072: 8.7 us at one row, 10.4
+  // at two, 14.2 at four).
+  constexpr int R = 1;
+  const int64_t pblocks = (M + 4 * R - 1) / (4 * R);
+  const int64_t ch = ((K >> 3) + kWave - 1) / kWave;  // 16-byte chunks per lane
+  if (ch <= 2) return launch(quantize_rows_pipe_kernel<2, R>, dim3(pblocks), dim3(256), 0, s, x, q, a_scale, M, K);
+  if (ch <= 4) return launch(quantize_rows_pipe_kernel<4, R>, dim3(pblocks), dim3(256), 0, s, x, q, a_scale, M, K);
+  if (ch <= 6) return launch(quantize_rows_pipe_kernel<6, R>, dim3(pblocks), dim3(256), 0, s, x, q, a_scale, M, K);
+  if (ch <= 8) return launch(quantize_rows_pipe_kernel<8, R>, dim3(pblocks), dim3(256), 0, s, x, q, a_scale, M, K);
   return launch(quantize_rows_kernel<8>, dim3(blocks), dim3(256), 0, s, x, q, a_scale, M, K);
 }
 

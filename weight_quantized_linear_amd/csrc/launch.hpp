@@ -61,6 +61,13 @@ hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* o
                                    hipStream_t s, const Epilogue& epi = Epilogue{});
 hipError_t launch_splitk_reduce(const float* part, void* out, int out_bf16, int64_t M, int64_t N, int splits,
                                 float alpha, hipStream_t s, const Epilogue& epi = Epilogue{});
+// Streaming skinny kernel (M <= 16, K in {1024, 2048, 3072, 4096}, 16-byte
+// aligned weight and activation): weight tiles of 16 rows DMA'd whole into
+// an LDS ring; hipErrorInvalidValue when the shape does not suit it.
+bool fp8_skinny_stream_supported(const void* w, const void* x, int64_t M, int64_t N, int64_t K);
+hipError_t launch_fp8_skinny_stream(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
+                                    int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s,
+                                    const Epilogue& epi = Epilogue{});
 // Workspace bytes the split-K skinny kernel takes for (M, N, K) (0: it does not apply).
 size_t fp8_skinny_splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
 
