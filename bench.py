@@ -146,7 +146,7 @@ COUNTER_PASSES = [
 ]
 
 
-def write_counters(workload, csvs, kernel_substr, num_cus=256):
+def write_counters(workload, csvs, kernel_substr):
     """profiles/counters_<workload>.md from rocprofv3 --pmc runs of
     ``bench.py --profile`` (COUNTER_PASSES): per-dispatch medians of every
     counter for the dominant kernel, and the derived figures -- matrix-core
@@ -161,15 +161,20 @@ def write_counters(workload, csvs, kernel_substr, num_cus=256):
                 names.add(row["Counter_Name"])
         for name in sorted(names):
             vals[name] = counter_per_dispatch(path, name, lambda k: kernel_substr in k)[0]
-    g = vals.get("GRBM_GUI_ACTIVE")
+    # The tool sums each counter over its instances: SQ_BUSY_CU_CYCLES over
+    # the CUs (cycles the CUs had work), GRBM_GUI_ACTIVE over the 8 XCDs.
+    cu = vals.get("SQ_BUSY_CU_CYCLES")
     derived = {}
-    if g and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
-        derived["MFMA busy, % of SIMD cycles"] = 100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 4 * num_cus)
+    if "GRBM_GUI_ACTIVE" in vals:
+        derived["GPU-active cycles per XCD"] = vals["GRBM_GUI_ACTIVE"] / 8
+    if cu and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+        derived["MFMA busy, % of SIMD cycles while the CUs have work"] = \
+            100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cu)
     if "SQ_LDS_IDX_ACTIVE" in vals and "SQ_LDS_BANK_CONFLICT" in vals:
         act = vals["SQ_LDS_IDX_ACTIVE"] - vals["SQ_LDS_BANK_CONFLICT"]
         derived["LDS bank-conflict cycles per conflict-free LDS cycle"] = vals["SQ_LDS_BANK_CONFLICT"] / max(act, 1)
-        if g:
-            derived["LDS active, % of CU cycles"] = 100 * vals["SQ_LDS_IDX_ACTIVE"] / (g * num_cus)
+        if cu:
+            derived["LDS active, % of CU cycles with work"] = 100 * vals["SQ_LDS_IDX_ACTIVE"] / cu
     if "SQ_WAIT_INST_LDS" in vals and "SQ_WAVE_CYCLES" in vals:
         derived["wave cycles waiting to issue LDS instructions, %"] = \
             100 * vals["SQ_WAIT_INST_LDS"] / max(vals["SQ_WAVE_CYCLES"], 1)
@@ -193,6 +198,63 @@ def write_counters(workload, csvs, kernel_substr, num_cus=256):
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps({"workload": workload, "derived": derived}))
+
+
+TRACE_TITLES = {
+    "decode": ("fp8_gemv_decode", "FP8 W8A16 decode workload (M in {1,4,16} x four (N,K) shapes)"),
+    "gemv2048": ("fp8_gemv_n2048", "FP8 W8A16 GEMV M=1, N=2048, K in {2048, 2050}"),
+    "nvfp4": ("nvfp4_w4a16", "W4A16 NVFP4 workload (M in {1,128,2048}, N=K=4096)"),
+    "grouped": ("grouped_moe_w8a16", "Grouped MoE W8A16 workload (64 experts [64,1536,2048], 4096 tokens)"),
+    "grouped_nvfp4": ("grouped_moe_w4a16_nvfp4", "Grouped MoE W4A16 NVFP4 workload"),
+    "grouped_int8": ("grouped_moe_w8a8_int8", "Grouped MoE W8A8 int8 workload"),
+    "int8": ("int8_w8a8", "W8A8 int8 workload (quantiser + GEMM, M=4096, K=3072, N in {3072,12288})"),
+    "fp8_w8a8": ("fp8_w8a8", "FP8 W8A8 workload (quantiser + fp8 GEMM, M=4096, K=3072, N in {3072,12288})"),
+    "bf16_decode": ("bf16_decode_control", "Dense bf16 control: the decode workload with bf16 weights"),
+}
+
+
+def _short_kernel(name):
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("qlinear::", "")
+
+
+def write_trace(workload, d):
+    """profiles/<name>_workload_kernel_trace.md from the csv directory of
+    ``rocprofv3 --kernel-trace --stats`` over ``bench.py --workload <w>``:
+    the tool's per-kernel statistics and, per launch shape, the median and
+    mean duration and the register / LDS use."""
+    import collections
+    import csv
+    prefix = [f for f in os.listdir(d) if f.endswith("_kernel_trace.csv")][0][:-len("_kernel_trace.csv")]
+    stats = list(csv.DictReader(open(os.path.join(d, prefix + "_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(d, prefix + "_kernel_trace.csv"))))
+    groups, meta = collections.defaultdict(list), {}
+    for r in trace:
+        key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000)
+        meta[key] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"])
+    name, title = TRACE_TITLES[workload]
+    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <outdir> -o t -- python3 "
+           f"<repo>/bench.py --workload {workload} --steps 20 --warmup 2 --no-cpu-baseline")
+    lines = [f"# Kernel trace: {title}", "", f"Kernel sources hash: {kernel_source_hash()}.  Command (on one MI355X):",
+             "", "```", cmd, f"python3 bench.py --workload {workload} --trace-from <outdir>", "```", "",
+             "## rocprofv3 --stats (kernel_stats.csv)", "", "| kernel | calls | average us | min us | max us | % |",
+             "|---|---|---|---|---|---|"]
+    for st in stats:
+        lines.append(f"| `{_short_kernel(st['Name'])}` | {st['Calls']} | {float(st['AverageNs']) / 1e3:.2f} | "
+                     f"{float(st['MinNs']) / 1e3:.2f} | {float(st['MaxNs']) / 1e3:.2f} | "
+                     f"{float(st['Percentage']):.1f} |")
+    lines += ["", "## Per launch shape (kernel_trace.csv)", "",
+              "| kernel | grid threads | block | launches | median us | mean us | VGPR / AGPR / SGPR / LDS |",
+              "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        m = meta[k]
+        lines.append(f"| `{k[0]}` | {k[1]} | {k[2]} | {len(v)} | {v[len(v) // 2]:.2f} | {sum(v) / len(v):.2f} | "
+                     f"{m[0]} / {m[1]} / {m[2]} / {m[3]} |")
+    out = os.path.join(ROOT, "profiles", f"{name}_workload_kernel_trace.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def blas_threads():
@@ -775,6 +837,11 @@ def main():
                     help="write profiles/traffic_<workload>.json from two --profile counter runs")
     ap.add_argument("--counters-from", nargs="+", metavar="CSV",
                     help="write profiles/counters_<workload>.md from the --profile runs of COUNTER_PASSES")
+    ap.add_argument("--trace-from", metavar="DIR",
+                    help="write profiles/<workload>_kernel_trace.md from a rocprofv3 --kernel-trace --stats "
+                         "csv directory of this workload's bench run")
+    ap.add_argument("--profile-case", type=int, default=None, metavar="I",
+                    help="with --profile: launch case I of the workload instead of the dominant one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the quantized linear kernels run on a single device "
@@ -787,6 +854,9 @@ def main():
                "bf16_decode": "bf16_gemv_wide_kernel", "grouped_int8": "int8_grouped_kernel"}
     if args.counters_from:
         write_counters(args.workload, args.counters_from, kernels[args.workload])
+        return
+    if args.trace_from:
+        write_trace(args.workload, args.trace_from)
         return
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
@@ -812,7 +882,7 @@ def main():
     cases = wl["cases"]
     clocks_before = read_clocks()
     if args.profile:
-        dom = wl["dominant"]
+        dom = wl["dominant"] if args.profile_case is None else cases[args.profile_case]
         for i in range(args.profile):
             dom.run(i)
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
