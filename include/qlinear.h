@@ -17,10 +17,10 @@
  *   synchronises.  Outputs are valid once the stream has reached the work.
  * - Ownership: the caller owns every buffer, including the optional
  *   float32 workspace of the *_ws calls (split-K partial sums; size from
- *   qlinear_gemm_workspace_size).  The library allocates and frees nothing,
- *   keeps no pointer past the call and has no workspace of its own; its only
- *   state is a per-device cache of the device's properties (architecture,
- *   CU count).  A call's kernel choice, and so its summation order and
+ *   qlinear_gemm_workspace_size).  The library allocates and frees nothing
+ *   and keeps no pointer past the call; its state is a per-device cache of
+ *   the device's properties (architecture, CU count) and the fixed 8 MiB
+ *   device buffer that only qlinear_fp8_gemm_noalloc uses.  A call's kernel choice, and so its summation order and
  *   output bits, depends only on its arguments (shapes, operand alignment,
  *   the workspace size given) and the device's CU count, never on earlier
  *   calls.  Calls without a workspace run whole-K tiles.
