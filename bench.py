@@ -755,6 +755,8 @@ def measure_ceilings(torch, dev, weight_sizes, mfma_dtype):
     lib.qlinear_ceiling_stream_dma.argtypes = lib.qlinear_ceiling_stream_read.argtypes
     lib.qlinear_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                          ctypes.c_void_p]
+    lib.qlinear_ceiling_reread.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.qlinear_ceiling_mfma_ops_per_wave_round.argtypes = [ctypes.c_int]
     lib.qlinear_ceiling_mfma_ops_per_wave_round.restype = ctypes.c_int64
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -796,6 +798,28 @@ def measure_ceilings(torch, dev, weight_sizes, mfma_dtype):
             out[key][str(nbytes)] = round(best, 1)
         del pool
     if mfma_dtype is not None:
+        # what the L2s deliver to the CUs (LDS DMA and register loads): the
+        # rate the tiled kernels' operand strips are fetched at
+        small = torch.ones(2 << 20, dtype=torch.uint8, device=dev)
+        for key, dma in (("l2_to_lds_tbs", 1), ("l2_to_vgpr_tbs", 0)):
+            best = 0.0
+            for blocks in (num_cus * 2, num_cus * 8):
+                iters = 200
+                lib.qlinear_ceiling_reread(ctypes.c_void_p(small.data_ptr()), small.numel(), dma, blocks, 5,
+                                           ctypes.c_void_p(sink.data_ptr()), stream())
+                a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                a_ev.record()
+                st = lib.qlinear_ceiling_reread(ctypes.c_void_p(small.data_ptr()), small.numel(), dma, blocks, iters,
+                                                ctypes.c_void_p(sink.data_ptr()), stream())
+                b_ev.record()
+                torch.cuda.synchronize()
+                if st:
+                    raise RuntimeError(f"qlinear_ceiling_reread failed ({st})")
+                tbs = blocks * 4 * iters * 8192 / (a_ev.elapsed_time(b_ev) * 1e-3) / 1e12
+                best = max(best, tbs)
+            out[key] = round(best, 2)
+        del small
         blocks, iters = num_cus * 2, 20000
         lib.qlinear_ceiling_mfma(mfma_dtype, blocks, 10, ctypes.c_void_p(sink.data_ptr()), stream())
         a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -44,6 +44,17 @@ int qlinear_ceiling_stream_dma(const void* buf, int64_t bytes, int span_kib, int
                                void* stream);
 
 /*
+ * Re-reads of a small buffer (about 2 MiB: resident in every XCD's L2 after
+ * the first pass), to measure what the L2s deliver to the CUs: each of the
+ * `blocks` x 4 waves reads `iters` spans of 8 KiB (span (wave + 7919 i) mod
+ * the buffer's spans), through the DMA unit into LDS (dma != 0, one span in
+ * flight per wave) or into registers.  bytes >= 8 KiB; the bytes read are
+ * blocks x 4 x iters x 8 KiB.
+ */
+int qlinear_ceiling_reread(const void* buf, int64_t bytes, int dma, int64_t blocks, int iters, void* sink,
+                           void* stream);
+
+/*
  * `blocks` blocks of 4 waves, each wave running `iters` rounds of four
  * independent back-to-back matrix-core instructions on register operands:
  * dtype 0 = v_mfma_f32_32x32x16_bf16, 1 = v_mfma_i32_32x32x32_i8,

@@ -71,6 +71,39 @@ __global__ __launch_bounds__(kThreads) void stream_dma_kernel(const char* __rest
   if (r == key) sink[0] = r;
 }
 
+// L2 -> CU rate: every wave re-reads `iters` spans of U KiB of a small
+// buffer (resident in each XCD's L2 after the first pass), span (wave +
+// 7919 it) mod spans, into LDS through the DMA unit (one span in flight per
+// wave) or into registers.
+template <int U, bool DMA>
+__global__ __launch_bounds__(kThreads) void reread_kernel(const char* __restrict__ buf, int64_t spans, int iters,
+                                                          uint32_t key, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) char ring[kThreads / 64][U * 1024];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x / 64;
+  const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + wid;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+    const char* base = buf + ((wave + int64_t(it) * 7919) % spans) * U * 1024;
+    if constexpr (DMA) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(base + u * 1024 + lane * 16),
+                                         (__attribute__((address_space(3))) void*)(&ring[wid][u * 1024]), 16, 0, 0);
+    } else {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const u32x4*>(base + u * 1024 + lane * 16);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if constexpr (DMA) r ^= *reinterpret_cast<const uint32_t*>(&ring[wid][lane * 16]);
+  if (r == key) sink[0] = r;
+}
+
 // Back-to-back MFMAs on register operands, NACC independent accumulators
 // per wave, `iters` rounds; the accumulators are stored only if their sum
 // equals `key`.
@@ -180,6 +213,22 @@ int qlinear_ceiling_stream_dma(const void* buf, int64_t bytes, int span_kib, int
     case 16: hipLaunchKernelGGL(stream_dma_kernel<16>, g, b, 0, s, p, bytes / 16, 0x9E3779B9u, k); break;
     default: return 1;
   }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int qlinear_ceiling_reread(const void* buf, int64_t bytes, int dma, int64_t blocks, int iters, void* sink,
+                           void* stream) {
+  constexpr int U = 8;
+  const int64_t spans = bytes / (U * 1024);
+  if (!buf || !sink || spans < 1 || blocks < 1 || blocks > (int64_t(1) << 31) - 1 || iters < 1 ||
+      reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return 1;
+  auto s = static_cast<hipStream_t>(stream);
+  const dim3 g{unsigned(blocks), 1, 1}, b{unsigned(kThreads), 1, 1};
+  auto* p = static_cast<const char*>(buf);
+  auto* k = static_cast<uint32_t*>(sink);
+  if (dma) hipLaunchKernelGGL((reread_kernel<U, true>), g, b, 0, s, p, spans, iters, 0x9E3779B9u, k);
+  else hipLaunchKernelGGL((reread_kernel<U, false>), g, b, 0, s, p, spans, iters, 0x9E3779B9u, k);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
