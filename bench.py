@@ -721,11 +721,22 @@ def capture(torch, fn):
     return g
 
 
+def under_profiler():
+    """True inside a rocprofv3 run: its preloaded library initialises the GPU
+    in every process it is loaded into, so a child started from here (the
+    SMI tools are scripts started through /usr/bin/env) would replace a
+    process that has initialised the GPU.  No child processes then."""
+    return any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
 def read_clocks():
     """GPU 0's current clocks and power as the SMI tool reports them (its
-    clock / power lines, at most 16), or None where no tool answers."""
+    clock / power lines, at most 16), or None where no tool answers or the
+    run is under a profiler."""
     import re
     import subprocess
+    if under_profiler():
+        return None
     for cmd in (["amd-smi", "metric", "-g", "0", "-c", "-p"], ["rocm-smi", "-d", "0", "--showclocks", "--showpower"]):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
