@@ -30,9 +30,10 @@
 // * fp8_skinny_xlds_kernel (the same instruction, M <= 8, K % 256 == 0): the
 //   activation is copied to LDS once per block and every wave streams whole
 //   4 KiB weight row segments; described at the kernel.
-// * fp8_skinny_stream_kernel (16x16x32, 5 <= M <= 16, N >= 65536, K up to
-//   4096): whole weight rows DMA'd into an LDS ring, the activation held in
-//   registers; described at the kernel.
+// * fp8_skinny_stream_kernel (16x16x32, K up to 4096, N >= 8192 for
+//   5 <= M <= 16 and 8192 <= N < 65536 for 3 <= M <= 4): whole weight rows
+//   DMA'd into an LDS ring, the activation held in registers; described at
+//   the kernel.
 // * fp8_skinny_splitk_kernel (16x16x32, long K): K slices over blocks into
 //   float32 partial planes of the caller's workspace.
 //
@@ -868,11 +869,13 @@ bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s, const Epilogue& epi) {
-  // Very many output features: the streaming kernel (whole weight rows into
-  // an LDS ring) for 5 <= M <= 16 (M = 16, N = 128256, K = 4096: 94 us
-  // against 102 us for the 4x4x4 kernel; at M = 4 the 4x4x4 kernel keeps
-  // the lead, 86 against 91 us).
-  if (M > 4 && N >= 65536 && fp8_skinny_stream_supported(w, x, M, N, K))
+  // Many output features: the streaming kernel (whole weight rows into an
+  // LDS ring).  Measured at K = 4096: M = 16, N = 128256: 94 us against 102
+  // us for the 4x4x4 kernel; N = 14336: 16.6 against 19.2 us (M = 8: 15.2
+  // against 18.1; M = 4: 14.7 against 15.7); at N = 4096 (one 16-row tile
+  // per CU) it loses (10.2 against 8.4 us at M = 16), and at M = 4 over
+  // the 128256-row weight the 4x4x4 kernel keeps the lead (86 against 87-91).
+  if (M >= 3 && N >= 8192 && (M > 4 || N < 65536) && fp8_skinny_stream_supported(w, x, M, N, K))
     return launch_fp8_skinny_stream(w, x, out, out_bf16, M, N, K, alpha, num_cus, s, epi);
   // Measured: for 5 <= M <= 8 the activation-in-LDS kernel wins only at
   // very many output features, where its whole-row weight bursts matter most.
