@@ -55,8 +55,10 @@ def test_quantizer_rejects_bad_scale(q):
 
 
 W8A8_DYADIC = [(256, 128, 64), (300, 200, 512), (1, 7, 4096), (513, 1000, 1024), (64, 2048, 128),
-               # 256 x 256 tiles (ragged N; one, two and three K strips), 256 x 128 tiles (ragged M)
-               (2048, 4100, 192), (2048, 4096, 64), (2100, 4096, 128), (1100, 4000, 128),
+               # 256 x 256 tiles: 64-byte strips (K % 128 == 64; ragged N; one and three strips), 128-byte
+               # strips (one, two and three; ragged M and N); 256 x 128 tiles (ragged M)
+               (2048, 4100, 192), (2048, 4096, 64), (2100, 4096, 128), (2100, 4096, 256), (2048, 4100, 384),
+               (1100, 4000, 128),
                (5, 9, 100), (33, 17, 2050)]  # the last two: K % 64 != 0, element-wise kernel
 
 

@@ -113,9 +113,11 @@ def test_quantizer_unaligned_view(q):
     assert np.array_equal(qd.cpu().numpy(), want_q) and np.array_equal(sd.cpu().numpy(), want_s)
 
 
-# (4000, 3000, 1024): 256 x 256 tiles, ragged in both directions
+# (4000, 3000, 1024): 256 x 256 tiles with 128-byte strips, ragged in both directions;
+# (4000, 3000, 1088) the same tiles with 64-byte strips (K % 128 == 64); (2048, 4096, 128 / 256)
+# one and two 128-byte strips (a ring of two stages, the prologue re-fetching the last strip)
 @pytest.mark.parametrize("m,n,k", [(1, 1, 1), (130, 70, 100), (257, 129, 4099), (128, 256, 3072), (333, 1000, 64),
-                                   (4000, 3000, 1024)])
+                                   (4000, 3000, 1024), (4000, 3000, 1088), (2048, 4096, 128), (2048, 4096, 256)])
 def test_int32_accumulators_bit_exact(q, m, n, k):
     r = np.random.default_rng(m * 7 + n)
     a = r.integers(-127, 128, size=(m, k)).astype(np.int8)

@@ -882,16 +882,21 @@ size_t planes_bytes(int sp, int64_t M, int64_t N) { return sp > 1 ? size_t(sp) *
 
 // ---------------------------------------------------------------- W8A8 int8
 //
-// Strips are 64 bytes per row (4 chunks); step t, half h reads chunk 2t + h
-// (k = 32t + 16h .. +15) of both operands.
-template <int BM, int BN, int S, int WY, int NW>
+// Strips are SB bytes per row (SB / 16 chunks, SB = 64 or 128); step t of a
+// strip, half h reads chunk 2t + h (k = 32t + 16h .. +15) of both operands.
+// With 128-byte strips every DMA lane group covers a whole 128-byte line,
+// which the L2 -> LDS path delivers at about 1.5x the rate of half lines
+// (measured with 64 to 128 KiB in flight per CU: 24-26 against 32-39 bytes
+// per clock per CU).
+template <int BM, int BN, int S, int WY, int NW, int SB = 64>
 struct I8Layout {
   static constexpr int WX = NW / WY;
   static constexpr int FM = BM / WY / 32, FN = BN / WX / 32;
-  using ADma = StripDma<BM, 64, NW>;
-  using BDma = StripDma<BN, 64, NW>;
-  static constexpr int kA = BM * 64;
-  static constexpr int kStage = kA + BN * 64;
+  using ADma = StripDma<BM, SB, NW>;
+  using BDma = StripDma<BN, SB, NW>;
+  static constexpr int kA = BM * SB;
+  static constexpr int kStage = kA + BN * SB;
+  static constexpr int kSteps = SB / 32;  // MFMA k-steps per strip
   static constexpr int kLds = S * kStage;
   static constexpr int kLoads = ADma::kInst + BDma::kInst;
   static_assert(kLds <= kMaxLds, "LDS budget");
@@ -905,12 +910,14 @@ struct I8Layout {
 // One BM x BN output tile at (m0, n0) of out[M, N]: a [M, K], b [N, K],
 // a_scale [M], b_scale [N], bias [N] or null.  Every thread of the block
 // calls it; the LDS ring starts at `lds`.
-template <int BM, int BN, int S, int WY, int NW, int OUT>
+template <int BM, int BN, int S, int WY, int NW, int OUT, int SB = 64>
 __device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ a, const int8_t* __restrict__ b,
                                           const float* __restrict__ a_scale, const float* __restrict__ b_scale,
                                           const uint16_t* __restrict__ bias, void* __restrict__ out, int64_t M,
                                           int64_t N, int64_t K, int vec, int64_t m0, int64_t n0) {
-  using L = I8Layout<BM, BN, S, WY, NW>;
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
+  constexpr int T = L::kSteps;
+  static_assert(T % 2 == 0, "register sets alternate per step and a strip starts in the first");
   constexpr int FM = L::FM, FN = L::FN;
   constexpr int NM = FM * FN;  // MFMAs per step
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -923,21 +930,21 @@ __device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ 
   adma.init(m0, M, K);
   typename L::BDma bdma;
   bdma.init(n0, N, K);
-  uint32_t aoff[2], boff[2];
+  uint32_t aoff[T], boff[T];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    aoff[t] = uint32_t((row0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
-    boff[t] = uint32_t(L::kA + (col0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+  for (int t = 0; t < T; ++t) {
+    aoff[t] = uint32_t((row0 + r) * SB + 16 * ((2 * t + h) ^ swz<SB / 16>(r)));
+    boff[t] = uint32_t(L::kA + (col0 + r) * SB + 16 * ((2 * t + h) ^ swz<SB / 16>(r)));
   }
-  const int nk = int(K / 64);
+  const int nk = int(K / SB);
 
   // Strip s goes to slot s % S; past the end of K it re-fetches the last
   // strip, so every wave issues kLoads loads per call.
   auto fetch = [&](int s) {
     char* st = lds + (s % S) * L::kStage;
     const int src = s < nk ? s : nk - 1;
-    adma.fetch(st, ra, uint32_t(src) * 64);
-    bdma.fetch(st + L::kA, rb, uint32_t(src) * 64);
+    adma.fetch(st, ra, uint32_t(src) * SB);
+    bdma.fetch(st + L::kA, rb, uint32_t(src) * SB);
   };
 
   // Epilogue scales of this tile, loaded before the main loop so their
@@ -962,9 +969,9 @@ __device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ 
   u32x4 aX[FM], bX[FN], aY[FM], bY[FN];
   auto read = [&](u32x4 (&fa)[FM], u32x4 (&fb)[FN], const char* st, int t) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = lds16(st + aoff[t] + i * 32 * 64);
+    for (int i = 0; i < FM; ++i) fa[i] = lds16(st + aoff[t] + i * 32 * SB);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = lds16(st + boff[t] + j * 32 * 64);
+    for (int j = 0; j < FN; ++j) fb[j] = lds16(st + boff[t] + j * 32 * SB);
   };
   auto mma = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN]) {
 #pragma unroll
@@ -981,11 +988,23 @@ __device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ 
   block_barrier();
   read(aX, bX, lds, 0);
 
+  // Steps 0 .. T - 2 of the strip in slot `st`: read step t + 1 while the
+  // matrix cores run step t (register sets X for even t, Y for odd t).
+  auto inner = [&](const char* st) {
+#pragma unroll
+    for (int t = 0; t + 1 < T; ++t) {
+      if (t % 2 == 0) {
+        read(aY, bY, st, t + 1);
+        mma(aX, bX);
+      } else {
+        read(aX, bX, st, t + 1);
+        mma(aY, bY);
+      }
+      interleave<NM, 0, FM + FN, 0>();
+    }
+  };
   for (int kt = 0; kt < nk - 1; ++kt) {
-    const char* st = lds + (kt % S) * L::kStage;
-    read(aY, bY, st, 1);
-    mma(aX, bX);
-    interleave<NM, 0, FM + FN, 0>();
+    inner(lds + (kt % S) * L::kStage);
     // Cross into strip kt + 1 (landed for every wave after the barrier); the
     // slot of strip kt is free once every wave's reads of it have returned.
     wait_lds();
@@ -996,8 +1015,7 @@ __device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ 
     mma(aY, bY);
     interleave<NM, L::kLoads, FM + FN, 0>();
   }
-  read(aY, bY, lds + ((nk - 1) % S) * L::kStage, 1);
-  mma(aX, bX);
+  inner(lds + ((nk - 1) % S) * L::kStage);
   mma(aY, bY);
   wait_vm<0>();  // no LDS write may land after the block ends
 
@@ -1075,7 +1093,7 @@ __device__ __forceinline__ void int8_tile(char* lds, const int8_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int S, int WY, int NW, int OUT>
+template <int BM, int BN, int S, int WY, int NW, int OUT, int SB>
 __global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __restrict__ a,
                                                                  const int8_t* __restrict__ b,
                                                                  const float* __restrict__ a_scale,
@@ -1086,7 +1104,7 @@ __global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  int8_tile<BM, BN, S, WY, NW, OUT>(lds, a, b, a_scale, b_scale, bias, out, M, N, K, vec, tm * BM, tn * BN);
+  int8_tile<BM, BN, S, WY, NW, OUT, SB>(lds, a, b, a_scale, b_scale, bias, out, M, N, K, vec, tm * BM, tn * BN);
 }
 
 // Grouped MoE W8A8: the ragged walk of grouped_gemm_kernel (prefix sum of
@@ -1320,14 +1338,16 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds_kernel(const uint8_t* __
 // A row block i for strip s + 1 are read right after the MFMAs of block i
 // for strip s, so only one set of A fragments (and two of B) is live.  This
 // fits a 256 x 256 tile (128 x 64 per wave) in the 256 registers a wave has
-// at two waves per SIMD.
-template <int BM, int BN, int S, int WY, int NW, int OUT>
+// at two waves per SIMD.  Strips of SB = 64 or 128 bytes per row: a 128-byte
+// strip is two 64-value k-steps, with one barrier and one DMA round per strip.
+template <int BM, int BN, int S, int WY, int NW, int OUT, int SB = 64>
 __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* __restrict__ a,
                                                                  const uint8_t* __restrict__ b,
                                                                  void* __restrict__ out, int64_t M, int64_t N,
                                                                  int64_t K, float alpha, int vec) {
-  using L = I8Layout<BM, BN, S, WY, NW>;
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
   constexpr int FM = L::FM, FN = L::FN;
+  constexpr int U = SB / 64;  // k-steps of 64 values per strip
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
@@ -1342,19 +1362,22 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
   adma.init(m0, M, K);
   typename L::BDma bdma;
   bdma.init(n0, N, K);
-  uint32_t aoff[2], boff[2];
+  // k-step u of a strip: lane half h supplies chunks 4u + h and 4u + 2 + h
+  uint32_t aoff[U][2], boff[U][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    aoff[t] = uint32_t((row0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
-    boff[t] = uint32_t(L::kA + (col0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
-  }
-  const int nk = int(K / 64);
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      aoff[u][e] = uint32_t((row0 + r) * SB + 16 * ((4 * u + 2 * e + h) ^ swz<SB / 16>(r)));
+      boff[u][e] = uint32_t(L::kA + (col0 + r) * SB + 16 * ((4 * u + 2 * e + h) ^ swz<SB / 16>(r)));
+    }
+  const int nk = int(K / SB);
 
   auto fetch = [&](int s) {
     char* st = lds + (s % S) * L::kStage;
     const int src = s < nk ? s : nk - 1;
-    adma.fetch(st, ra, uint32_t(src) * 64);
-    bdma.fetch(st + L::kA, rb, uint32_t(src) * 64);
+    adma.fetch(st, ra, uint32_t(src) * SB);
+    bdma.fetch(st + L::kA, rb, uint32_t(src) * SB);
   };
 
   v16f acc[FM][FN];
@@ -1364,28 +1387,29 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
   v8i fa[FM], bP[FN], bQ[FN];
-  auto read_a = [&](int i, const char* st) {
-    fa[i].lo = __builtin_bit_cast(v4i, lds16(st + aoff[0] + i * 32 * 64));
-    fa[i].hi = __builtin_bit_cast(v4i, lds16(st + aoff[1] + i * 32 * 64));
+  auto read_a = [&](int i, const char* st, int u) {
+    fa[i].lo = __builtin_bit_cast(v4i, lds16(st + aoff[u][0] + i * 32 * SB));
+    fa[i].hi = __builtin_bit_cast(v4i, lds16(st + aoff[u][1] + i * 32 * SB));
   };
-  auto read_b = [&](v8i (&fb)[FN], const char* st) {
+  auto read_b = [&](v8i (&fb)[FN], const char* st, int u) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      fb[j].lo = __builtin_bit_cast(v4i, lds16(st + boff[0] + j * 32 * 64));
-      fb[j].hi = __builtin_bit_cast(v4i, lds16(st + boff[1] + j * 32 * 64));
+      fb[j].lo = __builtin_bit_cast(v4i, lds16(st + boff[u][0] + j * 32 * SB));
+      fb[j].hi = __builtin_bit_cast(v4i, lds16(st + boff[u][1] + j * 32 * SB));
     }
   };
-  // MFMAs of the current strip (A in fa, B in fb) while the fragments of the
-  // next strip (at `next`) are read: B first, then A block by block behind
-  // the MFMAs that last use it.  `last` multiplies the final strip.
-  auto step = [&](const v8i (&fb)[FN], v8i (&fb_next)[FN], const char* next) {
-    read_b(fb_next, next);
+  // MFMAs of the current k-step (A in fa, B in fb) while the fragments of
+  // the next one (k-step u of the strip at `next`) are read: B first, then A
+  // block by block behind the MFMAs that last use it.  `last` multiplies the
+  // final k-step.
+  auto step = [&](const v8i (&fb)[FN], v8i (&fb_next)[FN], const char* next, int u) {
+    read_b(fb_next, next, u);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-      read_a(i, next);
+      read_a(i, next, u);
     }
   };
   auto last = [&](const v8i (&fb)[FN]) {
@@ -1416,15 +1440,22 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
   wait_vm<(S - 1) * L::kLoads>();
   block_barrier();
 #pragma unroll
-  for (int i = 0; i < FM; ++i) read_a(i, lds);
-  read_b(bP, lds);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    cross(kt);
-    step(bP, bQ, lds + ((kt + 1) % S) * L::kStage);
+  for (int i = 0; i < FM; ++i) read_a(i, lds, 0);
+  read_b(bP, lds, 0);
+  auto advance = [&](const char* next, int u) {  // into k-step u of the strip at `next`
+    step(bP, bQ, next, u);
     order();
 #pragma unroll
     for (int j = 0; j < FN; ++j) bP[j] = bQ[j];
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+#pragma unroll
+    for (int u = 1; u < U; ++u) advance(lds + (kt % S) * L::kStage, u);
+    cross(kt);
+    advance(lds + ((kt + 1) % S) * L::kStage, 0);
   }
+#pragma unroll
+  for (int u = 1; u < U; ++u) advance(lds + ((nk - 1) % S) * L::kStage, u);
   wait_lds();
   last(bP);
   wait_vm<0>();  // no LDS write may land after the block ends
@@ -1460,16 +1491,16 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
   }
 }
 
-template <int BM, int BN, int S, int WY, int NW>
+template <int BM, int BN, int S, int WY, int NW, int SB = 64>
 hipError_t launch_fp8_w8a8_cfg2(const uint8_t* a, const uint8_t* b, void* out, int out_bf16, int64_t M, int64_t N,
                                 int64_t K, float alpha, hipStream_t s) {
-  using L = I8Layout<BM, BN, S, WY, NW>;
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
   const int64_t blocks = tiles(M, N, BM, BN);
   const int vec = aligned16(out) && (N * (out_bf16 ? 2 : 4)) % 16 == 0;
   if (out_bf16)
-    return launch_big_lds<fp8_w8a8_lds2_kernel<BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N,
+    return launch_big_lds<fp8_w8a8_lds2_kernel<BM, BN, S, WY, NW, 1, SB>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N,
                                                                       K, alpha, vec);
-  return launch_big_lds<fp8_w8a8_lds2_kernel<BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N, K,
+  return launch_big_lds<fp8_w8a8_lds2_kernel<BM, BN, S, WY, NW, 0, SB>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N, K,
                                                                     alpha, vec);
 }
 
@@ -1486,22 +1517,22 @@ hipError_t launch_fp8_w8a8_cfg(const uint8_t* a, const uint8_t* b, void* out, in
                                                                    alpha, vec);
 }
 
-template <int BM, int BN, int S, int WY, int NW>
+template <int BM, int BN, int S, int WY, int NW, int SB = 64>
 hipError_t launch_int8_cfg(const int8_t* a, const int8_t* b, const float* sa, const float* sb, const uint16_t* bias,
                            void* out, int out_mode, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  using L = I8Layout<BM, BN, S, WY, NW>;
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
   const int64_t blocks = tiles(M, N, BM, BN);
   const int es = out_mode == 1 ? 2 : 4;
   const int vec = aligned16(out) && (N * es) % 16 == 0;
   switch (out_mode) {
     case 0:
-      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 0, SB>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
                                                                         bias, out, M, N, K, vec);
     case 1:
-      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 1>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 1, SB>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
                                                                         bias, out, M, N, K, vec);
     default:
-      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 2>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
+      return launch_big_lds<int8_gemm_lds_kernel<BM, BN, S, WY, NW, 2, SB>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb,
                                                                         bias, out, M, N, K, vec);
   }
 }
@@ -1686,8 +1717,10 @@ hipError_t launch_fp8_w8a8_lds(const uint8_t* xq, const uint8_t* w, void* out, i
   // The 256 x 256 tile needs the in-place fragment refresh of
   // fp8_w8a8_lds2_kernel to fit two waves per SIMD (4096 x 12288 x 3072:
   // 175 us against 199 us for 256 x 128).
-  if (tiles(M, N, 256, 256) >= num_cus / 2)
+  if (tiles(M, N, 256, 256) >= num_cus / 2) {
+    if (K % 128 == 0) return launch_fp8_w8a8_cfg2<256, 256, 2, 2, 8, 128>(xq, w, out, out_bf16, M, N, K, alpha, s);
     return launch_fp8_w8a8_cfg2<256, 256, 4, 2, 8>(xq, w, out, out_bf16, M, N, K, alpha, s);
+  }
   if (tiles(M, N, 256, 128) >= num_cus / 2)
     return launch_fp8_w8a8_cfg<256, 128, 4, 2, 8>(xq, w, out, out_bf16, M, N, K, alpha, s);
   return launch_fp8_w8a8_cfg<128, 128, 4, 2, 8>(xq, w, out, out_bf16, M, N, K, alpha, s);
@@ -1697,9 +1730,13 @@ hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* s
                                 const uint16_t* bias, void* out, int out_mode, int64_t M, int64_t N, int64_t K,
                                 int num_cus, hipStream_t s) {
   // 256 x 256 tiles halve the L2 -> LDS traffic of 256 x 128 ones, which
-  // pays even when some CUs get no tile.
-  if (tiles(M, N, 256, 256) >= num_cus / 2)
+  // pays even when some CUs get no tile.  128-byte strips (two stages in the
+  // ring) beat 64-byte ones (four stages) where K allows: 4096 x 12288 x
+  // 3072 147 against 158 us, 4096 x 3072 x 3072 42.5 against 45.8 us.
+  if (tiles(M, N, 256, 256) >= num_cus / 2) {
+    if (K % 128 == 0) return launch_int8_cfg<256, 256, 2, 2, 8, 128>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
     return launch_int8_cfg<256, 256, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+  }
   if (tiles(M, N, 256, 128) >= num_cus / 2)
     return launch_int8_cfg<256, 128, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
   return launch_int8_cfg<128, 128, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
