@@ -66,8 +66,9 @@ def test_grouped_int8_workload_bf16(q, workload):
     assert inactive.sum() == 40 and np.all(got[inactive] == 0)
 
 
-# K % 64 == 0 (LDS kernel), K % 16 == 0 (register-staged, wide loads), neither
-@pytest.mark.parametrize("k", [256, 1024, 208, 100])
+# K % 128 == 0 (LDS kernel, 128-byte strips), K % 64 == 0 (64-byte strips), K % 16 == 0
+# (register-staged, wide loads), neither
+@pytest.mark.parametrize("k", [256, 1024, 192, 208, 100])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_grouped_int8_ragged_cases(q, k, with_bias):
     e, n, t = 4, 200, 300

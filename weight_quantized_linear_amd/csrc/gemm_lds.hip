@@ -1113,13 +1113,13 @@ __global__ __launch_bounds__(64 * NW) void int8_gemm_lds_kernel(const int8_t* __
 // rows a_offsets[z] .. (clipped to T) of a / a_scale and expert
 // e = expert_ids[z] of b [E, N, K], b_scale [E, N] and bias [E, N]; an id
 // outside 0 .. E - 1 writes zeros.
-template <int BM, int BN, int S, int WY, int NW, int OUT>
+template <int BM, int BN, int S, int WY, int NW, int OUT, int SB = 64>
 __global__ __launch_bounds__(64 * NW) void int8_grouped_kernel(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, const float* __restrict__ a_scale,
     const float* __restrict__ b_scale, const uint16_t* __restrict__ bias, const uint32_t* __restrict__ a_offsets,
     const int32_t* __restrict__ expert_ids, void* __restrict__ out, int64_t G, int64_t T, int64_t N, int64_t K,
     int64_t E, int vec) {
-  using L = I8Layout<BM, BN, S, WY, NW>;
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int kEs = OUT == 1 ? 2 : 4;
   int* cum = reinterpret_cast<int*>(lds + L::kLds);  // cum[z] = row tiles of groups 0 .. z-1; cum[G] = total
@@ -1185,7 +1185,7 @@ __global__ __launch_bounds__(64 * NW) void int8_grouped_kernel(
     }
     if (!first) __syncthreads();  // the previous tile's LDS use is over for every wave
     first = false;
-    int8_tile<BM, BN, S, WY, NW, OUT>(lds, a + start * K, b + e * N * K, a_scale ? a_scale + start : nullptr,
+    int8_tile<BM, BN, S, WY, NW, OUT, SB>(lds, a + start * K, b + e * N * K, a_scale ? a_scale + start : nullptr,
                                       b_scale ? b_scale + e * N : nullptr,
                                       bias ? bias + e * N : nullptr, gout, rows, N, K, vec, m0, n0);
   }
@@ -1744,12 +1744,12 @@ hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* s
 
 namespace {
 
-template <int BM, int BN, int S, int WY, int NW>
+template <int BM, int BN, int S, int WY, int NW, int SB = 64>
 hipError_t launch_int8_grouped_cfg(const int8_t* a, const int8_t* b, const float* sa, const float* sb,
                                    const uint16_t* bias, const uint32_t* a_offsets, const int32_t* expert_ids,
                                    void* out, int out_mode, int64_t G, int64_t E, int64_t T, int64_t N, int64_t K,
                                    int num_cus, hipStream_t s) {
-  using L = I8Layout<BM, BN, S, WY, NW>;
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
   const int lds_bytes = int(L::kLds + 4 * (G + 1));
   if (lds_bytes > kMaxLds) return hipErrorInvalidValue;
   const int64_t upper = ((T + BM - 1) / BM + G) * ((N + BN - 1) / BN);
@@ -1764,9 +1764,9 @@ hipError_t launch_int8_grouped_cfg(const int8_t* a, const int8_t* b, const float
     return launch(kernel, dim3(blocks), dim3(64 * NW), lds_bytes, s, a, b, sa, sb, bias, a_offsets, expert_ids, out,
                   G, T, N, K, E, vec);
   };
-  if (out_mode == 1) return go(int8_grouped_kernel<BM, BN, S, WY, NW, 1>);
-  if (out_mode == 2) return go(int8_grouped_kernel<BM, BN, S, WY, NW, 2>);
-  return go(int8_grouped_kernel<BM, BN, S, WY, NW, 0>);
+  if (out_mode == 1) return go(int8_grouped_kernel<BM, BN, S, WY, NW, 1, SB>);
+  if (out_mode == 2) return go(int8_grouped_kernel<BM, BN, S, WY, NW, 2, SB>);
+  return go(int8_grouped_kernel<BM, BN, S, WY, NW, 0, SB>);
 }
 
 }  // namespace
@@ -1781,7 +1781,12 @@ hipError_t launch_int8_grouped_lds(const int8_t* a, const int8_t* b, const float
                                    void* out, int out_mode, int64_t G, int64_t E, int64_t T, int64_t N, int64_t K,
                                    int num_cus, hipStream_t s) {
   // The grouped W8A16 tile shape: 64 rows (groups average ~64 tokens), 128
-  // columns, four waves side by side.
+  // columns, four waves side by side.  Where K allows, 128-byte strips in a
+  // two-stage ring (the same 48 KiB of LDS, three blocks per CU): 49 against
+  // 62 us on the 64-expert workload (a three-stage ring: 52 us).
+  if (K % 128 == 0)
+    return launch_int8_grouped_cfg<64, 128, 2, 1, 4, 128>(a, b, sa, sb, bias, a_offsets, expert_ids, out, out_mode, G,
+                                                          E, T, N, K, num_cus, s);
   return launch_int8_grouped_cfg<64, 128, 4, 1, 4>(a, b, sa, sb, bias, a_offsets, expert_ids, out, out_mode, G, E, T,
                                                    N, K, num_cus, s);
 }
