@@ -119,14 +119,16 @@ def test_grouped_single_group_equals_tiled(q):
     assert torch.equal(g, d)
 
 
-def test_grouped_dyadic_bit_exact(q):
-    e, n, k = 5, 130, 2050
+# K % 64 != 0 (element-wise kernel), K % 128 == 64 (64-value strips), K % 128 == 0 (128-value strips)
+@pytest.mark.parametrize("k", [2050, 192, 256])
+def test_grouped_dyadic_bit_exact(q, k):
+    e, n = 5, 130
     w = synth.dyadic_fp8_weight((45,), e * n, k).reshape(e, n, k)
     x = synth.dyadic_activation((46,), 401, k)
     offs = np.array([0, 1, 129, 129, 300, 401])
     ids = np.array([4, 0, 1, -1, 2], np.int32)
     ref, _, written = R.fp8_grouped(w, x, offs, ids)
-    show("grouped dyadic")
+    show("grouped dyadic", k)
     out = _grouped(q, w, x, offs, ids, out_dtype=torch.bfloat16, max_tokens=1)
     assert written.all()
     assert np.array_equal(bf16_bits(out), F.f64_to_bf16_bits(ref))

@@ -127,6 +127,17 @@ __device__ __forceinline__ void interleave() {
   sched_region<NM, NV, ND, NA>(std::make_integer_sequence<int, NM>{});
 }
 
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N - 1>{}):
+// a loop whose index is a compile-time constant in the body.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---------------------------------------------------------------- strip DMA
 
 // One strip of ROWS rows x SB bytes of a row-major operand (row stride `ld`
@@ -216,36 +227,40 @@ struct Fp8Args { const uint8_t* w; };
 struct Nvfp4Args { const uint8_t* packed; const uint8_t* scales; };
 struct Bf16Args { const uint16_t* w; };
 
-// fp8: 64 bytes per row per strip (4 chunks).  Step t, half h reads chunk
-// 2t + h (16 values) and feeds bytes 8e .. 8e + 7 to k-slice e.
-template <int BN, int FN, int NW>
-struct Fp8Weight {
+// fp8: 64 KM bytes per row per strip (4 KM chunks; a strip of KM = 2 is 128
+// values of k, whole 128-byte lines of the weight).  Step t, half h reads
+// chunk 2t + h (16 values) and feeds bytes 8e .. 8e + 7 to k-slice e.
+template <int BN, int FN, int NW, int KM>
+struct Fp8WeightK {
   using Args = Fp8Args;
   // Expert e of a stack [E, N, K].
   __device__ static Args expert(Args a, int64_t e, int64_t N, int64_t K) { return Args{a.w + e * N * K}; }
-  static constexpr int kBytes = BN * 64;
-  using Dma = StripDma<BN, 64, NW>;
+  static constexpr int kKM = KM;   // 64-value k blocks per strip
+  static constexpr int kSB = 64 * KM;  // weight bytes per row per strip
+  static constexpr int kBytes = BN * kSB;
+  using Dma = StripDma<BN, kSB, NW>;
   static constexpr int kLoads = Dma::kInst;
-  static constexpr int kReads[2] = {FN, FN};  // LDS reads per step
-  static constexpr int kValu = 8 * FN;        // decode instructions per step
+  __device__ static constexpr int reads(int) { return FN; }  // LDS reads per step
+  static constexpr int kValu = 8 * FN;                          // decode instructions per step
   __device__ static constexpr int a_chunk(int t, int h, int e) { return 2 * (2 * t + h) + e; }
 
   Dma dma;
   const char* w;
-  uint32_t foff[2];
+  uint32_t foff[2 * KM];
   u32x4 raw[FN];
 
   __device__ __forceinline__ void init(Args a, int64_t n0, int64_t N, int64_t K, int col0, int r, int h) {
     dma.init(n0, N, K);
     w = reinterpret_cast<const char*>(a.w);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) foff[t] = uint32_t((col0 + r) * 64 + 16 * ((2 * t + h) ^ swz<4>(r)));
+    for (int t = 0; t < 2 * KM; ++t)
+      foff[t] = uint32_t((col0 + r) * kSB + 16 * ((2 * t + h) ^ swz<4 * KM>(r)));
   }
-  __device__ __forceinline__ void fetch(char* tile, int64_t strip) const { dma.fetch(tile, w + strip * 64); }
+  __device__ __forceinline__ void fetch(char* tile, int64_t strip) const { dma.fetch(tile, w + strip * kSB); }
   template <int T>
   __device__ __forceinline__ void read(const char* tile) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) raw[j] = lds16(tile + foff[T] + j * 32 * 64);
+    for (int j = 0; j < FN; ++j) raw[j] = lds16(tile + foff[T] + j * 32 * kSB);
   }
   template <int T>
   __device__ __forceinline__ void decode(v8bf (&b)[2][FN]) const {
@@ -256,6 +271,11 @@ struct Fp8Weight {
     }
   }
 };
+
+template <int BN, int FN, int NW>
+using Fp8Weight = Fp8WeightK<BN, FN, NW, 1>;
+template <int BN, int FN, int NW>
+using Fp8Weight2 = Fp8WeightK<BN, FN, NW, 2>;
 
 // NVFP4: 32 packed bytes (64 values) + 4 E4M3 scale bytes per row per strip.
 // Half h reads packed chunk h (k = 32h .. 32h + 31) once per strip; step t
@@ -273,7 +293,8 @@ struct Nvfp4Weight {
   using Dma = StripDma<BN, 32, NW>;
   using SDma = ScaleDma<BN, NW>;
   static constexpr int kLoads = Dma::kInst + SDma::kInst;
-  static constexpr int kReads[2] = {2 * FN, 0};
+  static constexpr int kKM = 1;
+  __device__ static constexpr int reads(int t) { return t == 0 ? 2 * FN : 0; }
   static constexpr int kValu = 34 * FN;
   __device__ static constexpr int a_chunk(int t, int h, int e) { return 4 * h + 2 * t + e; }
 
@@ -335,7 +356,8 @@ struct Bf16Weight {
   static constexpr int kBytes = BN * 128;
   using Dma = StripDma<BN, 128, NW>;
   static constexpr int kLoads = Dma::kInst;
-  static constexpr int kReads[2] = {2 * FN, 2 * FN};
+  static constexpr int kKM = 1;
+  __device__ static constexpr int reads(int) { return 2 * FN; }
   static constexpr int kValu = 0;
   __device__ static constexpr int a_chunk(int t, int h, int e) { return 2 * (2 * t + h) + e; }
 
@@ -488,8 +510,11 @@ struct WqLayout {
   static constexpr int WX = NW / WY;
   static constexpr int FM = BM / WY / 32, FN = BN / WX / 32;
   using W = WP<BN, FN, NW>;
-  using ADma = StripDma<BM, 128, NW>;
-  static constexpr int kA = BM * 128;
+  static constexpr int kKM = W::kKM;           // 64-value k blocks per strip
+  static constexpr int kAsb = 128 * kKM;       // activation bytes per row per strip
+  static constexpr int kSteps = 2 * kKM;       // MFMA steps per strip
+  using ADma = StripDma<BM, kAsb, NW>;
+  static constexpr int kA = BM * kAsb;
   static constexpr int kStage = kA + W::kBytes;
   static constexpr int kLds = S * kStage;
   static constexpr int kLoads = ADma::kInst + W::kLoads;
@@ -500,8 +525,8 @@ struct WqLayout {
 // OUT: 0 = float32, 1 = bfloat16 output.  vec: full tiles may use 16-byte
 // stores (out 16-byte aligned, N * element size a multiple of 16).
 // One BM x BN output tile at (m0, n0) of out[M, N] (leading dimension N).
-// Strips s0 .. s0 + ns - 1 of K (64 values each) are summed: all of K for
-// the plain GEMM, one slice for split-K partial sums.  FUSED: the store
+// Strips s0 .. s0 + ns - 1 of K (64 kKM values each) are summed: all of K
+// for the plain GEMM, one slice for split-K partial sums.  FUSED: the store
 // applies `epi` (a separate instance, so that the epilogue's code does not
 // raise the registers of the plain kernels).
 template <template <int, int, int> class WP, int BM, int BN, int S, int WY, int NW, int OUT, bool FUSED = false>
@@ -524,19 +549,20 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
   adma.init_open(m0, 2 * K);
   W wq;
   wq.init(wa, n0, N, K, col0, r, h);
-  uint32_t aoff[2][2];
+  constexpr int T = L::kSteps;
+  uint32_t aoff[T][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      aoff[t][e] = uint32_t((row0 + r) * 128 + 16 * (W::a_chunk(t, h, e) ^ swz<8>(r)));
+      aoff[t][e] = uint32_t((row0 + r) * L::kAsb + 16 * (W::a_chunk(t, h, e) ^ swz<8 * L::kKM>(r)));
   const int64_t nk = ns;
 
   // Strip s goes to slot s % S; past the last strip it re-fetches the last one.
   auto fetch = [&](int64_t s) {
     char* st = lds + (s % S) * L::kStage;
     const int64_t src = s0 + (s < nk ? s : nk - 1);
-    adma.fetch(st, rx, uint32_t(src * 128));
+    adma.fetch(st, rx, uint32_t(src * L::kAsb));
     wq.fetch(st + L::kA, src);
   };
 
@@ -552,7 +578,7 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[e][i] = lds16(st + aoff[t][e] + i * 32 * 128);
+      for (int i = 0; i < FM; ++i) a[e][i] = lds16(st + aoff[t][e] + i * 32 * L::kAsb);
   };
   auto mma = [&](const u32x4 (&a)[2][FM], const v8bf (&b)[2][FN]) {
 #pragma unroll
@@ -580,17 +606,29 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
       wq.template decode<0>(bX);
     }
 
+    // Steps 0 .. T - 2 of the strip at `st`: read step t + 1 while the
+    // matrix cores run step t (register sets X for even t, Y for odd t).
+    auto inner = [&](const char* st) {
+      if constexpr (LIVE)
+        static_for<T - 1>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          if constexpr (t % 2 == 0) {
+            read_a(aY, st, t + 1);
+            wq.template read<t + 1>(st + L::kA);
+            mma(aX, bX);
+            wq.template decode<t + 1>(bY);
+          } else {
+            read_a(aX, st, t + 1);
+            wq.template read<t + 1>(st + L::kA);
+            mma(aY, bY);
+            wq.template decode<t + 1>(bX);
+          }
+          interleave<NM, 0, 2 * FM + W::reads(t + 1), W::kValu>();
+        });
+    };
     for (int64_t kt = 0; kt < nk - 1; ++kt) {
-      const char* st = lds + (kt % S) * L::kStage;
-      // step 0: read step 1 of this strip, multiply step 0
-      if constexpr (LIVE) {
-        read_a(aY, st, 1);
-        wq.template read<1>(st + L::kA);
-        mma(aX, bX);
-        wq.template decode<1>(bY);
-        interleave<NM, 0, 2 * FM + W::kReads[1], W::kValu>();
-      }
-      // step 1: cross into strip kt + 1 (landed for every wave after the
+      inner(lds + (kt % S) * L::kStage);
+      // last step: cross into strip kt + 1 (landed for every wave after the
       // barrier); slot kt % S is free once every wave's reads of it returned
       wait_lds();
       wait_vm<(S - 2) * kLoads>();
@@ -602,17 +640,11 @@ __device__ __forceinline__ void wq_tile(char* lds, const uint16_t* __restrict__ 
         wq.template read<0>(sn + L::kA);
         mma(aY, bY);
         wq.template decode<0>(bX);
-        interleave<NM, kLoads, 2 * FM + W::kReads[0], W::kValu>();
+        interleave<NM, kLoads, 2 * FM + W::reads(0), W::kValu>();
       }
     }
-    if constexpr (LIVE) {
-      const char* st = lds + ((nk - 1) % S) * L::kStage;
-      read_a(aY, st, 1);
-      wq.template read<1>(st + L::kA);
-      mma(aX, bX);
-      wq.template decode<1>(bY);
-      mma(aY, bY);
-    }
+    inner(lds + ((nk - 1) % S) * L::kStage);
+    if constexpr (LIVE) mma(aY, bY);
     wait_vm<0>();  // no LDS write may land after the block ends
   };
   if (m0 + row0 < M) main_loop(std::true_type{});
@@ -668,8 +700,9 @@ __global__ __launch_bounds__(64 * NW) void wq_gemm_kernel(const uint16_t* __rest
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t tm, tn;
   tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  wq_tile<WP, BM, BN, S, WY, NW, OUT, FUSED>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0, K / 64,
-                                             epi);
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
+  wq_tile<WP, BM, BN, S, WY, NW, OUT, FUSED>(lds, x, wa, out, M, N, K, alpha, vec, tm * BM, tn * BN, 0,
+                                             K / (64 * L::kKM), epi);
 }
 
 // Split-K: block b computes slice b % splits of tile b / splits into the
@@ -683,7 +716,8 @@ __global__ __launch_bounds__(64 * NW) void wq_splitk_kernel(const uint16_t* __re
   const int64_t slice = blockIdx.x % splits, tile = blockIdx.x / splits;
   int64_t tm, tn;
   tile_of_block(tile, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int64_t nk = K / 64, per = (nk + splits - 1) / splits;
+  using L = WqLayout<WP, BM, BN, S, WY, NW>;
+  const int64_t nk = K / (64 * L::kKM), per = (nk + splits - 1) / splits;
   const int64_t s0 = slice * per, ns = nk - s0 < per ? nk - s0 : per;
   wq_tile<WP, BM, BN, S, WY, NW, 0>(lds, x, wa, part + slice * M * N, M, N, K, 1.f, vec, tm * BM, tn * BN, s0, ns,
                                     Epilogue{});
@@ -821,7 +855,8 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(const uint16_t* _
     if (!first) __syncthreads();
     first = false;
     wq_tile<WP, BM, BN, S, WY, NW, OUT>(lds, x + start * K, WP<BN, 1, NW>::expert(wa, e, N, K), gout, rows, N, K,
-                                         expert_scale ? expert_scale[e] : 1.f, vec, m0, n0, 0, K / 64, Epilogue{});
+                                         expert_scale ? expert_scale[e] : 1.f, vec, m0, n0, 0, K / (64 * L::kKM),
+                                         Epilogue{});
   }
 }
 
@@ -1700,6 +1735,12 @@ bool nvfp4_grouped_lds_supported(const void* x, const void* packed, const void* 
 hipError_t launch_fp8_grouped_lds(const uint8_t* w, const uint16_t* x, const uint32_t* a_offsets,
                                   const int32_t* expert_ids, void* out, int out_bf16, int64_t G, int64_t E, int64_t T,
                                   int64_t N, int64_t K, int num_cus, hipStream_t s, const float* expert_scale) {
+  // Where K allows, 128-value strips (whole 128-byte weight lines) in a
+  // two-stage ring, the same 64 KiB of LDS: 64 against 68 us on the
+  // 64-expert workload (a three-stage ring, one block per CU: 82 us).
+  if (K % 128 == 0)
+    return launch_grouped_cfg<Fp8Weight2, kGrpBM, kGrpBN, 2, kGrpWY, kGrpNW>(
+        Fp8Args{w}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s, expert_scale);
   return launch_grouped_cfg<Fp8Weight, kGrpBM, kGrpBN, kGrpS, kGrpWY, kGrpNW>(
       Fp8Args{w}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s, expert_scale);
 }
