@@ -51,7 +51,8 @@ def test_grouped_nvfp4_workload(q):
     assert inactive.sum() == 40 and np.all(got[inactive] == 0)
 
 
-@pytest.mark.parametrize("k", [2048, 2080, 1040])  # LDS path; element-wise path (K % 64 != 0, then K % 32 != 0)
+# LDS path (128-value strips, then 64-value strips); element-wise path (K % 64 != 0, then K % 32 != 0)
+@pytest.mark.parametrize("k", [2048, 192, 2080, 1040])
 def test_grouped_nvfp4_dyadic_bit_exact(q, k):
     e, n = 5, 130
     p, s = _dyadic_stack((70, k), e, n, k)

@@ -62,8 +62,10 @@ def test_gemv_one_hot_returns_dequantised_column(q):
 NVFP4_DYADIC = [("gemv", 1, 7, 4096), ("gemv", 1, 515, 48), ("gemv", 3, 129, 2048), ("gemv", 4, 1000, 4096),
                 ("gemv", 2, 65, 4112), ("tiled", 5, 100, 4096), ("tiled", 128, 300, 1024),
                 ("tiled", 200, 129, 2064), ("tiled", 1, 17, 16),
-                # 128x256 tiles (ragged N) and 256x256 tiles (ragged M)
-                ("tiled", 2048, 2100, 64), ("tiled", 4100, 4096, 64),
+                # 128x256 tiles (ragged N; strips of 64 values, K % 128 == 64, and of 128 values: one and
+                # three) and 256x256 tiles (ragged M)
+                ("tiled", 2048, 2100, 64), ("tiled", 2048, 2100, 192), ("tiled", 2048, 4096, 128),
+                ("tiled", 2048, 2100, 384), ("tiled", 4100, 4096, 64),
                 # split-K: 64-row tiles up to M = 256 (the M = 128 workload shape), 128-row above
                 ("tiled", 128, 4096, 4096), ("tiled", 77, 1000, 2048), ("tiled", 256, 640, 1024),
                 ("tiled", 257, 640, 1024)]

@@ -277,32 +277,35 @@ using Fp8Weight = Fp8WeightK<BN, FN, NW, 1>;
 template <int BN, int FN, int NW>
 using Fp8Weight2 = Fp8WeightK<BN, FN, NW, 2>;
 
-// NVFP4: 32 packed bytes (64 values) + 4 E4M3 scale bytes per row per strip.
-// Half h reads packed chunk h (k = 32h .. 32h + 31) once per strip; step t
-// uses its bytes 8t .. 8t + 7 (k = 32h + 16t .. +15, scale block 2h + t) and
-// k-slice e the dword 2t + e.
-template <int BN, int FN, int NW>
-struct Nvfp4Weight {
+// NVFP4: per row and 64-value block of k, 32 packed bytes + 4 E4M3 scale
+// bytes; a strip holds KM blocks (KM = 2: 64 packed bytes, whole halves of
+// 128-byte lines, and 8 scale bytes per row).  In block u of a strip, half h
+// reads packed chunk 2u + h (k = 64u + 32h .. +31) once; step T = 2u + t uses
+// its bytes 8t .. 8t + 7 (k = 64u + 32h + 16t .. +15, scale block 4u + 2h + t)
+// and k-slice e the dword 2t + e.  The scale bytes of block u sit in a plane
+// of BN dwords of their own.
+template <int BN, int FN, int NW, int KM>
+struct Nvfp4WeightK {
   using Args = Nvfp4Args;
   // Expert e of stacks [E, N, K/2] (packed) and [E, N, K/16] (scales).
   __device__ static Args expert(Args a, int64_t e, int64_t N, int64_t K) {
     return Args{a.packed + e * N * (K / 2), a.scales + e * N * (K / 16)};
   }
-  static constexpr int kPacked = BN * 32;
-  static constexpr int kBytes = BN * 36;
-  using Dma = StripDma<BN, 32, NW>;
+  static constexpr int kKM = KM;
+  static constexpr int kPacked = BN * 32 * KM;
+  static constexpr int kBytes = kPacked + BN * 4 * KM;
+  using Dma = StripDma<BN, 32 * KM, NW>;
   using SDma = ScaleDma<BN, NW>;
-  static constexpr int kLoads = Dma::kInst + SDma::kInst;
-  static constexpr int kKM = 1;
-  __device__ static constexpr int reads(int t) { return t == 0 ? 2 * FN : 0; }
+  static constexpr int kLoads = Dma::kInst + KM * SDma::kInst;
+  __device__ static constexpr int reads(int t) { return t % 2 == 0 ? 2 * FN : 0; }
   static constexpr int kValu = 34 * FN;
-  __device__ static constexpr int a_chunk(int t, int h, int e) { return 4 * h + 2 * t + e; }
+  __device__ static constexpr int a_chunk(int t, int h, int e) { return 8 * (t / 2) + 4 * h + 2 * (t % 2) + e; }
 
   Dma dma;
   SDma sdma;
   const char* packed;
   const char* scales;
-  uint32_t foff, soff, shift;
+  uint32_t foff[KM], soff, shift;
   u32x4 raw[FN];
   uint32_t sc[FN];
 
@@ -311,32 +314,36 @@ struct Nvfp4Weight {
     sdma.init(n0, N, K / 16);
     packed = reinterpret_cast<const char*>(a.packed);
     scales = reinterpret_cast<const char*>(a.scales);
-    foff = uint32_t((col0 + r) * 32 + 16 * (h ^ swz<2>(r)));
+#pragma unroll
+    for (int u = 0; u < KM; ++u) foff[u] = uint32_t((col0 + r) * 32 * KM + 16 * ((2 * u + h) ^ swz<2 * KM>(r)));
     soff = uint32_t(kPacked + (col0 + r) * 4);
     shift = 16 * h;
   }
   __device__ __forceinline__ void fetch(char* tile, int64_t strip) const {
-    dma.fetch(tile, packed + strip * 32);
-    sdma.fetch(tile + kPacked, scales + strip * 4);
+    dma.fetch(tile, packed + strip * 32 * KM);
+#pragma unroll
+    for (int u = 0; u < KM; ++u) sdma.fetch(tile + kPacked + u * BN * 4, scales + strip * 4 * KM + 4 * u);
   }
   template <int T>
   __device__ __forceinline__ void read(const char* tile) {
-    if constexpr (T == 0) {
+    if constexpr (T % 2 == 0) {
+      constexpr int u = T / 2;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        raw[j] = lds16(tile + foff + j * 32 * 32);
-        sc[j] = *reinterpret_cast<const uint32_t*>(tile + soff + j * 32 * 4);
+        raw[j] = lds16(tile + foff[u] + j * 32 * 32 * KM);
+        sc[j] = *reinterpret_cast<const uint32_t*>(tile + soff + u * BN * 4 + j * 32 * 4);
       }
     }
   }
   template <int T>
   __device__ __forceinline__ void decode(v8bf (&b)[2][FN]) const {
+    constexpr int t = T % 2;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const float s = e4m3_to_f32((sc[j] >> (shift + 8 * T)) & 0xFFu);
+      const float s = e4m3_to_f32((sc[j] >> (shift + 8 * t)) & 0xFFu);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t d = raw[j][2 * T + e];
+        const uint32_t d = raw[j][2 * t + e];
         const u32x4 o{e2m1x2_to_bf16x2<0>(d, s), e2m1x2_to_bf16x2<1>(d, s), e2m1x2_to_bf16x2<2>(d, s),
                       e2m1x2_to_bf16x2<3>(d, s)};
         b[e][j] = __builtin_bit_cast(v8bf, o);
@@ -344,6 +351,10 @@ struct Nvfp4Weight {
     }
   }
 };
+template <int BN, int FN, int NW>
+using Nvfp4Weight = Nvfp4WeightK<BN, FN, NW, 1>;
+template <int BN, int FN, int NW>
+using Nvfp4Weight2 = Nvfp4WeightK<BN, FN, NW, 2>;
 
 // Dense bf16 weight (the control): 128 bytes per row per strip, the
 // activation strip's layout.  Step t, half h, k-slice e reads the chunk the
@@ -1624,8 +1635,14 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   // traffic wins instead (M = N = K = 4096: 156 -> 143 us).
   if (tiles(M, N, 256, 256) >= num_cus)
     return launch_wq<Nvfp4Weight, 256, 256, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
-  if (tiles(M, N, 128, 256) >= num_cus / 2)
+  // Where K allows, 128-value strips (64 packed bytes per weight row) in a
+  // two-stage ring: M = 2048, N = K = 4096 70 against 73 us with a few
+  // weight copies, the same 75 us with weights cycled through 1 GiB (three
+  // stages: 74 us).
+  if (tiles(M, N, 128, 256) >= num_cus / 2) {
+    if (K % 128 == 0) return launch_wq<Nvfp4Weight2, 128, 256, 2, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
     return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+  }
   return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
@@ -1749,6 +1766,11 @@ hipError_t launch_nvfp4_grouped_lds(const uint8_t* packed, const uint8_t* scales
                                     const uint32_t* a_offsets, const int32_t* expert_ids, void* out, int out_bf16,
                                     int64_t G, int64_t E, int64_t T, int64_t N, int64_t K, int num_cus,
                                     hipStream_t s, const float* expert_scale) {
+  // 128-value strips in a two-stage ring where K allows: 65 against 76 us on
+  // the 64-expert workload.
+  if (K % 128 == 0)
+    return launch_grouped_cfg<Nvfp4Weight2, kGrpBM, kGrp4BN, 2, kGrp4WY, kGrp4NW>(
+        Nvfp4Args{packed, scales}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s, expert_scale);
   return launch_grouped_cfg<Nvfp4Weight, kGrpBM, kGrp4BN, kGrpS, kGrp4WY, kGrp4NW>(
       Nvfp4Args{packed, scales}, x, a_offsets, expert_ids, out, out_bf16, G, E, T, N, K, num_cus, s, expert_scale);
 }
