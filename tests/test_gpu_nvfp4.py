@@ -68,7 +68,9 @@ NVFP4_DYADIC = [("gemv", 1, 7, 4096), ("gemv", 1, 515, 48), ("gemv", 3, 129, 204
                 ("tiled", 2048, 2100, 384), ("tiled", 4100, 4096, 64),
                 # split-K: 64-row tiles up to M = 256 (the M = 128 workload shape), 128-row above
                 ("tiled", 128, 4096, 4096), ("tiled", 77, 1000, 2048), ("tiled", 256, 640, 1024),
-                ("tiled", 257, 640, 1024)]
+                ("tiled", 257, 640, 1024),
+                # split-K with nine 128-value strips over three slices, and seventeen 64-value strips
+                ("tiled", 128, 4096, 1152), ("tiled", 100, 2048, 1088)]
 
 
 @pytest.mark.parametrize("path,m,n,k", NVFP4_DYADIC)

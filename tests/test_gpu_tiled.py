@@ -20,7 +20,12 @@ def q():
 
 
 TILED_DYADIC = [(1, 1, 16), (17, 33, 48), (130, 257, 200), (256, 128, 4096), (300, 500, 2050),
-                (129, 1, 64), (5, 1000, 4096), (128, 128, 13)]
+                (129, 1, 64), (5, 1000, 4096), (128, 128, 13), (256, 128, 4032),
+                # 256 x 128 tiles: 128-value strips (one; three, ragged M and N), 64-value strips
+                # (K % 128 == 64); 256 x 256 tiles
+                (2048, 4096, 128), (4100, 2100, 384), (2048, 4100, 192), (4096, 4096, 256),
+                # split-K: nine 128-value strips over three slices; seventeen 64-value strips
+                (128, 4096, 1152), (128, 4096, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", TILED_DYADIC)

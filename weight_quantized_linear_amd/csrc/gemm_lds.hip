@@ -907,15 +907,16 @@ hipError_t launch_wq_splitk(const uint16_t* x, typename WP<BN, 1, NW>::Args wa, 
   return launch(wq_reduce_kernel<0>, dim3(rblocks), dim3(256), 0, s, ws, out, count, splits, alpha, N, epi);
 }
 
-// Number of K slices for a grid of `nt` tiles: enough blocks to cover the
-// CUs, slices of at least 4 strips, partial planes within the workspace.
-int splitk_count(int64_t nt, int64_t M, int64_t N, int64_t K, int num_cus, size_t ws_bytes) {
+// Number of K slices for a grid of `nt` tiles whose strips hold `kv` values
+// of k: enough blocks to cover the CUs, slices of at least 256 values of k,
+// partial planes within the workspace.
+int splitk_count(int64_t nt, int64_t M, int64_t N, int64_t K, int kv, int num_cus, size_t ws_bytes) {
   if (nt * 2 > num_cus) return 1;
   int64_t sp = num_cus / nt;
-  const int64_t nk = K / 64;
-  if (sp > nk / 4) sp = nk / 4;
+  if (sp > K / 256) sp = K / 256;
   while (sp > 1 && size_t(sp) * size_t(M) * size_t(N) * 4 > ws_bytes) --sp;
   if (sp < 2) return 1;
+  const int64_t nk = K / kv;
   // The kernel gives slice i the strips i * per .. with per = ceil(nk / sp):
   // use only as many slices as that fills, so that none is empty.
   const int64_t per = (nk + sp - 1) / sp;
@@ -1601,14 +1602,23 @@ hipError_t launch_fp8_gemm_lds(const uint8_t* w, const uint16_t* x, void* out, i
                                const Epilogue& epi) {
   const Fp8Args wa{w};
   if (ws) {
-    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
-    if (sp > 1) return launch_wq_splitk<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
+    const int kv = K % 128 == 0 ? 128 : 64;  // values of k per strip
+    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, kv, num_cus, ws_bytes);
+    if (sp > 1) {
+      if (kv == 128)
+        return launch_wq_splitk<Fp8Weight2, 128, 128, 2, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
+      return launch_wq_splitk<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
+    }
   }
-  // Largest tile that still gives every CU a block.
+  // Largest tile that still gives every CU a block; 128-value strips (whole
+  // weight lines, two stages) where K allows and the LDS holds them
+  // (M = 2048, N = K = 4096: 67 against 71-72 us; split-K M = 128: 20.7
+  // against 21.1 us).
   if (tiles(M, N, 256, 256) >= num_cus)
     return launch_wq<Fp8Weight, 256, 256, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   if (tiles(M, N, 256, 128) >= num_cus)
-    return launch_wq<Fp8Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+    return K % 128 == 0 ? launch_wq<Fp8Weight2, 256, 128, 2, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s)
+                        : launch_wq<Fp8Weight, 256, 128, 3, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   return launch_wq<Fp8Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
@@ -1621,11 +1631,14 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
     // row decoded twice) and half the partial planes of 128-row tiles
     // (M = 128, N = K = 4096: 22.2 -> 18.4 us); larger M keeps 128 x 128.
     if (M <= 256) {
-      const int sp = splitk_count(tiles(M, N, 64, 128), M, N, K, num_cus, ws_bytes);
+      const int kv = K % 128 == 0 ? 128 : 64;
+      const int sp = splitk_count(tiles(M, N, 64, 128), M, N, K, kv, num_cus, ws_bytes);
+      if (sp > 1 && kv == 128)  // 128-value strips: M = 128 17.7 against 18.5 us
+        return launch_wq_splitk<Nvfp4Weight2, 64, 128, 2, 1, 4>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
       if (sp > 1)
         return launch_wq_splitk<Nvfp4Weight, 64, 128, 4, 1, 4>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
     }
-    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
+    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, 64, num_cus, ws_bytes);
     if (sp > 1)
       return launch_wq_splitk<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
   }
@@ -1649,20 +1662,22 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
 // Workspace bytes with which the launchers above take their split-K kernels
 // for (M, N, K) on a device with num_cus CUs (0: they run whole-K tiles).
 // These mirror the launchers' own choice made with an unbounded workspace.
+// The workspace each launch above asks for (the same slice counts).
 size_t fp8_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
-  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, SIZE_MAX), M, N);
+  const int kv = K % 128 == 0 ? 128 : 64;
+  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, kv, num_cus, SIZE_MAX), M, N);
 }
 
 size_t nvfp4_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
   if (M <= 256) {
-    const int sp = splitk_count(tiles(M, N, 64, 128), M, N, K, num_cus, SIZE_MAX);
+    const int sp = splitk_count(tiles(M, N, 64, 128), M, N, K, K % 128 == 0 ? 128 : 64, num_cus, SIZE_MAX);
     if (sp > 1) return planes_bytes(sp, M, N);
   }
-  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, SIZE_MAX), M, N);
+  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, 64, num_cus, SIZE_MAX), M, N);
 }
 
 size_t bf16_gemm_lds_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
-  return fp8_gemm_lds_ws_bytes(M, N, K, num_cus);
+  return planes_bytes(splitk_count(tiles(M, N, 128, 128), M, N, K, 64, num_cus, SIZE_MAX), M, N);
 }
 
 hipError_t launch_splitk_reduce(const float* part, void* out, int out_bf16, int64_t M, int64_t N, int splits,
@@ -1683,7 +1698,7 @@ hipError_t launch_bf16_gemm_lds(const uint16_t* w, const uint16_t* x, void* out,
                                 const Epilogue& epi) {
   const Bf16Args wa{w};
   if (ws) {
-    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, num_cus, ws_bytes);
+    const int sp = splitk_count(tiles(M, N, 128, 128), M, N, K, 64, num_cus, ws_bytes);
     if (sp > 1) return launch_wq_splitk<Bf16Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, sp, ws, epi, s);
   }
   // A 256 x 256 stage of both bf16 operands (64 KiB) leaves room for only two
