@@ -30,7 +30,11 @@ activations + outputs once, GB/s) or work (nvfp4, fp8_w8a8: TFLOP/s, int8: TOPS)
 time; ``roofline`` for the workload's dominant kernel, whose average launch
 duration is measured with HIP events around a graph of back-to-back launches
 of that kernel on its stream; ``cpu_baseline`` = the CPU oracle on a bounded
-sample of the same workload.
+sample of the same workload.  ``ceilings`` are attainable figures measured on
+the same GPU in the same run: a read-only stream over each weight size (for
+the grouped workloads, over as many bytes as the case moves), the rate the
+L2s deliver to the CUs, and back-to-back matrix-core instructions of the
+workload's type; ``roofline.frac_attainable`` divides by the matching one.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
                        [--no-cpu-baseline]
@@ -493,7 +497,8 @@ def build_grouped(dev, q, synth, np, torch):
 
     def run(copy):
         q.fp8_grouped_gemm(pw[copy % copies], x, offs, ids, out=out, max_tokens_per_group=c.max_tokens)
-    cases = [Case(c.name, run, nbytes, flops, copies)]
+    # attainable: a read stream over as many bytes as the case moves
+    cases = [Case(c.name, run, nbytes, flops, copies, weight_bytes=nbytes)]
 
     def baseline():
         from oracle import ref
@@ -535,7 +540,8 @@ def build_grouped_nvfp4(dev, q, synth, np, torch):
     def run(copy):
         q.nvfp4_grouped_gemm(pp[copy % copies], ps[copy % copies], x, offs, ids, out=out,
                              max_tokens_per_group=c.max_tokens)
-    cases = [Case(c.name, run, nbytes, flops, copies)]
+    # attainable: a read stream over as many bytes as the case moves
+    cases = [Case(c.name, run, nbytes, flops, copies, weight_bytes=nbytes)]
 
     def baseline():
         from oracle import ref
@@ -574,6 +580,8 @@ def build_grouped_int8(dev, q, synth, np, torch):
     active = [z for z in range(e) if c.expert_ids[z] >= 0 and c.a_offsets[z + 1] > c.a_offsets[z]]
     rows_active = int(sum(int(c.a_offsets[z + 1]) - int(c.a_offsets[z]) for z in active))
 
+    gbytes = len(active) * n * (k + 4 + 2) + t * (k + 4) + t * n * 2
+
     def quant(copy):
         q.int8_quantize_act(x, q=qa, a_scale=sa)
 
@@ -581,8 +589,7 @@ def build_grouped_int8(dev, q, synth, np, torch):
         q.int8_grouped_gemm(qa, pb[copy % copies], sa, sb, offs, ids, bias=bias, out=out,
                             max_tokens_per_group=c.max_tokens)
     cases = [Case("int8 quantize t=4096 k=2048", quant, t * k * 2 + t * k + t * 4, 0),
-             Case(c.name, run, len(active) * n * (k + 4 + 2) + t * (k + 4) + t * n * 2, 2 * rows_active * n * k,
-                  copies)]
+             Case(c.name, run, gbytes, 2 * rows_active * n * k, copies, weight_bytes=gbytes)]
 
     def baseline():
         from oracle import ref
