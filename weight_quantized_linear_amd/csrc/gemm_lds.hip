@@ -1475,11 +1475,24 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its A reads
     }
   };
+  // With two stages the strip fetched at a crossing has one strip's time to
+  // land: its B half (the weight, usually from HBM) goes out right after the
+  // barrier and its A half one k-step later, which spreads the DMA issue
+  // (4096 x 12288 x 3072: 131-133 -> 127.5-129.5 us; the same split gained
+  // nothing in the int8 kernel, which keeps one fetch).
+  auto fetch_a = [&](int s) {
+    adma.fetch(lds + (s % S) * L::kStage, ra, uint32_t(s < nk ? s : nk - 1) * SB);
+  };
+  auto fetch_b = [&](int s) {
+    bdma.fetch(lds + (s % S) * L::kStage + L::kA, rb, uint32_t(s < nk ? s : nk - 1) * SB);
+  };
+  constexpr bool kSplit = S == 2 && U > 1;
   auto cross = [&](int kt) {
     wait_lds();
     wait_vm<(S - 2) * L::kLoads>();
     block_barrier();
-    fetch(kt + S);
+    if constexpr (kSplit) fetch_b(kt + S);
+    else fetch(kt + S);
   };
 
 #pragma unroll
@@ -1496,6 +1509,8 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
     for (int j = 0; j < FN; ++j) bP[j] = bQ[j];
   };
   for (int kt = 0; kt + 1 < nk; ++kt) {
+    if constexpr (kSplit)
+      if (kt >= 1) fetch_a(kt - 1 + S);  // its slot was freed at the last crossing
 #pragma unroll
     for (int u = 1; u < U; ++u) advance(lds + (kt % S) * L::kStage, u);
     cross(kt);
