@@ -35,6 +35,10 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# QLINEAR_TILE_ORDER=flat builds the tiled GEMMs with the plain row-major
+# tile order instead of the XCD-aware one, to measure what the latter buys.
+if os.environ.get("QLINEAR_TILE_ORDER") == "flat":
+    COMMON_FLAGS.append("-DQLINEAR_FLAT_TILE_ORDER")
 
 
 def hipcc() -> str:

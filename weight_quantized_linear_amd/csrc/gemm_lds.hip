@@ -407,6 +407,13 @@ struct Bf16Weight {
 // tiles, and inside the range walk 8 row tiles per column tile.
 __device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
                                               int64_t& tn) {
+#ifdef QLINEAR_FLAT_TILE_ORDER
+  // Build option (QLINEAR_TILE_ORDER=flat in build.py) for measuring what the
+  // order below buys: the plain row-major grid.
+  tm = b / tiles_n;
+  tn = b % tiles_n;
+  return;
+#endif
   constexpr int kXcd = 8, kGroupM = 8;
   const int64_t total = tiles_m * tiles_n;
   const int64_t q = total / kXcd, r = total % kXcd;
@@ -419,26 +426,6 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_m, int64_
   const int64_t in_group = t % group;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
-}
-
-// The same mapping in 32-bit arithmetic with the results moved to scalar
-// registers (for kernels that change tiles inside their main loop).
-__device__ __forceinline__ void tile_of_block32(uint32_t b, uint32_t tiles_m, uint32_t tiles_n, int& tm_out,
-                                                int& tn_out) {
-  constexpr uint32_t kXcd = 8, kGroupM = 8;
-  const uint32_t total = tiles_m * tiles_n;
-  const uint32_t q = total / kXcd, r = total % kXcd;
-  const uint32_t xcd = b % kXcd, local = b / kXcd;
-  const uint32_t t = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-  const uint32_t group = kGroupM * tiles_n;
-  const uint32_t g = t / group;
-  const uint32_t first_m = g * kGroupM;
-  const uint32_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
-  const uint32_t in_group = t - g * group;
-  const uint32_t tn = in_group / gm;
-  const uint32_t tm = first_m + (in_group - tn * gm);
-  tm_out = __builtin_amdgcn_readfirstlane(int(tm));
-  tn_out = __builtin_amdgcn_readfirstlane(int(tn));
 }
 
 // ---------------------------------------------------------------- output staging
