@@ -1540,6 +1540,249 @@ __global__ __launch_bounds__(64 * NW) void fp8_w8a8_lds2_kernel(const uint8_t* _
   }
 }
 
+// The W8A8 int8 GEMM with the structure of fp8_w8a8_lds2_kernel: k-steps of
+// 64 values whose fragments hold chunks h and 2 + h of the step (lane half
+// h), each pair multiplied by two v_mfma_i32_32x32x32_i8 (the low halves:
+// k = 0 .. 31 of the step, the high halves: 32 .. 63), the A fragments
+// refreshed in place behind the MFMAs that last use them, and the int8
+// kernel's dequant epilogue (acc * a_scale[m] * b_scale[n] + bias[n]).
+template <int BM, int BN, int S, int WY, int NW, int OUT, int SB = 64>
+__global__ __launch_bounds__(64 * NW) void int8_lds2_kernel(const int8_t* __restrict__ a,
+                                                             const int8_t* __restrict__ b,
+                                                             const float* __restrict__ a_scale,
+                                                             const float* __restrict__ b_scale,
+                                                             const uint16_t* __restrict__ bias,
+                                                             void* __restrict__ out, int64_t M, int64_t N,
+                                                             int64_t K, int vec) {
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
+  constexpr int FM = L::FM, FN = L::FN;
+  constexpr int U = SB / 64;  // k-steps of 64 values per strip
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t tm, tn;
+  tile_of_block(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wy = wid / L::WX, wx = wid % L::WX;
+  const int r = lane & 31, h = lane >> 5;
+  const int row0 = wy * (BM / WY), col0 = wx * (BN / L::WX);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, M * K), rb = make_rsrc(b, N * K);
+  typename L::ADma adma;
+  adma.init(m0, M, K);
+  typename L::BDma bdma;
+  bdma.init(n0, N, K);
+  // k-step u of a strip: lane half h supplies chunks 4u + h and 4u + 2 + h
+  uint32_t aoff[U][2], boff[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      aoff[u][e] = uint32_t((row0 + r) * SB + 16 * ((4 * u + 2 * e + h) ^ swz<SB / 16>(r)));
+      boff[u][e] = uint32_t(L::kA + (col0 + r) * SB + 16 * ((4 * u + 2 * e + h) ^ swz<SB / 16>(r)));
+    }
+  const int nk = int(K / SB);
+
+  auto fetch = [&](int s) {
+    char* st = lds + (s % S) * L::kStage;
+    const int src = s < nk ? s : nk - 1;
+    adma.fetch(st, ra, uint32_t(src) * SB);
+    bdma.fetch(st + L::kA, rb, uint32_t(src) * SB);
+  };
+
+  // Epilogue scales of this tile, loaded before the main loop so their
+  // latency hides behind it: thread t holds row m0 + t and column n0 + t.
+  float pre_as = 0.f, pre_bs = 0.f, pre_bb = 0.f;
+  if constexpr (OUT != 2) {
+    const int t = threadIdx.x;
+    if (t < BM) pre_as = a_scale[m0 + t < M ? m0 + t : M - 1];
+    if (t < BN) {
+      const int64_t n = n0 + t < N ? n0 + t : N - 1;
+      pre_bs = b_scale[n];
+      pre_bb = bias ? bf16_to_f32(bias[n]) : 0.f;
+    }
+  }
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+
+  v8i fa[FM], bP[FN], bQ[FN];
+  auto read_a = [&](int i, const char* st, int u) {
+    fa[i].lo = __builtin_bit_cast(v4i, lds16(st + aoff[u][0] + i * 32 * SB));
+    fa[i].hi = __builtin_bit_cast(v4i, lds16(st + aoff[u][1] + i * 32 * SB));
+  };
+  auto read_b = [&](v8i (&fb)[FN], const char* st, int u) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      fb[j].lo = __builtin_bit_cast(v4i, lds16(st + boff[u][0] + j * 32 * SB));
+      fb[j].hi = __builtin_bit_cast(v4i, lds16(st + boff[u][1] + j * 32 * SB));
+    }
+  };
+  // MFMAs of the current k-step (A in fa, B in fb) while the fragments of
+  // the next one (k-step u of the strip at `next`) are read: B first, then A
+  // block by block behind the MFMAs that last use it.  `last` multiplies the
+  // final k-step.
+  auto step = [&](const v8i (&fb)[FN], v8i (&fb_next)[FN], const char* next, int u) {
+    read_b(fb_next, next, u);
+    // low halves of every block first, so that the two MFMAs into one
+    // accumulator are FM * FN instructions apart
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i].lo, fb[j].lo, acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i].hi, fb[j].hi, acc[i][j], 0, 0, 0);
+      read_a(i, next, u);
+    }
+  };
+  auto last = [&](const v8i (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i].lo, fb[j].lo, acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i].hi, fb[j].hi, acc[i][j], 0, 0, 0);
+  };
+  auto order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x020, L::kLoads, 0);  // DMA issue
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * FN, 0);     // B reads
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);    // the low halves
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);  // block i's high halves
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then its A reads
+    }
+  };
+  // With two stages the strip fetched at a crossing has one strip's time to
+  // land: its B half (the weight, usually from HBM) goes out right after the
+  // barrier and its A half one k-step later, which spreads the DMA issue
+  // (4096 x 12288 x 3072: 131-133 -> 127.5-129.5 us; the same split gained
+  // nothing in the int8 kernel, which keeps one fetch).
+  auto fetch_a = [&](int s) {
+    adma.fetch(lds + (s % S) * L::kStage, ra, uint32_t(s < nk ? s : nk - 1) * SB);
+  };
+  auto fetch_b = [&](int s) {
+    bdma.fetch(lds + (s % S) * L::kStage + L::kA, rb, uint32_t(s < nk ? s : nk - 1) * SB);
+  };
+  constexpr bool kSplit = S == 2 && U > 1;
+  auto cross = [&](int kt) {
+    wait_lds();
+    wait_vm<(S - 2) * L::kLoads>();
+    block_barrier();
+    if constexpr (kSplit) fetch_b(kt + S);
+    else fetch(kt + S);
+  };
+
+#pragma unroll
+  for (int s = 0; s < S; ++s) fetch(s);
+  wait_vm<(S - 1) * L::kLoads>();
+  block_barrier();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) read_a(i, lds, 0);
+  read_b(bP, lds, 0);
+  auto advance = [&](const char* next, int u) {  // into k-step u of the strip at `next`
+    step(bP, bQ, next, u);
+    order();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bP[j] = bQ[j];
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    if constexpr (kSplit)
+      if (kt >= 1) fetch_a(kt - 1 + S);  // its slot was freed at the last crossing
+#pragma unroll
+    for (int u = 1; u < U; ++u) advance(lds + (kt % S) * L::kStage, u);
+    cross(kt);
+    advance(lds + ((kt + 1) % S) * L::kStage, 0);
+  }
+#pragma unroll
+  for (int u = 1; u < U; ++u) advance(lds + ((nk - 1) % S) * L::kStage, u);
+  wait_lds();
+  last(bP);
+  wait_vm<0>();  // no LDS write may land after the block ends
+
+  // Scales through LDS (free now): as[BM], bs[BN], bb[BN].
+  float* sh_as = reinterpret_cast<float*>(lds);
+  float* sh_bs = sh_as + BM;
+  float* sh_bb = sh_bs + BN;
+  block_barrier();  // every wave is done reading the last strip
+  if constexpr (OUT != 2) {
+    const int t = threadIdx.x;
+    if (t < BM) sh_as[t] = pre_as;
+    if (t < BN) {
+      sh_bs[t] = pre_bs;
+      sh_bb[t] = pre_bb;
+    }
+    __syncthreads();
+  }
+  float bs[FN], bb[FN];
+  if constexpr (OUT != 2) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bs[j] = sh_bs[col0 + r + 32 * j];
+      bb[j] = sh_bb[col0 + r + 32 * j];
+    }
+  }
+  // Element (i, j, v): row m0 + row0 + 32 i + 8 (v / 4) + 4 h + v % 4, column n0 + col0 + 32 j + r.
+  auto value = [&](int i, int j, int v, const v4f& as4) {
+    return float(acc[i][j][v]) * as4[v % 4] * bs[j] + bb[j];
+  };
+  auto scales4 = [&](int i, int q) {  // a_scale of rows 32 i + 8 q + 4 h .. +3 of the wave part
+    v4f t{};
+    if constexpr (OUT != 2) t = *reinterpret_cast<const v4f*>(sh_as + row0 + 32 * i + 8 * q + 4 * h);
+    return t;
+  };
+  if (vec && m0 + BM <= M && n0 + BN <= N) {
+    const Slab<OUT, FN, 32> slab{lds + kSlabBase + wid * Slab<OUT, FN, 32>::kBytes, lane};
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f as4 = scales4(i, q);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int row = 8 * q + 4 * h + p, col = 32 * j + r;
+            if constexpr (OUT == 2) slab.put_i(row, col, acc[i][j][4 * q + p]);
+            else slab.put_f(row, col, value(i, j, 4 * q + p, as4));
+          }
+      }
+      slab.flush(out, N, m0 + row0 + 32 * i, n0 + col0);
+      wait_lds();  // slab reads done before it is rewritten
+    }
+  } else {
+    const int64_t mw = m0 + row0 + 4 * h, nw = n0 + col0 + r;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f as4 = scales4(i, q);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int64_t m = mw + 32 * i + 8 * q + p;
+          if (m >= M) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = nw + 32 * j;
+            if (n >= N) continue;
+            if constexpr (OUT == 2) reinterpret_cast<int32_t*>(out)[m * N + n] = acc[i][j][4 * q + p];
+            else put_out<OUT>(out, m * N + n, value(i, j, 4 * q + p, as4));
+          }
+        }
+      }
+  }
+}
+
 template <int BM, int BN, int S, int WY, int NW, int SB = 64>
 hipError_t launch_fp8_w8a8_cfg2(const uint8_t* a, const uint8_t* b, void* out, int out_bf16, int64_t M, int64_t N,
                                 int64_t K, float alpha, hipStream_t s) {
@@ -1564,6 +1807,26 @@ hipError_t launch_fp8_w8a8_cfg(const uint8_t* a, const uint8_t* b, void* out, in
                                                                      alpha, vec);
   return launch_big_lds<fp8_w8a8_lds_kernel<BM, BN, S, WY, NW, 0>>(L::kLds, blocks, 64 * NW, s, a, b, out, M, N, K,
                                                                    alpha, vec);
+}
+
+template <int BM, int BN, int S, int WY, int NW, int SB>
+hipError_t launch_int8_lds2(const int8_t* a, const int8_t* b, const float* sa, const float* sb, const uint16_t* bias,
+                            void* out, int out_mode, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  using L = I8Layout<BM, BN, S, WY, NW, SB>;
+  const int64_t blocks = tiles(M, N, BM, BN);
+  const int es = out_mode == 1 ? 2 : 4;
+  const int vec = aligned16(out) && (N * es) % 16 == 0;
+  switch (out_mode) {
+    case 0:
+      return launch_big_lds<int8_lds2_kernel<BM, BN, S, WY, NW, 0, SB>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb, bias,
+                                                                        out, M, N, K, vec);
+    case 1:
+      return launch_big_lds<int8_lds2_kernel<BM, BN, S, WY, NW, 1, SB>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb, bias,
+                                                                        out, M, N, K, vec);
+    default:
+      return launch_big_lds<int8_lds2_kernel<BM, BN, S, WY, NW, 2, SB>>(L::kLds, blocks, 64 * NW, s, a, b, sa, sb, bias,
+                                                                        out, M, N, K, vec);
+  }
 }
 
 template <int BM, int BN, int S, int WY, int NW, int SB = 64>
@@ -1812,9 +2075,12 @@ hipError_t launch_int8_gemm_lds(const int8_t* a, const int8_t* b, const float* s
   // 256 x 256 tiles halve the L2 -> LDS traffic of 256 x 128 ones, which
   // pays even when some CUs get no tile.  128-byte strips (two stages in the
   // ring) beat 64-byte ones (four stages) where K allows: 4096 x 12288 x
-  // 3072 147 against 158 us, 4096 x 3072 x 3072 42.5 against 45.8 us.
+  // 3072 147 against 158 us, 4096 x 3072 x 3072 42.5 against 45.8 us.  With
+  // such strips the W8A8 structure (split DMA, fragments refreshed in place)
+  // is about 1 % faster again: 138.9 against 140.1 us, 40.9 against 41.2 us.
   if (tiles(M, N, 256, 256) >= num_cus / 2) {
-    if (K % 128 == 0) return launch_int8_cfg<256, 256, 2, 2, 8, 128>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
+    if (K % 128 == 0)
+      return launch_int8_lds2<256, 256, 2, 2, 8, 128>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
     return launch_int8_cfg<256, 256, 4, 2, 8>(a, b, sa, sb, bias, out, out_mode, M, N, K, s);
   }
   if (tiles(M, N, 256, 128) >= num_cus / 2)
