@@ -657,7 +657,7 @@ def build_int8(dev, q, synth, np, torch):
 
     return dict(metric="W8A8 int8 GEMM TOPS (quantiser + GEMM + dequant epilogue)", unit="TOPS", per="work",
                 cases=cases, dominant=cases[2], bound="mfma", peak=INT8_PEAK_TOPS, mfma_dtype=1,
-                kernel="int8_gemm_lds_kernel<256, 256> (M=4096, N=12288, K=3072)", dtype="i8",
+                kernel="int8_lds2_kernel<256, 256> (M=4096, N=12288, K=3072)", dtype="i8",
                 config={"workload": "w8a8_int8: quantise bf16 [4096,3072] + int8 GEMM N in {3072,12288}, bf16 out"},
                 baseline=baseline)
 
@@ -891,7 +891,7 @@ def main():
         sys.exit(2)
 
     kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
-               "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
+               "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_lds2_kernel",
                "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds2_kernel",
                "bf16_decode": "bf16_gemv_wide_kernel", "grouped_int8": "int8_grouped_kernel"}
     if args.counters_from:
@@ -902,7 +902,7 @@ def main():
         return
     if args.traffic_from:
         kernels = {"decode": "fp8_gemv_wide_kernel", "gemv2048": "fp8_gemv_wide_kernel",
-                   "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_gemm_lds_kernel",
+                   "nvfp4": "wq_gemm_kernel", "grouped": "grouped_gemm_kernel", "int8": "int8_lds2_kernel",
                    "grouped_nvfp4": "grouped_gemm_kernel", "fp8_w8a8": "fp8_w8a8_lds2_kernel",
                    "bf16_decode": "bf16_gemv_wide_kernel", "grouped_int8": "int8_grouped_kernel"}
         write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], kernels[args.workload])
