@@ -171,3 +171,44 @@ def test_grouped_random_shapes(q, case):
     g4 = out4.cpu().numpy()
     assert np.array_equal(g4[written], ref4[written].astype(np.float32))
     assert np.all(np.isnan(g4[~written]))
+
+
+@pytest.mark.parametrize("g", [65, 129, 200])
+def test_grouped_many_groups(q, g):
+    """More groups than one wave's 64 lanes: the kernels' prefix sum of the
+    groups' row tiles carries across several passes (exact inputs, every
+    family bit for bit; empty, inactive and uncovered rows included)."""
+    r = _rng(7, g)
+    e, n, k, t = 8, 136, 256, 900
+    cuts = np.sort(r.integers(0, t + 1, size=g + 1)).astype(np.int64)
+    ids = r.integers(-1, e, size=g).astype(np.int32)
+    offs_dev = torch.from_numpy(cuts.astype(np.int32)).to(DEV)
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    w = synth.dyadic_fp8_weight((82, g), e * n, k).reshape(e, n, k)
+    x = synth.dyadic_activation((83, g), t, k)
+    ref, _, written = R.fp8_grouped(w, x, cuts, ids)
+    show("many groups fp8", g, e, n, t, k)
+    out = torch.full((t, n), float("nan"), dtype=torch.float32, device=DEV)
+    q.fp8_grouped_gemm(to_dev_u8(w), to_dev_bf16(x), offs_dev, ids_dev, out=out, out_dtype=torch.float32)
+    got = out.cpu().numpy()
+    assert np.array_equal(got[written], ref[written].astype(np.float32))
+    assert np.all(np.isnan(got[~written]))
+    a = r.integers(-127, 128, size=(t, k)).astype(np.int8)
+    b = r.integers(-127, 128, size=(e, n, k)).astype(np.int8)
+    acc, _, written = R.int8_grouped(a, b, None, None, None, cuts, ids, raw=True)
+    show("many groups int8", g)
+    raw = torch.full((t, n), -7, dtype=torch.int32, device=DEV)
+    q.int8_grouped_gemm(to_dev_i8(a), to_dev_i8(b), None, None, offs_dev, ids_dev, out=raw, out_dtype=torch.int32)
+    gi = raw.cpu().numpy()
+    assert np.array_equal(gi[written], acc[written].astype(np.int32))
+    assert np.all(gi[~written] == -7)
+    p, s = synth.dyadic_nvfp4_weight((84, g), e * n, k)
+    p, s = p.reshape(e, n, k // 2), s.reshape(e, n, k // 16)
+    ref4, _, written = R.nvfp4_grouped(p, s, x, cuts, ids)
+    show("many groups nvfp4", g)
+    out4 = torch.full((t, n), float("nan"), dtype=torch.float32, device=DEV)
+    q.nvfp4_grouped_gemm(to_dev_u8(p), to_dev_u8(s), to_dev_bf16(x), offs_dev, ids_dev, out=out4,
+                         out_dtype=torch.float32)
+    g4 = out4.cpu().numpy()
+    assert np.array_equal(g4[written], ref4[written].astype(np.float32))
+    assert np.all(np.isnan(g4[~written]))
