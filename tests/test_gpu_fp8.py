@@ -79,12 +79,15 @@ DYADIC = [
     # one block, every M, and the automatic choice at M = 12, K = 8192
     ("splitk", 16, 4096, 14336), ("splitk", 3, 1000, 4096), ("splitk", 9, 300, 2112), ("splitk", 16, 70, 1024),
     ("splitk", 1, 129, 512), ("auto", 12, 2000, 8192),
-    # streaming skinny kernel (K in {1024, 2048, 3072, 4096}; N >= 8192 for 5 <= M <= 16, 8192 <= N <
-    # 65536 for 3 <= M <= 4): every ring depth, a ragged last 16-row tile, every M class, the smallest
-    # N it takes (fewer tiles than blocks on some CUs) and M = 3, 4 below the 4x4x4 kernel's range
+    # streaming skinny kernel (K in {1024, 2048, 3072, 4096}; N >= 6144 for 5 <= M <= 16, 8192 <= N <
+    # 65536 for M = 3, and for M = 4 also 4096 <= N < 8192 at K = 4096): every ring depth, a ragged
+    # last 16-row tile, every M class, the smallest N it takes (fewer tiles than blocks on some CUs,
+    # one stage on a block), M = 3, 4 below the 4x4x4 kernel's range
     ("skinny", 16, 65553, 2048), ("skinny", 5, 65536, 3072), ("auto", 9, 65537, 1024),
     ("skinny", 16, 131087, 4096), ("auto", 6, 100003, 4096),
     ("auto", 16, 14336, 4096), ("auto", 3, 8192, 1024), ("auto", 4, 14343, 2048), ("skinny", 5, 8197, 3072),
+    ("auto", 4, 4096, 4096), ("auto", 4, 4111, 4096), ("auto", 16, 6144, 4096), ("auto", 8, 6150, 1024),
+    ("skinny", 5, 6144, 2048),
 ]
 
 

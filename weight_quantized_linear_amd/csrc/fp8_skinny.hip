@@ -604,12 +604,10 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
   const int64_t stages = cnt * KS;
 
   // DMA of this block's stage j (tile j / KS, part j % KS) into its ring
-  // slot: instruction i of wave w moves 1 KiB (part p) of stage row r.  A
-  // stage past the block's last one re-fetches the last one (only in the
-  // prologue of a block with fewer than S stages), so that the prologue
-  // always issues the same loads.
+  // slot: instruction i of wave w moves 1 KiB (part p) of stage row r.
+  // A block with fewer than S stages issues only those it has (the waits
+  // below count only issued stages).
   auto issue = [&](int64_t j) {
-    if (j >= stages) j = stages - 1;
     const int64_t t = t0 + (j / KS) * gridDim.x;
     const int h = int(j % KS);
     char* slot = lds + (j % S) * kStage;
@@ -639,7 +637,8 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
                                                                 wid * (kRow / NW) + 64 * c + 16 * q + 8 * e))
                               : v8bf{};
 #pragma unroll
-  for (int j = 1; j < S; ++j) issue(j);
+  for (int j = 1; j < S; ++j)
+    if (j < stages) issue(j);
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int64_t j = 0; j < stages; ++j) {
@@ -861,6 +860,12 @@ hipError_t launch_fp8_skinny_stream(const uint8_t* w, const uint16_t* x, void* o
   return launch_stream<false>(w, x, out, out_bf16, M, N, K, alpha, num_cus, epi, s);
 }
 
+bool fp8_skinny_stream_wins(int64_t M, int64_t N, int64_t K) {
+  if (M >= 5) return N >= 6144;
+  if (M == 4) return N < 65536 && (N >= 8192 || (N >= 4096 && K == 4096));
+  return M == 3 && N >= 8192 && N < 65536;
+}
+
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && K >= 256 && K % 256 == 0 && N >= 1 && N <= (int64_t(1) << 30) &&
          int64_t(xlds_groups(M)) * K * 8 + 16 * kWave * 4 <= kMaxLds;
@@ -872,10 +877,12 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
   // Many output features: the streaming kernel (whole weight rows into an
   // LDS ring).  Measured at K = 4096: M = 16, N = 128256: 94 us against 102
   // us for the 4x4x4 kernel; N = 14336: 16.6 against 19.2 us (M = 8: 15.2
-  // against 18.1; M = 4: 14.7 against 15.7); at N = 4096 (one 16-row tile
-  // per CU) it loses (10.2 against 8.4 us at M = 16), and at M = 4 over
+  // against 18.1; M = 4: 14.7 against 15.7); N = 6144: M = 16 11.3 against
+  // 14.7 us, M = 8 10.1 against 11.9; at N = 4096 (one 16-row tile per CU)
+  // it loses for M >= 8 (8.8 against 8.5 us at M = 16) but wins at M = 4
+  // (6.8 against 7.7 us for the GEMV, which takes M = 4 there); at M = 4 over
   // the 128256-row weight the 4x4x4 kernel keeps the lead (86 against 87-91).
-  if (M >= 3 && N >= 8192 && (M > 4 || N < 65536) && fp8_skinny_stream_supported(w, x, M, N, K))
+  if (fp8_skinny_stream_wins(M, N, K) && fp8_skinny_stream_supported(w, x, M, N, K))
     return launch_fp8_skinny_stream(w, x, out, out_bf16, M, N, K, alpha, num_cus, s, epi);
   // Measured: for 5 <= M <= 8 the activation-in-LDS kernel wins only at
   // very many output features, where its whole-row weight bursts matter most.

@@ -48,6 +48,9 @@ hipError_t launch_fp8_gemv(const uint8_t* w, const uint16_t* x, void* out, int o
 // True when the activation-resident matrix-core kernel serves (M, N, K)
 // (M <= 8, K % 256 == 0, the zero-padded activation fits in LDS).
 bool fp8_skinny_xlds_supported(int64_t M, int64_t N, int64_t K);
+// True where the streaming matrix-core kernel is the measured best skinny
+// kernel for (M, N, K), given that it supports the shape.
+bool fp8_skinny_stream_wins(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int out_bf16,
                              int64_t M, int64_t N, int64_t K, float alpha, int num_cus,
                              hipStream_t s, const Epilogue& epi = Epilogue{});

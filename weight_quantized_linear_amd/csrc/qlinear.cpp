@@ -109,8 +109,11 @@ int fp8_choose(int path, int64_t M, int64_t N, int64_t K, bool wide, bool splitk
   // below 65536 output features and for M <= 4 on small weights; the
   // matrix-core skinny kernels win above that (for 3 <= M <= 4 from 8192
   // output features or a K of 8192 when the activation-in-LDS kernel
-  // applies) and for 5 <= M <= 16; beyond 16 rows the LDS-tiled GEMM.
-  const bool big = N >= 65536 || (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K));
+  // applies, and for M = 4 from 4096 output features where the streaming
+  // kernel takes the shape) and for 5 <= M <= 16; beyond 16 rows the
+  // LDS-tiled GEMM.
+  const bool big = N >= 65536 || (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K)) ||
+                   (M == 4 && fp8_skinny_stream_wins(M, N, K) && (K == 1024 || K == 2048 || K == 3072 || K == 4096));
   if (M == 1) return QLINEAR_PATH_GEMV;
   if (M <= 4) return (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
   // For 9 <= M <= 16 with a long K and fewer than 65536 output features the
