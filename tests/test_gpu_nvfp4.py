@@ -70,7 +70,11 @@ NVFP4_DYADIC = [("gemv", 1, 7, 4096), ("gemv", 1, 515, 48), ("gemv", 3, 129, 204
                 ("tiled", 128, 4096, 4096), ("tiled", 77, 1000, 2048), ("tiled", 256, 640, 1024),
                 ("tiled", 257, 640, 1024),
                 # split-K with nine 128-value strips over three slices, and seventeen 64-value strips
-                ("tiled", 128, 4096, 1152), ("tiled", 100, 2048, 1088)]
+                ("tiled", 128, 4096, 1152), ("tiled", 100, 2048, 1088),
+                # 128x128 tiles of four side-by-side waves with 64-value strips (at most half of the
+                # CUs would get a 128x256 tile): exactly half, and ragged M and N with five and
+                # sixty-five strips
+                ("tiled", 1024, 4096, 256), ("tiled", 1000, 1030, 320), ("tiled", 640, 770, 4160)]
 
 
 @pytest.mark.parametrize("path,m,n,k", NVFP4_DYADIC)

@@ -1916,12 +1916,18 @@ hipError_t launch_nvfp4_gemm_lds(const uint8_t* packed, const uint8_t* scales, c
   // Where K allows, 128-value strips (64 packed bytes per weight row) in a
   // two-stage ring: M = 2048, N = K = 4096 70 against 73 us with a few
   // weight copies, the same 75 us with weights cycled through 1 GiB (three
-  // stages: 74 us).
-  if (tiles(M, N, 128, 256) >= num_cus / 2) {
+  // stages: 74 us).  Taken while more than half of the CUs get a tile.
+  if (tiles(M, N, 128, 256) > num_cus / 2) {
     if (K % 128 == 0) return launch_wq<Nvfp4Weight2, 128, 256, 2, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
     return launch_wq<Nvfp4Weight, 128, 256, 4, 1, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
   }
-  return launch_wq<Nvfp4Weight, 128, 128, 4, 2, 8>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
+  // Fewer tiles: 128 x 128 with four waves side by side (each 128 x 32, no
+  // weight row decoded twice) and 64-value strips in a two-stage ring, 41
+  // KiB of LDS, so that two or three blocks share a CU.  M = 1024, N = K =
+  // 4096: 49.6 against 61.4 us for 128 x 256 tiles on half of the CUs; at M
+  // = 256 .. 768 without split-K within 1 us of 128 x 128 with 2 x 4 waves
+  // and four stages, which it replaces.
+  return launch_wq<Nvfp4Weight, 128, 128, 2, 1, 4>(x, wa, out, out_bf16, M, N, K, alpha, epi, s);
 }
 
 // Workspace bytes with which the launchers above take their split-K kernels
