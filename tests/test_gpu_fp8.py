@@ -79,6 +79,9 @@ DYADIC = [
     # one block, every M, and the automatic choice at M = 12, K = 8192
     ("splitk", 16, 4096, 14336), ("splitk", 3, 1000, 4096), ("splitk", 9, 300, 2112), ("splitk", 16, 70, 1024),
     ("splitk", 1, 129, 512), ("auto", 12, 2000, 8192),
+    # its streaming form where K is made of 2048-value slices (two to eight slices): the smallest N,
+    # a ragged last 16-row tile, several tiles per block
+    ("splitk", 1, 16, 4096), ("splitk", 16, 4111, 6144), ("splitk", 5, 20000, 16384), ("splitk", 4, 4096, 14336),
     # streaming skinny kernel (K in {1024, 2048, 3072, 4096}; N >= 6144 for 5 <= M <= 16, 8192 <= N <
     # 65536 for M = 3, and for M = 4 also 4096 <= N < 8192 at K = 4096): every ring depth, a ragged
     # last 16-row tile, every M class, the smallest N it takes (fewer tiles than blocks on some CUs,

@@ -579,12 +579,17 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_splitk_kernel(const uint8_
 //   8 q + e of instruction h on both operands);
 // * after a tile's last stage the NW partial 16 x 16 tiles meet in LDS and
 //   one wave (a different one each tile) adds them in wave order and stores.
-template <int NW, int SPW, int KS, int S, bool FUSED>
+// SPLIT: K here is one slice of rows `ld` values long; block row blockIdx.y
+// takes slice blockIdx.y and stores its sums, unscaled, to float32 plane
+// blockIdx.y of `part` ([slices][M][N]) for the split-K reduction.
+template <int NW, int SPW, int KS, int S, bool FUSED, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, void* __restrict__ out,
-    int out_bf16, int M, int64_t N, float alpha, Epilogue epi) {
+    int out_bf16, int M, int64_t N, float alpha, Epilogue epi, int64_t ld, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  constexpr int K = 64 * NW * SPW;          // the kernel is instantiated per K
+  constexpr int K = 64 * NW * SPW;          // the kernel is instantiated per K (per slice with SPLIT)
+  const int64_t row_len = SPLIT ? ld : int64_t(K);
+  const int64_t k0 = SPLIT ? int64_t(blockIdx.y) * K : 0;
   constexpr int kRow = K / KS;              // bytes of a row in one stage
   constexpr int kSteps = SPW / KS;          // 64-value steps of a wave per stage
   constexpr int kRowParts = kRow / 1024;    // 1 KiB DMA instructions per stage row
@@ -617,7 +622,7 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
       const int r = ins / kRowParts, p = ins % kRowParts;
       int64_t n = 16 * t + r;
       if (n >= N) n = N - 1;  // rows past N re-read the last row; never stored
-      dma16_nt(reinterpret_cast<const char*>(w + n * K + h * kRow) + 16 * (64 * p + (lane ^ r)),
+      dma16_nt(reinterpret_cast<const char*>(w + n * row_len + k0 + h * kRow) + 16 * (64 * p + (lane ^ r)),
                slot + r * kRow + 1024 * p);
     }
   };
@@ -633,7 +638,7 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
     for (int c = 0; c < kSteps; ++c)
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        xa[h][c][e] = r16 < M ? __builtin_bit_cast(v8bf, ld16(x + int64_t(r16) * K + h * kRow +
+        xa[h][c][e] = r16 < M ? __builtin_bit_cast(v8bf, ld16(x + int64_t(r16) * row_len + k0 + h * kRow +
                                                                 wid * (kRow / NW) + 64 * c + 16 * q + 8 * e))
                               : v8bf{};
 #pragma unroll
@@ -687,7 +692,10 @@ __global__ __launch_bounds__(NW * 64) void fp8_skinny_stream_kernel(
         if (n < N) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (4 * q + e < M) store_maybe_epi<FUSED>(out, 4 * q + e, n, N, sum[e], alpha, out_bf16, epi);
+            if (4 * q + e < M) {
+              if constexpr (SPLIT) part[(int64_t(blockIdx.y) * M + 4 * q + e) * N + n] = sum[e];
+              else store_maybe_epi<FUSED>(out, 4 * q + e, n, N, sum[e], alpha, out_bf16, epi);
+            }
         }
       }
       acc0 = v4f{0.f, 0.f, 0.f, 0.f};
@@ -784,10 +792,28 @@ int64_t skinny_splits(int64_t M, int64_t N, int64_t K, int num_cus, int64_t* ksl
 
 }  // namespace
 
+namespace {
+
+// Slices of the streaming kernel's split-K form: 2048 values each (one slice
+// instantiation), at least two; 0 when K does not split so.
+constexpr int kStreamSlice = 2048;
+int64_t stream_splits(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > 16 || N < 16 || N > (int64_t(1) << 31) / 16 || K % kStreamSlice != 0) return 0;
+  const int64_t splits = K / kStreamSlice;
+  return splits >= 2 && splits <= 65535 ? splits : 0;
+}
+
+hipError_t launch_stream_split(const uint8_t* w, const uint16_t* x, float* ws, int64_t M, int64_t N, int64_t K,
+                               int num_cus, hipStream_t s);
+
+}  // namespace
+
 size_t fp8_skinny_splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
   int64_t ksl = 0;
   const int64_t splits = skinny_splits(M, N, K, num_cus, &ksl);
-  return splits > 1 ? size_t(splits) * size_t(M) * size_t(N) * 4 : 0;
+  if (splits < 2) return 0;  // the shape does not suit split-K
+  // The call may take either split-K kernel: room for the larger plane count.
+  return size_t(std::max(splits, stream_splits(M, N, K))) * size_t(M) * size_t(N) * 4;
 }
 
 hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
@@ -798,6 +824,14 @@ hipError_t launch_fp8_skinny_splitk(const uint8_t* w, const uint16_t* x, void* o
   int64_t ksl = 0;
   const int64_t splits = skinny_splits(M, N, K, num_cus, &ksl);
   if (splits < 2) return hipErrorInvalidValue;
+  // Where K is made of 2048-value slices, the streaming kernel's split-K form
+  // (whole weight-row segments DMA'd into LDS, activation slice in registers).
+  const int64_t ssplits = stream_splits(M, N, K);
+  if (ssplits > 1 && size_t(ssplits) * size_t(M) * size_t(N) * 4 <= ws_bytes &&
+      reinterpret_cast<uintptr_t>(w) % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {
+    if (hipError_t e = launch_stream_split(w, x, ws, M, N, K, num_cus, s)) return e;
+    return launch_splitk_reduce(ws, out, out_bf16, M, N, int(ssplits), alpha, s, epi);
+  }
   const int64_t row_blocks = (N + 16 * kNW - 1) / (16 * kNW);
   if (size_t(splits) * size_t(M) * size_t(N) * 4 > ws_bytes) return hipErrorInvalidValue;
   const int lds = int(16 * (2 * ksl + 16));
@@ -826,7 +860,7 @@ hipError_t launch_stream_k(const uint8_t* w, const uint16_t* x, void* out, int o
   const int64_t tiles = (N + 15) / 16;
   const int64_t blocks = std::min<int64_t>(tiles, num_cus);
   return launch(kern, dim3(unsigned(blocks)), dim3(kNW * kWave), size_t(kLds), s, w, x, out, out_bf16, int(M), N,
-                alpha, epi);
+                alpha, epi, int64_t(K), static_cast<float*>(nullptr));
 }
 
 template <bool FUSED>
@@ -842,6 +876,39 @@ hipError_t launch_stream(const uint8_t* w, const uint16_t* x, void* out, int out
     case 4096: return launch_stream_k<8, 1, 2, FUSED>(w, x, out, out_bf16, M, N, alpha, num_cus, epi, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Split-K form: grid (column blocks, K / slice); the column blocks of one
+// slice share the 16-row tiles, and all blocks together fill the CUs once.
+template <int SPW, int KS, int S>
+hipError_t launch_stream_split_k(const uint8_t* w, const uint16_t* x, float* ws, int64_t M, int64_t N, int64_t K,
+                                 int num_cus, hipStream_t s) {
+  constexpr int kNW = 8;
+  constexpr int kSlice = 64 * kNW * SPW;
+  static_assert(kSlice == kStreamSlice, "one slice width");
+  constexpr int kLds = S * 16 * (kSlice / KS) + kNW * kWave * 16;
+  static_assert(kLds <= kMaxLds, "ring and partial tiles fit in LDS");
+  auto kern = fp8_skinny_stream_kernel<kNW, SPW, KS, S, false, true>;
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), kLds, lds_set)) return e;
+  const int64_t splits = K / kSlice;
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t per_cu = std::max<int64_t>(1, kMaxLds / kLds);
+  const int64_t bx = std::max<int64_t>(1, std::min<int64_t>(tiles, int64_t(num_cus) * per_cu / splits));
+  return launch(kern, dim3(unsigned(bx), unsigned(splits)), dim3(kNW * kWave), size_t(kLds), s, w, x,
+                static_cast<void*>(nullptr), 0, int(M), N, 1.f, Epilogue{}, K, ws);
+}
+
+// Whole-slice stages in a two-stage ring (72 KiB, two blocks per CU): N =
+// 4096, K = 14336 at M = 4 / 8 / 16 15.0 / 15.4 / 17.8 us, against 15.8 /
+// 16.3 / 18.4 with half-slice stages four deep (also two blocks per CU),
+// 19.1 / 19.4 / 20.3 with eight deep (one block per CU) and 16.6 / 17.0 /
+// 19.1 for the split-K skinny kernel; N = K = 14336 37.7 / 39.7 / 44.4
+// against 56.9 / 57.9 / 59.4 for the latter.
+hipError_t launch_stream_split(const uint8_t* w, const uint16_t* x, float* ws, int64_t M, int64_t N, int64_t K,
+                               int num_cus, hipStream_t s) {
+  if (stream_splits(M, N, K) < 2) return hipErrorInvalidValue;
+  return launch_stream_split_k<4, 1, 2>(w, x, ws, M, N, K, num_cus, s);
 }
 
 }  // namespace

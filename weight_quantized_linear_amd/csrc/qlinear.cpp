@@ -114,14 +114,22 @@ int fp8_choose(int path, int64_t M, int64_t N, int64_t K, bool wide, bool splitk
   // LDS-tiled GEMM.
   const bool big = N >= 65536 || (M >= 3 && (N >= 8192 || K >= 8192) && fp8_skinny_xlds_supported(M, N, K)) ||
                    (M == 4 && fp8_skinny_stream_wins(M, N, K) && (K == 1024 || K == 2048 || K == 3072 || K == 4096));
+  // Split-K needs the caller's workspace.  Where K is made of 2048-value
+  // slices (K >= 8192) and there are fewer than 65536 output features, its
+  // streaming form wins from M = 3 (N = 4096, K = 14336: M = 4 14.8 against
+  // 17.2 us for the 4x4x4 skinny kernel, M = 8 15.4 against 18.5; N = K =
+  // 14336, M = 8: 40.1 against 51.7) and at M = 2 from 8192 output features
+  // (N = K = 14336: 37.2 against 47.2 us for the GEMV; at N = 4096 the GEMV
+  // keeps 12.6 against 14.3); for 9 <= M <= 16 the split-K skinny kernel also
+  // wins at other long K (M = 16, N = 4096, K = 14336: 19.2 against 23.1 us).
+  const bool split_long = splitk_ok && wide && K >= 8192 && N < 65536;
   if (M == 1) return QLINEAR_PATH_GEMV;
-  if (M <= 4) return (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
-  // For 9 <= M <= 16 with a long K and fewer than 65536 output features the
-  // split-K skinny kernel wins (M = 16, N = 4096, K = 14336: 19.2 us against
-  // 23.1 us) when the caller gives it a workspace.
+  if (M <= 4) {
+    if ((M >= 3 || N >= 8192) && split_long && K % 2048 == 0) return QLINEAR_PATH_SPLITK;
+    return (wide && big) ? QLINEAR_PATH_SKINNY : QLINEAR_PATH_GEMV;
+  }
   if (M <= 16 && wide)
-    return (splitk_ok && M > 8 && K >= 8192 && K % 64 == 0 && N < 65536) ? QLINEAR_PATH_SPLITK
-                                                                          : QLINEAR_PATH_SKINNY;
+    return (split_long && (K % 2048 == 0 || (M > 8 && K % 64 == 0))) ? QLINEAR_PATH_SPLITK : QLINEAR_PATH_SKINNY;
   return QLINEAR_PATH_TILED;
 }
 
