@@ -82,6 +82,8 @@ DYADIC = [
     # its streaming form where K is made of 2048-value slices (two to eight slices): the smallest N,
     # a ragged last 16-row tile, several tiles per block
     ("splitk", 1, 16, 4096), ("splitk", 16, 4111, 6144), ("splitk", 5, 20000, 16384), ("splitk", 4, 4096, 14336),
+    # the automatic choice takes it from M = 3, and at M = 2 from 8192 output features
+    ("auto", 2, 8192, 8192), ("auto", 3, 4096, 14336), ("auto", 2, 4096, 14336),
     # streaming skinny kernel (K in {1024, 2048, 3072, 4096}; N >= 6144 for 5 <= M <= 16, 8192 <= N <
     # 65536 for M = 3, and for M = 4 also 4096 <= N < 8192 at K = 4096): every ring depth, a ragged
     # last 16-row tile, every M class, the smallest N it takes (fewer tiles than blocks on some CUs,
