@@ -31,7 +31,8 @@ FAMILIES = [
     ("fp8 skinny activation-in-LDS", "fp8", "skinny", 4, 5000, 4096),
     ("fp8 skinny 4x4x4", "fp8", "skinny", 2, 700, 1040),
     ("fp8 skinny LDS wide-N", "fp8", "skinny", 12, 66000, 192),
-    ("fp8 skinny split-K", "fp8", "splitk", 12, 1000, 8192),
+    ("fp8 streaming split-K", "fp8", "splitk", 12, 1000, 8192),
+    ("fp8 skinny split-K", "fp8", "splitk", 12, 1000, 8256),
     ("fp8 tiled split-K", "fp8", "tiled", 20, 1000, 2048),
     ("fp8 tiled whole-K", "fp8", "tiled", 300, 700, 1024),
     ("fp8 tiled 256x256", "fp8", "tiled", 2048, 8200, 64),

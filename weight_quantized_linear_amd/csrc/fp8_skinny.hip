@@ -769,8 +769,9 @@ hipError_t launch_xlds(const uint8_t* w, const uint16_t* x, void* out, int out_b
 
 // Split-K skinny GEMM: K slices of at least 256 values, enough (row block,
 // slice) pairs to give every CU a block, partial planes within the
-// workspace.  Returns hipErrorInvalidValue when the shape or workspace does
-// not suit it (the caller then takes another kernel).
+// workspace; where K is made of 2048-value slices, the streaming kernel's
+// split-K form instead.  Returns hipErrorInvalidValue when the shape or
+// workspace does not suit it (the caller then takes another kernel).
 namespace {
 
 constexpr int kSplitNW = 8, kSplitU = 4;

@@ -56,6 +56,8 @@ hipError_t launch_fp8_skinny(const uint8_t* w, const uint16_t* x, void* out, int
                              hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // Split-K skinny GEMM (M <= 16, K % 64 == 0, aligned, workspace present):
+// the streaming kernel's split-K form where K is made of 2048-value slices
+// and the workspace holds its planes, else the split-K skinny kernel;
 // hipErrorInvalidValue when the shape does not suit it.  The second kernel
 // (gemm_lds.hip) adds the float32 partial planes [splits, M, N] in order,
 // then applies alpha and the epilogue.
@@ -71,7 +73,8 @@ bool fp8_skinny_stream_supported(const void* w, const void* x, int64_t M, int64_
 hipError_t launch_fp8_skinny_stream(const uint8_t* w, const uint16_t* x, void* out, int out_bf16, int64_t M,
                                     int64_t N, int64_t K, float alpha, int num_cus, hipStream_t s,
                                     const Epilogue& epi = Epilogue{});
-// Workspace bytes the split-K skinny kernel takes for (M, N, K) (0: it does not apply).
+// Workspace bytes a split-K skinny call takes for (M, N, K): room for the
+// planes of either split-K kernel (0: split-K does not apply).
 size_t fp8_skinny_splitk_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
 
 // gemm_bf16.hip (dispatches to gemm_lds.hip when K % 64 == 0 and operands are aligned)
