@@ -71,6 +71,24 @@ def test_fp8_gemm_random_shapes(q, case):
     _check(out, ref, out_dtype)
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_fp8_gemm_random_long_k(q, case):
+    """The split-K region of the automatic choice (a workspace is given):
+    K >= 8192 made of 2048-value slices (the streaming kernel's split-K form)
+    or any other multiple of 64 (the split-K skinny kernel), M = 2..16 and
+    N from 16 to 12000 (ragged 16-row tiles)."""
+    r = _rng(8, case)
+    m, n = int(r.integers(2, 17)), int(r.integers(16, 12001))
+    k = 2048 * int(r.integers(4, 9)) if case % 3 else 64 * int(r.integers(128, 257))
+    out_dtype = torch.float32 if case % 2 else torch.bfloat16
+    wc = synth.dyadic_fp8_weight((72, case), n, k)
+    xc = synth.dyadic_activation((73, case), m, k)
+    ref, _ = R.fp8_linear(wc, xc)
+    show("sweep fp8 long K", m, n, k, out_dtype)
+    out = q.fp8_gemm(to_dev_u8(wc), to_dev_bf16(xc), out_dtype=out_dtype)
+    _check(out, ref, out_dtype)
+
+
 @pytest.mark.parametrize("case", range(32))
 def test_nvfp4_gemm_random_shapes(q, case):
     r = _rng(2, case)
